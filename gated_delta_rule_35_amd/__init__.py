@@ -1,0 +1,202 @@
+"""gated_delta_rule_35_amd — the gated delta-rule layer on MI355X (gfx950).
+
+Thin Python binding over the C ABI of libagnes_gdn (include/agnes_gdn.h).  The
+functions below only check tensor layouts and pass device pointers, sizes and
+the current HIP stream to the library; every step of the layer runs in the
+library's HIP kernels.  torch supplies device memory and streams.
+
+The layer (model card "Agnes-3.0-Flash Preview", 架构 table, delta-rule row;
+discosf article "Agnes 3.0 Flash 刚上线就刷屏…", section 二.1):
+  conv            kernel-4 causal depth-wise conv + SiLU (+ L2 norm of q/k heads)
+  prefill_chunked chunked gated delta rule (chunk 64) over a packed batch
+  decode_step     stepwise gated delta rule, state updated in place
+  gated_rmsnorm   y = rmsnorm(o) * w * silu(z)
+"""
+import torch
+
+from . import _lib
+
+__all__ = ["conv", "prefill_chunked", "decode_step", "gated_rmsnorm", "prefill_workspace_size",
+           "AgnesError", "version", "LIB_PATH"]
+
+LIB_PATH = _lib.LIB_PATH
+HEAD_DIM = 128
+
+
+class AgnesError(RuntimeError):
+    def __init__(self, fn, status):
+        lib = _lib.load()
+        msg = lib.agnes_gdn_status_string(status).decode()
+        if status == _lib.ERR_HIP:
+            msg += f" (hipError_t {lib.agnes_gdn_last_hip_error()})"
+        super().__init__(f"{fn}: {msg}")
+        self.status = status
+
+
+def _dt(t):
+    if t.dtype == torch.bfloat16:
+        return _lib.BF16
+    if t.dtype == torch.float32:
+        return _lib.F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check(fn, status):
+    if status != _lib.OK:
+        raise AgnesError(fn, status)
+
+
+def _rows(t, name, width):
+    """(token stride) of a [T, width] view whose last dim is contiguous."""
+    if t.dim() != 2 or t.shape[1] != width or (t.numel() > 0 and t.shape[0] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name}: expected a [T, {width}] view with unit inner stride, got "
+                         f"{tuple(t.shape)} / {t.stride()}")
+    return t.stride(0) if t.numel() > 0 else width
+
+
+def _heads(t, name, heads):
+    """Token stride of a [T, heads, 128] view with contiguous heads."""
+    if t.dim() != 3 or t.shape[1] != heads or t.shape[2] != HEAD_DIM:
+        raise ValueError(f"{name}: expected [T, {heads}, {HEAD_DIM}], got {tuple(t.shape)}")
+    if t.numel() == 0:
+        return heads * HEAD_DIM
+    if t.stride(2) != 1 or (heads > 1 and t.stride(1) != HEAD_DIM):
+        raise ValueError(f"{name}: heads must be contiguous (strides {t.stride()})")
+    return t.stride(0) if t.shape[0] > 0 else heads * HEAD_DIM
+
+
+def version():
+    return _lib.load().agnes_gdn_version().decode()
+
+
+def conv(x, weight, *, y=None, bias=None, cu_seqlens=None, conv_state=None, l2norm_heads=0,
+         head_dim=HEAD_DIM, eps=1e-6):
+    """Causal depth-wise conv (kernel 4) + SiLU (+ L2 norm of the leading ``l2norm_heads`` heads).
+
+    x: [T, C] (row stride free, inner stride 1); weight: [C, 4] contiguous; bias: [C] or None.
+    cu_seqlens: int32 [N+1] on the device (prefill), or None for decode mode (T sequences of
+    one token, conv_state required).  conv_state: [N, C, 3] oldest first, updated in place.
+    Returns y ([T, C], x's dtype, contiguous unless given).
+    """
+    T, C = x.shape
+    xs = _rows(x, "x", C)
+    if y is None:
+        y = torch.empty((T, C), dtype=x.dtype, device=x.device)
+    ys = _rows(y, "y", C)
+    if weight.dim() != 2 or not weight.is_contiguous():
+        raise ValueError("weight: expected a contiguous [C, K] tensor")
+    for t, name in ((y, "y"), (weight, "weight"), (bias, "bias"), (conv_state, "conv_state")):
+        if t is not None and t.dtype != x.dtype:
+            raise TypeError(f"{name} must have x's dtype {x.dtype}")
+    if conv_state is not None and not conv_state.is_contiguous():
+        raise ValueError("conv_state must be contiguous [N, C, K-1]")
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        n = cu_seqlens.numel() - 1
+    else:
+        n = T
+    st = _lib.load().agnes_gdn_conv(
+        _ptr(x), xs, _ptr(y), ys, _dt(x), _ptr(weight), _ptr(bias), _ptr(cu_seqlens), n, T, C,
+        weight.shape[1], _ptr(conv_state), l2norm_heads, head_dim, eps, _stream(x.device))
+    _check("agnes_gdn_conv", st)
+    return y
+
+
+def prefill_workspace_size(num_seqs, total_tokens, num_k_heads, num_v_heads, in_dtype):
+    return _lib.load().agnes_gdn_prefill_workspace_size(
+        num_seqs, total_tokens, num_k_heads, num_v_heads, HEAD_DIM,
+        _lib.BF16 if in_dtype == torch.bfloat16 else _lib.F32)
+
+
+def prefill_chunked(q, k, v, g, beta, cu_seqlens, *, initial_state=None, final_state=None,
+                    output_final_state=True, scale=1.0, o=None, o_dtype=None, workspace=None):
+    """Chunked gated delta-rule prefill over a packed batch.
+
+    q, k: [T, Hk, 128]; v: [T, Hv, 128] (token strides free; views of a conv output work);
+    g, beta: fp32 [T, Hv]; cu_seqlens: int32 [N+1] (device); initial_state: fp32
+    [N, Hv, 128, 128] or None.  final_state: preallocated output (may be initial_state for
+    an in-place update); allocated when None and ``output_final_state``.
+    Returns (o [T, Hv, 128], final_state or None).
+    """
+    T, Hk, _ = q.shape
+    Hv = v.shape[1]
+    qs = _heads(q, "q", Hk)
+    if _heads(k, "k", Hk) != qs:
+        raise ValueError("q and k must share one token stride")
+    vs = _heads(v, "v", Hv)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share one dtype")
+    for t, name in ((g, "g"), (beta, "beta")):
+        if t.dtype != torch.float32 or tuple(t.shape) != (T, Hv) or not t.is_contiguous():
+            raise ValueError(f"{name}: expected contiguous fp32 [{T}, {Hv}]")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    n = cu_seqlens.numel() - 1
+    if o is None:
+        o = torch.empty((T, Hv, HEAD_DIM), dtype=o_dtype or q.dtype, device=q.device)
+    elif not o.is_contiguous():
+        raise ValueError("o must be contiguous")
+    for s, name in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if s is not None and (s.dtype != torch.float32 or not s.is_contiguous()
+                              or tuple(s.shape) != (n, Hv, HEAD_DIM, HEAD_DIM)):
+            raise ValueError(f"{name}: expected contiguous fp32 [{n}, {Hv}, 128, 128]")
+    if final_state is None and output_final_state:
+        final_state = torch.empty((n, Hv, HEAD_DIM, HEAD_DIM), dtype=torch.float32, device=q.device)
+    need = prefill_workspace_size(n, T, Hk, Hv, q.dtype)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = _lib.load().agnes_gdn_prefill_chunked(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), qs, vs, _ptr(g), _ptr(beta), _ptr(cu_seqlens), n, T,
+        Hk, Hv, HEAD_DIM, scale, _ptr(initial_state), _ptr(final_state), _ptr(o), _dt(o),
+        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(q.device))
+    _check("agnes_gdn_prefill_chunked", st)
+    return o, final_state
+
+
+def decode_step(q, k, v, g, beta, state, *, scale=1.0, o=None, o_dtype=None):
+    """One stepwise decode token per sequence; ``state`` (fp32 [B, Hv, 128, 128]) is updated
+    in place.  q, k: [B, Hk, 128]; v: [B, Hv, 128]; g, beta: fp32 [B, Hv].  Returns o."""
+    B, Hk, _ = q.shape
+    Hv = v.shape[1]
+    qs = _heads(q, "q", Hk)
+    if _heads(k, "k", Hk) != qs:
+        raise ValueError("q and k must share one token stride")
+    vs = _heads(v, "v", Hv)
+    if state.dtype != torch.float32 or not state.is_contiguous() or tuple(state.shape) != (B, Hv, HEAD_DIM, HEAD_DIM):
+        raise ValueError("state: expected contiguous fp32 [B, Hv, 128, 128]")
+    for t, name in ((g, "g"), (beta, "beta")):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, Hv) or not t.is_contiguous():
+            raise ValueError(f"{name}: expected contiguous fp32 [{B}, {Hv}]")
+    if o is None:
+        o = torch.empty((B, Hv, HEAD_DIM), dtype=o_dtype or q.dtype, device=q.device)
+    st = _lib.load().agnes_gdn_decode_step(
+        _ptr(q), _ptr(k), _ptr(v), _dt(q), qs, vs, _ptr(g), _ptr(beta), B, Hk, Hv, HEAD_DIM, scale,
+        _ptr(state), _ptr(o), _dt(o), _stream(q.device))
+    _check("agnes_gdn_decode_step", st)
+    return o
+
+
+def gated_rmsnorm(o, z, weight, *, eps=1e-6, y=None, y_dtype=None):
+    """y = o / sqrt(mean(o^2) + eps) * weight * silu(z) per row of 128 (o, z contiguous)."""
+    if o.shape[-1] != HEAD_DIM or z.shape != o.shape or not o.is_contiguous() or not z.is_contiguous():
+        raise ValueError("o and z: contiguous tensors of one shape ending in 128")
+    if weight.numel() != HEAD_DIM or weight.dtype != z.dtype:
+        raise ValueError("weight: [128] with z's dtype")
+    if y is None:
+        y = torch.empty(o.shape, dtype=y_dtype or o.dtype, device=o.device)
+    rows = o.numel() // HEAD_DIM
+    st = _lib.load().agnes_gdn_gated_rmsnorm(
+        _ptr(o), _dt(o), _ptr(z), _ptr(weight), _dt(z), eps, rows, HEAD_DIM, _ptr(y), _dt(y),
+        _stream(o.device))
+    _check("agnes_gdn_gated_rmsnorm", st)
+    return y

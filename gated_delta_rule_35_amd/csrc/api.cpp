@@ -1,0 +1,187 @@
+// C-ABI host layer of libagnes_gdn: argument checks, dtype dispatch and launches.
+// Every check runs before anything is enqueued; a failed check launches nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "agnes_gdn.h"
+#include "launch.h"
+
+#define AGNES_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kHeadDim = 128;
+
+bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+bool valid_dtype(int d) { return d == AGNES_F32 || d == AGNES_BF16; }
+size_t esize(int d) { return d == AGNES_BF16 ? 2 : 4; }
+
+// Byte span [lo, hi) touched by `rows` rows of `width` elements at `stride` elements.
+struct Span {
+  uintptr_t lo, hi;
+};
+Span span(const void* p, int64_t rows, int64_t stride, int64_t width, size_t es) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  if (rows <= 0 || width <= 0) return {lo, lo};
+  return {lo, lo + (uintptr_t)(((rows - 1) * stride + width) * (int64_t)es)};
+}
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return AGNES_OK;
+  g_last_hip_error = (int)e;
+  return AGNES_ERR_HIP;
+}
+
+}  // namespace
+
+AGNES_API const char* agnes_gdn_status_string(int status) {
+  switch (status) {
+    case AGNES_OK: return "AGNES_OK";
+    case AGNES_ERR_INVALID_ARG: return "AGNES_ERR_INVALID_ARG: invalid argument (pointer, size, stride or overlap)";
+    case AGNES_ERR_UNSUPPORTED: return "AGNES_ERR_UNSUPPORTED: outside the supported set (head_dim 128, kernel 4, Hv % Hk == 0)";
+    case AGNES_ERR_WORKSPACE: return "AGNES_ERR_WORKSPACE: workspace missing or too small";
+    case AGNES_ERR_HIP: return "AGNES_ERR_HIP: a HIP launch failed";
+    default: return "unknown agnes_status";
+  }
+}
+
+AGNES_API int agnes_gdn_last_hip_error(void) { return g_last_hip_error; }
+
+AGNES_API const char* agnes_gdn_version(void) { return "0.1.0"; }
+
+AGNES_API int agnes_gdn_conv(const void* x, int64_t x_token_stride, void* y, int64_t y_token_stride,
+                             agnes_dtype dtype, const void* weight, const void* bias,
+                             const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens, int channels,
+                             int kernel_size, void* conv_state, int l2norm_heads, int head_dim,
+                             float l2norm_eps, void* stream) {
+  if (!valid_dtype(dtype)) return AGNES_ERR_INVALID_ARG;
+  if (!x || !y || !weight) return AGNES_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(y, 16) || !aligned(weight, 4) || (bias && !aligned(bias, 4)) ||
+      (conv_state && !aligned(conv_state, 4)))
+    return AGNES_ERR_INVALID_ARG;
+  if (num_seqs < 0 || total_tokens < 0 || channels <= 0 || channels % 8) return AGNES_ERR_INVALID_ARG;
+  if (x_token_stride < channels || y_token_stride < channels || x_token_stride % 8 || y_token_stride % 8)
+    return AGNES_ERR_INVALID_ARG;
+  if (l2norm_heads < 0 || !(l2norm_eps >= 0.f) || !std::isfinite(l2norm_eps)) return AGNES_ERR_INVALID_ARG;
+  if (kernel_size != 4) return AGNES_ERR_UNSUPPORTED;
+  if (l2norm_heads > 0) {
+    if (head_dim != kHeadDim) return AGNES_ERR_UNSUPPORTED;
+    if ((int64_t)l2norm_heads * head_dim > channels) return AGNES_ERR_INVALID_ARG;
+  }
+  if (!cu_seqlens) {  // decode mode
+    if (!conv_state || total_tokens != num_seqs) return AGNES_ERR_INVALID_ARG;
+  } else if (num_seqs == 0 && total_tokens != 0) {
+    return AGNES_ERR_INVALID_ARG;
+  }
+  if ((int64_t)num_seqs > 65535 && !cu_seqlens) return AGNES_ERR_UNSUPPORTED;  // grid.y limit
+  if (conv_state && num_seqs > 65535) return AGNES_ERR_UNSUPPORTED;
+  if ((total_tokens + 15) / 16 > 65535) return AGNES_ERR_UNSUPPORTED;
+  const size_t es = esize(dtype);
+  if (overlap(span(x, total_tokens, x_token_stride, channels, es), span(y, total_tokens, y_token_stride, channels, es)))
+    return AGNES_ERR_INVALID_ARG;
+  if (conv_state && overlap(span(conv_state, num_seqs, (int64_t)channels * 3, (int64_t)channels * 3, es),
+                            span(y, total_tokens, y_token_stride, channels, es)))
+    return AGNES_ERR_INVALID_ARG;
+
+  agnes::ConvArgs a{x, x_token_stride, y, y_token_stride, (int)dtype, weight, bias, cu_seqlens, num_seqs,
+                    total_tokens, channels, conv_state, l2norm_heads, l2norm_eps};
+  return hip_status(agnes::launch_conv(a, static_cast<hipStream_t>(stream)));
+}
+
+AGNES_API size_t agnes_gdn_prefill_workspace_size(int num_seqs, int64_t total_tokens, int num_k_heads,
+                                                  int num_v_heads, int head_dim, agnes_dtype in_dtype) {
+  if (num_seqs < 0 || total_tokens < 0 || num_k_heads <= 0 || num_v_heads <= 0 || head_dim != kHeadDim ||
+      num_v_heads % num_k_heads || !valid_dtype(in_dtype))
+    return 0;
+  if (in_dtype == AGNES_BF16) return agnes::prefill_mfma_workspace(num_seqs, total_tokens, num_k_heads, num_v_heads);
+  return 0;
+}
+
+AGNES_API int agnes_gdn_prefill_chunked(const void* q, const void* k, const void* v, agnes_dtype in_dtype,
+                                        int64_t qk_token_stride, int64_t v_token_stride, const float* g,
+                                        const float* beta, const int32_t* cu_seqlens, int num_seqs,
+                                        int64_t total_tokens, int num_k_heads, int num_v_heads, int head_dim,
+                                        float scale, const float* initial_state, float* final_state, void* o,
+                                        agnes_dtype o_dtype, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(o_dtype)) return AGNES_ERR_INVALID_ARG;
+  if (num_seqs < 0 || total_tokens < 0 || num_k_heads <= 0 || num_v_heads <= 0) return AGNES_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim || num_v_heads % num_k_heads) return AGNES_ERR_UNSUPPORTED;
+  if (num_seqs == 0 && total_tokens != 0) return AGNES_ERR_INVALID_ARG;
+  if (num_seqs > 0 && !cu_seqlens) return AGNES_ERR_INVALID_ARG;
+  if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return AGNES_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(g, 4) ||
+      !aligned(beta, 4) || !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(cu_seqlens, 4))
+    return AGNES_ERR_INVALID_ARG;
+  if (qk_token_stride < (int64_t)num_k_heads * head_dim || v_token_stride < (int64_t)num_v_heads * head_dim ||
+      qk_token_stride % 8 || v_token_stride % 8)
+    return AGNES_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return AGNES_ERR_INVALID_ARG;
+  if ((int64_t)num_seqs * num_v_heads * 8 > INT32_MAX) return AGNES_ERR_UNSUPPORTED;
+  const int64_t sbytes = (int64_t)num_seqs * num_v_heads * head_dim * head_dim;
+  const Span s0 = span(initial_state, 1, 0, sbytes, 4), s1 = span(final_state, 1, 0, sbytes, 4);
+  if (initial_state && final_state && initial_state != final_state && overlap(s0, s1)) return AGNES_ERR_INVALID_ARG;
+  const Span os = span(o, total_tokens, (int64_t)num_v_heads * head_dim, (int64_t)num_v_heads * head_dim, esize(o_dtype));
+  if (final_state && overlap(os, s1)) return AGNES_ERR_INVALID_ARG;
+  const size_t es = esize(in_dtype);
+  if (overlap(os, span(q, total_tokens, qk_token_stride, (int64_t)num_k_heads * head_dim, es)) ||
+      overlap(os, span(k, total_tokens, qk_token_stride, (int64_t)num_k_heads * head_dim, es)) ||
+      overlap(os, span(v, total_tokens, v_token_stride, (int64_t)num_v_heads * head_dim, es)))
+    return AGNES_ERR_INVALID_ARG;
+  const size_t need = agnes_gdn_prefill_workspace_size(num_seqs, total_tokens, num_k_heads, num_v_heads, head_dim,
+                                                       in_dtype);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return AGNES_ERR_WORKSPACE;
+
+  agnes::PrefillArgs a{q, k, v, (int)in_dtype, qk_token_stride, v_token_stride, g, beta, cu_seqlens, num_seqs,
+                       total_tokens, num_k_heads, num_v_heads, scale, initial_state, final_state, o, (int)o_dtype,
+                       workspace, workspace_bytes};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return hip_status(in_dtype == AGNES_BF16 ? agnes::launch_prefill_mfma(a, st) : agnes::launch_prefill_f32(a, st));
+}
+
+AGNES_API int agnes_gdn_decode_step(const void* q, const void* k, const void* v, agnes_dtype in_dtype,
+                                    int64_t qk_token_stride, int64_t v_token_stride, const float* g,
+                                    const float* beta, int batch, int num_k_heads, int num_v_heads, int head_dim,
+                                    float scale, float* state, void* o, agnes_dtype o_dtype, void* stream) {
+  if (!valid_dtype(in_dtype) || !valid_dtype(o_dtype)) return AGNES_ERR_INVALID_ARG;
+  if (batch < 0 || num_k_heads <= 0 || num_v_heads <= 0) return AGNES_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim || num_v_heads % num_k_heads) return AGNES_ERR_UNSUPPORTED;
+  if (batch > 0 && (!q || !k || !v || !g || !beta || !state || !o)) return AGNES_ERR_INVALID_ARG;
+  if (!aligned(q, 4) || !aligned(k, 4) || !aligned(v, 4) || !aligned(g, 4) || !aligned(beta, 4) ||
+      !aligned(state, 16) || !aligned(o, 4))
+    return AGNES_ERR_INVALID_ARG;
+  if (qk_token_stride < (int64_t)num_k_heads * head_dim || v_token_stride < (int64_t)num_v_heads * head_dim)
+    return AGNES_ERR_INVALID_ARG;
+  if (!std::isfinite(scale)) return AGNES_ERR_INVALID_ARG;
+  if ((int64_t)batch * num_v_heads > INT32_MAX) return AGNES_ERR_UNSUPPORTED;
+  const Span ss = span(state, 1, 0, (int64_t)batch * num_v_heads * head_dim * head_dim, 4);
+  const Span os = span(o, batch, (int64_t)num_v_heads * head_dim, (int64_t)num_v_heads * head_dim, esize(o_dtype));
+  if (overlap(ss, os)) return AGNES_ERR_INVALID_ARG;
+
+  agnes::DecodeArgs a{q, k, v, (int)in_dtype, qk_token_stride, v_token_stride, g, beta, batch, num_k_heads,
+                      num_v_heads, scale, state, o, (int)o_dtype};
+  return hip_status(agnes::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+AGNES_API int agnes_gdn_gated_rmsnorm(const void* o, agnes_dtype o_dtype, const void* z, const void* weight,
+                                      agnes_dtype zw_dtype, float eps, int64_t rows, int dim, void* y,
+                                      agnes_dtype y_dtype, void* stream) {
+  if (!valid_dtype(o_dtype) || !valid_dtype(zw_dtype) || !valid_dtype(y_dtype)) return AGNES_ERR_INVALID_ARG;
+  if (rows < 0 || !(eps >= 0.f) || !std::isfinite(eps)) return AGNES_ERR_INVALID_ARG;
+  if (dim != kHeadDim) return AGNES_ERR_UNSUPPORTED;
+  if (rows > 0 && (!o || !z || !weight || !y)) return AGNES_ERR_INVALID_ARG;
+  if (!aligned(o, 16) || !aligned(z, 16) || !aligned(weight, 16) || !aligned(y, 16)) return AGNES_ERR_INVALID_ARG;
+  const Span ys = span(y, rows, dim, dim, esize(y_dtype));
+  const Span osp = span(o, rows, dim, dim, esize(o_dtype));
+  const bool exact_alias = (o == y) && (o_dtype == y_dtype);
+  if (!exact_alias && overlap(ys, osp)) return AGNES_ERR_INVALID_ARG;
+  if (overlap(ys, span(z, rows, dim, dim, esize(zw_dtype)))) return AGNES_ERR_INVALID_ARG;
+
+  agnes::NormArgs a{o, (int)o_dtype, z, weight, (int)zw_dtype, eps, rows, y, (int)y_dtype};
+  return hip_status(agnes::launch_gated_rmsnorm(a, static_cast<hipStream_t>(stream)));
+}

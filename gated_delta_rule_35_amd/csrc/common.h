@@ -1,0 +1,109 @@
+// Device helpers shared by the gfx950 kernels of the gated delta-rule layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace agnes {
+
+enum : int { DT_F32 = 0, DT_BF16 = 1 };
+
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16 storage
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// 8 consecutive elements of a DT tensor as fp32 (16-byte aligned for bf16, 32 for f32).
+template <int DT>
+__device__ __forceinline__ void load8(const void* base, int64_t idx, float out[8]) {
+  if constexpr (DT == DT_BF16) {
+    uint4 u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+    float4 a = p[0], b = p[1];
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void store8(void* base, int64_t idx, const float v[8]) {
+  if constexpr (DT == DT_BF16) {
+    uint4 u;
+    u.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+    u.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+    u.z = f32_to_bf16(v[4]) | (f32_to_bf16(v[5]) << 16);
+    u.w = f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + idx) = u;
+  } else {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + idx);
+    p[0] = make_float4(v[0], v[1], v[2], v[3]);
+    p[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ float load1(const void* base, int64_t idx) {
+  if constexpr (DT == DT_BF16) return bf16_to_f32(static_cast<const uint16_t*>(base)[idx]);
+  else return static_cast<const float*>(base)[idx];
+}
+
+template <int DT>
+__device__ __forceinline__ void store1(void* base, int64_t idx, float v) {
+  if constexpr (DT == DT_BF16) static_cast<uint16_t*>(base)[idx] = (uint16_t)f32_to_bf16(v);
+  else static_cast<float*>(base)[idx] = v;
+}
+
+// ---------------------------------------------------------------- reductions
+// Sum over each aligned group of 16 lanes (a DPP row); every lane gets its group's sum.
+__device__ __forceinline__ float sum16(float v) {
+  v += __shfl_xor(v, 1, 16);
+  v += __shfl_xor(v, 2, 16);
+  v += __shfl_xor(v, 4, 16);
+  v += __shfl_xor(v, 8, 16);
+  return v;
+}
+
+__device__ __forceinline__ float silu(float u) { return u / (1.0f + __expf(-u)); }
+
+// ---------------------------------------------------------------- matrix cores
+// D = A(16x32) B(32x16) + C.  Lane l holds A[l%16][8(l/16)+e], B[8(l/16)+e][l%16],
+// and D[4(l/16)+i][l%16] (i = 0..3).
+__device__ __forceinline__ f4 mfma_16x16x32(h8 a, h8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// D = A(16x16) B(16x16) + C.  Lane l holds A[l%16][4(l/16)+e], B[4(l/16)+e][l%16],
+// D[4(l/16)+i][l%16]: the D fragment is already in B-operand order.
+__device__ __forceinline__ f4 mfma_16x16x16(h4 a, h4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ h4 to_h4(f4 v) {
+  h4 r;
+  r[0] = (_Float16)v[0]; r[1] = (_Float16)v[1]; r[2] = (_Float16)v[2]; r[3] = (_Float16)v[3];
+  return r;
+}
+
+// Clamp a device cu_seqlens entry into [0, total].
+__device__ __forceinline__ int64_t cu_at(const int32_t* cu, int i, int64_t total) {
+  int64_t v = cu[i];
+  return v < 0 ? 0 : (v > total ? total : v);
+}
+
+}  // namespace agnes

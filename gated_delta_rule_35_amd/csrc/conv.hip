@@ -1,0 +1,221 @@
+// Depth-wise causal convolution (kernel 4) + SiLU + per-head L2 normalisation of the q and
+// k heads, in front of the gated delta rule (model card "Agnes-3.0-Flash Preview", 架构
+// table, delta-rule row: causal conv of kernel 4; discosf article "Agnes 3.0 Flash
+// 刚上线就刷屏…", section 二.1: the same kernel-4 causal conv).
+//
+//   y[t, c] = SiLU(bias[c] + sum_j w[c, j] * xh[t - 3 + j, c]),  w[c, 3] on the current token,
+//
+// with xh taken from the sequence's conv history before its first token.  HBM-bound
+// streaming kernels: each thread owns 8 consecutive channels (one 16-byte bf16 vector)
+// and walks a block of tokens, keeping the three previous inputs in registers, so x is
+// read once (plus a 3-token halo per block) and y written once.  Sixteen lanes cover one
+// 128-channel head, so the L2 norm is a 16-lane reduction at each token.
+#include "common.h"
+#include "launch.h"
+
+namespace agnes {
+
+constexpr int CONV_TB = 16;       // tokens per block
+constexpr int CONV_THREADS = 256;  // 256 x 8 = 2048 channels per block
+
+template <int DT>
+__device__ __forceinline__ void load_hist8(const ConvArgs& a, int n, int c0, int idx, float out[8]) {
+  // history entry idx (0 = oldest) of channels c0..c0+7 of sequence n
+  const int64_t base = ((int64_t)n * a.channels + c0) * 3;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = load1<DT>(a.state, base + e * 3 + idx);
+}
+
+template <int DT>
+__device__ __forceinline__ void conv_token(const ConvArgs& a, const float w[8][4], const float bias[8],
+                                           const float h0[8], const float h1[8], const float h2[8],
+                                           const float xc[8], bool l2, bool active, float y[8]) {
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float acc = bias[e];
+    acc = fmaf(w[e][0], h0[e], acc);
+    acc = fmaf(w[e][1], h1[e], acc);
+    acc = fmaf(w[e][2], h2[e], acc);
+    acc = fmaf(w[e][3], xc[e], acc);
+    y[e] = active ? acc / (1.0f + expf(-acc)) : 0.f;
+    ss = fmaf(y[e], y[e], ss);
+  }
+  ss = sum16(ss);
+  if (l2) {
+    const float r = 1.0f / sqrtf(ss + a.eps);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] *= r;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void load_params(const ConvArgs& a, int c0, bool active, float w[8][4], float bias[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[e][j] = active ? load1<DT>(a.w, (int64_t)(c0 + e) * 4 + j) : 0.f;
+    bias[e] = (active && a.bias) ? load1<DT>(a.bias, c0 + e) : 0.f;
+  }
+}
+
+// Prefill over a packed batch: grid (channel blocks, token blocks).
+template <int DT>
+__global__ __launch_bounds__(CONV_THREADS) void conv_prefill_kernel(ConvArgs a) {
+  const int c0 = (blockIdx.x * CONV_THREADS + threadIdx.x) * 8;
+  const bool active = c0 < a.channels;
+  const bool l2 = active && (c0 / 128) < a.l2_heads;
+  const int64_t t0 = (int64_t)blockIdx.y * CONV_TB;
+  const int64_t t1 = t0 + CONV_TB < a.total ? t0 + CONV_TB : a.total;
+
+  float w[8][4], bias[8];
+  load_params<DT>(a, c0, active, w, bias);
+
+  // sequence holding t0: largest n with cu[n] <= t0
+  int lo = 0, hi = a.num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu_at(a.cu, mid, a.total) <= t0) lo = mid; else hi = mid - 1;
+  }
+  int n = lo;
+  int64_t start = cu_at(a.cu, n, a.total);
+  int64_t end = cu_at(a.cu, n + 1, a.total);
+
+  float h[3][8];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {  // h[j] = xh[t0 - 3 + j]
+    const int64_t pos = t0 - 3 + j;
+    if (!active) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[j][e] = 0.f;
+    } else if (pos >= start) {
+      load8<DT>(a.x, pos * a.x_stride + c0, h[j]);
+    } else if (a.state) {
+      load_hist8<DT>(a, n, c0, (int)(3 - (start - pos)), h[j]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[j][e] = 0.f;
+    }
+  }
+
+  for (int64_t t = t0; t < t1; ++t) {
+    if (t >= end) {  // next non-empty sequence starts at t
+      while (n + 1 < a.num_seqs && cu_at(a.cu, n + 1, a.total) <= t) ++n;
+      start = t;
+      end = cu_at(a.cu, n + 1, a.total);
+#pragma unroll
+      for (int j = 0; j < 3; ++j) {
+        if (active && a.state) load_hist8<DT>(a, n, c0, j, h[j]);
+        else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) h[j][e] = 0.f;
+        }
+      }
+    }
+    float xc[8], y[8];
+    if (active) load8<DT>(a.x, t * a.x_stride + c0, xc);
+    else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xc[e] = 0.f;
+    }
+    conv_token<DT>(a, w, bias, h[0], h[1], h[2], xc, l2, active, y);
+    if (active) store8<DT>(a.y, t * a.y_stride + c0, y);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      h[0][e] = h[1][e];
+      h[1][e] = h[2][e];
+      h[2][e] = xc[e];
+    }
+  }
+}
+
+// Final history of every sequence, after the prefill kernel has read the old one:
+// new[j] = xh[end - 3 + j] (old history for positions before the sequence start).
+template <int DT>
+__global__ __launch_bounds__(CONV_THREADS) void conv_state_kernel(ConvArgs a) {
+  const int c0 = (blockIdx.x * CONV_THREADS + threadIdx.x) * 8;
+  const int n = blockIdx.y;
+  if (c0 >= a.channels) return;
+  const int64_t start = cu_at(a.cu, n, a.total);
+  int64_t end = cu_at(a.cu, n + 1, a.total);
+  if (end < start) end = start;
+  const int64_t len = end - start;
+  float old[3][8], nw[3][8];
+#pragma unroll
+  for (int j = 0; j < 3; ++j) load_hist8<DT>(a, n, c0, j, old[j]);
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const int64_t p = len - 3 + j;  // position relative to the sequence start
+    if (p >= 0) load8<DT>(a.x, (start + p) * a.x_stride + c0, nw[j]);
+    else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) nw[j][e] = old[3 + p][e];
+    }
+  }
+  const int64_t base = ((int64_t)n * a.channels + c0) * 3;
+#pragma unroll
+  for (int j = 0; j < 3; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) store1<DT>(a.state, base + e * 3 + j, nw[j][e]);
+}
+
+// Decode: one token per sequence, history read and advanced in place.
+template <int DT>
+__global__ __launch_bounds__(CONV_THREADS) void conv_decode_kernel(ConvArgs a) {
+  const int c0 = (blockIdx.x * CONV_THREADS + threadIdx.x) * 8;
+  const int n = blockIdx.y;
+  const bool active = c0 < a.channels;
+  const bool l2 = active && (c0 / 128) < a.l2_heads;
+  float w[8][4], bias[8], h[3][8], xc[8], y[8];
+  load_params<DT>(a, c0, active, w, bias);
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    if (active) load_hist8<DT>(a, n, c0, j, h[j]);
+    else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) h[j][e] = 0.f;
+    }
+  }
+  if (active) load8<DT>(a.x, (int64_t)n * a.x_stride + c0, xc);
+  else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) xc[e] = 0.f;
+  }
+  conv_token<DT>(a, w, bias, h[0], h[1], h[2], xc, l2, active, y);
+  if (!active) return;
+  store8<DT>(a.y, (int64_t)n * a.y_stride + c0, y);
+  const int64_t base = ((int64_t)n * a.channels + c0) * 3;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    store1<DT>(a.state, base + e * 3 + 0, h[1][e]);
+    store1<DT>(a.state, base + e * 3 + 1, h[2][e]);
+    store1<DT>(a.state, base + e * 3 + 2, xc[e]);
+  }
+}
+
+template <int DT>
+static hipError_t launch_conv_t(const ConvArgs& a, hipStream_t st) {
+  const unsigned cblocks = (unsigned)((a.channels / 8 + CONV_THREADS - 1) / CONV_THREADS);
+  if (a.cu == nullptr) {
+    if (a.num_seqs == 0) return hipSuccess;
+    hipLaunchKernelGGL((conv_decode_kernel<DT>), dim3(cblocks, (unsigned)a.num_seqs), dim3(CONV_THREADS), 0, st, a);
+    return hipGetLastError();
+  }
+  if (a.total > 0) {
+    const unsigned tblocks = (unsigned)((a.total + CONV_TB - 1) / CONV_TB);
+    hipLaunchKernelGGL((conv_prefill_kernel<DT>), dim3(cblocks, tblocks), dim3(CONV_THREADS), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (a.state && a.num_seqs > 0) {
+    hipLaunchKernelGGL((conv_state_kernel<DT>), dim3(cblocks, (unsigned)a.num_seqs), dim3(CONV_THREADS), 0, st, a);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_conv(const ConvArgs& a, hipStream_t st) {
+  return a.dtype == DT_BF16 ? launch_conv_t<DT_BF16>(a, st) : launch_conv_t<DT_F32>(a, st);
+}
+
+}  // namespace agnes

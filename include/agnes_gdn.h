@@ -1,0 +1,192 @@
+/*
+ * agnes_gdn — gated delta-rule layer on AMD Instinct MI355X (gfx950).
+ *
+ * The layer, as the pages describe it (model card "Agnes-3.0-Flash Preview",
+ * section 架构, delta-rule row; discosf article "Agnes 3.0 Flash 刚上线就刷屏…",
+ * section 二.1): a depth-wise causal convolution of kernel 4 in front, the gated
+ * delta-rule recurrence with 16 key / 48 value heads of dimension 128 and an
+ * fp32 recurrent state, a gated RMS-norm behind; prefill runs chunked (chunk 64)
+ * and decode runs one token at a time.  The recurrence is the gated delta rule
+ * of Yang, Kautz & Hatamizadeh ("Gated Delta Networks", ICLR 2025):
+ *
+ *     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = scale * S_t q_t,         alpha_t = exp(g_t),
+ *
+ * per value head h, reading key head h / (Hv / Hk) for q and k.  The state S is
+ * stored [value dim][key dim] (the shape of v k^T).
+ *
+ * Conventions shared by every call:
+ *   - Every tensor pointer is a DEVICE pointer, row-major, with the head
+ *     dimension contiguous.  Tensor base pointers must be 16-byte aligned and
+ *     element strides multiples of 8 elements (vector loads of 16 bytes).
+ *   - The caller owns every buffer, including the prefill workspace.  The
+ *     library never allocates, frees or synchronises; every call is enqueued
+ *     on `stream` (a hipStream_t; NULL = the default stream) and returns
+ *     before the GPU work ends.
+ *   - All argument checks happen before anything is launched.  On a failed
+ *     check the call returns a negative agnes_status, launches nothing and
+ *     leaves every output untouched.  A launch failure returns AGNES_ERR_HIP and
+ *     records the hipError_t, readable with agnes_gdn_last_hip_error() on the
+ *     same thread.  Faults inside kernels surface at the caller's next sync.
+ *   - Device-side index arrays (cu_seqlens) cannot be checked on the host
+ *     without a sync: they must hold cu[0] = 0, be nondecreasing and end at
+ *     total_tokens.  Kernels clamp every index to [0, total_tokens], so a
+ *     malformed array cannot make them access memory outside the buffers, but
+ *     the results are then unspecified.
+ *   - Functions keep no state between calls and may be called concurrently
+ *     from several threads on disjoint buffers.
+ *   - Supported set: head_dim 128, conv kernel_size 4, Hv a multiple of Hk.
+ *     Anything else returns AGNES_ERR_UNSUPPORTED.
+ */
+#ifndef AGNES_GDN_H
+#define AGNES_GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum agnes_status {
+  AGNES_OK = 0,
+  AGNES_ERR_INVALID_ARG = -1, /* NULL / misaligned pointer, bad size, stride or overlap */
+  AGNES_ERR_UNSUPPORTED = -2, /* valid request outside the supported set       */
+  AGNES_ERR_WORKSPACE = -3,   /* workspace smaller than the size query returned */
+  AGNES_ERR_HIP = -4          /* a HIP launch failed; see agnes_gdn_last_hip_error */
+} agnes_status;
+
+typedef enum agnes_dtype {
+  AGNES_F32 = 0,  /* IEEE binary32 */
+  AGNES_BF16 = 1  /* bfloat16 (top half of binary32); stores round to nearest even */
+} agnes_dtype;
+
+/*
+ * agnes_gdn_conv — depth-wise causal convolution + SiLU, then optional per-head
+ * L2 normalisation (model card 架构 table, delta-rule row: causal conv of
+ * kernel 4 in front of the recurrence).
+ *
+ *   y[t, c] = SiLU(bias[c] + sum_{j=0}^{K-1} w[c, j] * xh[t - (K-1) + j, c])
+ *
+ * with xh = x inside the token's sequence and, before the sequence's first
+ * token, the sequence's conv history (conv_state, oldest first; zeros when
+ * conv_state is NULL).  w[c, K-1] multiplies the current token.  Nothing
+ * crosses a sequence boundary.  Then each of the first `l2norm_heads` groups of
+ * `head_dim` channels (the q and k heads: 32 for the 16+16 q/k heads) is
+ * divided by sqrt(sum of squares + l2norm_eps).  Arithmetic is fp32.
+ *
+ *   x           [total_tokens rows, channels], row stride x_token_stride elems, `dtype`
+ *   y           [total_tokens rows, channels], row stride y_token_stride elems, `dtype`;
+ *               must not overlap x
+ *   weight      [channels, kernel_size], `dtype`, contiguous
+ *   bias        [channels], `dtype`, or NULL (no bias)
+ *   cu_seqlens  device int32 [num_seqs + 1] (prefill mode), or NULL for DECODE
+ *               mode: num_seqs sequences of exactly one token (total_tokens ==
+ *               num_seqs), whose history is conv_state (required).
+ *   conv_state  [num_seqs, channels, kernel_size - 1], `dtype`, oldest first, or
+ *               NULL (prefill only: zero history, final history not written).
+ *               In: each sequence's history.  Out: the last kernel_size-1 inputs
+ *               of each sequence (history included for sequences shorter than
+ *               kernel_size-1), written after every read of the old contents.
+ *   head_dim    channels per head for the L2 step (128); channels must be a
+ *               multiple of 8 and l2norm_heads*head_dim <= channels.
+ */
+int agnes_gdn_conv(const void* x, int64_t x_token_stride, void* y, int64_t y_token_stride,
+                   agnes_dtype dtype, const void* weight, const void* bias,
+                   const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens,
+                   int channels, int kernel_size, void* conv_state, int l2norm_heads,
+                   int head_dim, float l2norm_eps, void* stream);
+
+/*
+ * agnes_gdn_prefill_workspace_size — bytes of device workspace that
+ * agnes_gdn_prefill_chunked needs for this problem (may be 0).  Returns 0 and
+ * sets nothing for arguments outside the supported set (the call then fails
+ * with the matching status).
+ */
+size_t agnes_gdn_prefill_workspace_size(int num_seqs, int64_t total_tokens, int num_k_heads,
+                                        int num_v_heads, int head_dim, agnes_dtype in_dtype);
+
+/*
+ * agnes_gdn_prefill_chunked — chunked prefill of the gated delta rule over a
+ * packed batch of sequences (discosf article, section 二.1: chunked prefill
+ * with chunk 64; model card 架构 table: fp32 state).  Exactly the token
+ * recurrence above, re-associated per chunk of 64 tokens (the WY/UT form of
+ * Yang et al., "Parallelizing Linear Transformers with the Delta Rule over
+ * Sequence Length", NeurIPS 2024, with the gate of Gated Delta Networks).
+ *
+ *   q, k          [total_tokens, num_k_heads, head_dim], row stride qk_token_stride
+ *                 elems (views into the conv output are fine), `in_dtype`
+ *   v             [total_tokens, num_v_heads, head_dim], row stride v_token_stride
+ *   g, beta       fp32 [total_tokens, num_v_heads] contiguous: log-decay and write strength
+ *   cu_seqlens    device int32 [num_seqs + 1] (see conventions)
+ *   scale         output multiplier (1.0 = o_t = S_t q_t)
+ *   initial_state fp32 [num_seqs, num_v_heads, head_dim(v), head_dim(k)] or NULL (zeros)
+ *   final_state   same shape, or NULL (not written).  May alias initial_state
+ *                 exactly (in-place update); any other overlap is rejected.
+ *   o             [total_tokens, num_v_heads, head_dim] contiguous, `o_dtype`
+ *   workspace     device buffer of >= agnes_gdn_prefill_workspace_size() bytes
+ *                 (may be NULL when that size is 0)
+ *
+ * in_dtype BF16 computes the chunk products on fp16 matrix cores with fp32
+ * accumulation and an fp32 state; in_dtype F32 computes everything in fp32.
+ * Sequences of length 0 pass their initial state (or zeros) to final_state.
+ */
+int agnes_gdn_prefill_chunked(const void* q, const void* k, const void* v, agnes_dtype in_dtype,
+                              int64_t qk_token_stride, int64_t v_token_stride,
+                              const float* g, const float* beta, const int32_t* cu_seqlens,
+                              int num_seqs, int64_t total_tokens, int num_k_heads,
+                              int num_v_heads, int head_dim, float scale,
+                              const float* initial_state, float* final_state, void* o,
+                              agnes_dtype o_dtype, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
+ * agnes_gdn_decode_step — one stepwise decode token for each of `batch`
+ * independent sequences (discosf article, section 二.1: stepwise decode path),
+ * updating each fp32 state in place with one read and one write:
+ *
+ *   d_i = beta (v_i - alpha (S k)_i);  o_i = scale (alpha (S q)_i + d_i (k . q));
+ *   S_i <- alpha S_i + d_i k^T       (row i = value dim)
+ *
+ *   q, k   [batch, num_k_heads, head_dim], row stride qk_token_stride elems, `in_dtype`
+ *   v      [batch, num_v_heads, head_dim], row stride v_token_stride elems
+ *   g, beta fp32 [batch, num_v_heads] contiguous
+ *   state  fp32 [batch, num_v_heads, head_dim(v), head_dim(k)], updated in place
+ *   o      [batch, num_v_heads, head_dim] contiguous, `o_dtype`
+ */
+int agnes_gdn_decode_step(const void* q, const void* k, const void* v, agnes_dtype in_dtype,
+                          int64_t qk_token_stride, int64_t v_token_stride,
+                          const float* g, const float* beta, int batch, int num_k_heads,
+                          int num_v_heads, int head_dim, float scale, float* state,
+                          void* o, agnes_dtype o_dtype, void* stream);
+
+/*
+ * agnes_gdn_gated_rmsnorm — gated RMS-norm after the recurrence (model card
+ * 架构 table, delta-rule row), per row of `dim` values:
+ *
+ *   y = o / sqrt(mean(o^2) + eps) * weight * z * sigmoid(z)
+ *
+ *   o       [rows, dim] contiguous, `o_dtype`   (rows = tokens * value heads)
+ *   z       [rows, dim] contiguous, `zw_dtype`  (the gate)
+ *   weight  [dim], `zw_dtype`, shared by all rows
+ *   y       [rows, dim] contiguous, `y_dtype`; may alias o exactly when o_dtype == y_dtype
+ *   dim     128
+ */
+int agnes_gdn_gated_rmsnorm(const void* o, agnes_dtype o_dtype, const void* z,
+                            const void* weight, agnes_dtype zw_dtype, float eps, int64_t rows,
+                            int dim, void* y, agnes_dtype y_dtype, void* stream);
+
+/* Human-readable name of an agnes_status value (static string). */
+const char* agnes_gdn_status_string(int status);
+
+/* hipError_t of the last AGNES_ERR_HIP returned on the calling thread (0 if none). */
+int agnes_gdn_last_hip_error(void);
+
+/* Library version string, e.g. "0.1.0". */
+const char* agnes_gdn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AGNES_GDN_H */

@@ -1,0 +1,143 @@
+"""C-ABI boundary on the CPU: the library loads, exports exactly the header's functions, and
+every argument check returns its documented status before anything is launched.
+
+Pointer values below are never dereferenced: every call is built to fail a host-side check.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from gated_delta_rule_35_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "agnes_gdn.h")
+
+INV, UNS, WS = _lib.ERR_INVALID_ARG, _lib.ERR_UNSUPPORTED, _lib.ERR_WORKSPACE
+BF16, F32 = _lib.BF16, _lib.F32
+P = [0x10000000 * (i + 1) for i in range(12)]  # distinct, 16-byte aligned fake device pointers
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from gated_delta_rule_35_amd.build import build
+        build()
+    return _lib.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(agnes_gdn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_four_layer_calls():
+    names = header_functions()
+    for n in ("agnes_gdn_conv", "agnes_gdn_prefill_chunked", "agnes_gdn_decode_step",
+              "agnes_gdn_gated_rmsnorm"):
+        assert n in names
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def test_library_exports_exactly_the_header(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = sorted(set(re.findall(r"\b(agnes_gdn_\w+)\b", out)))
+    assert exported == header_functions()
+
+
+def test_status_strings_and_version(lib):
+    assert lib.agnes_gdn_version().decode().count(".") == 2
+    for s in (0, -1, -2, -3, -4):
+        assert lib.agnes_gdn_status_string(s)
+    assert lib.agnes_gdn_last_hip_error() == 0
+
+
+def conv(lib, **kw):
+    a = dict(x=P[0], xs=512, y=P[1], ys=512, dt=BF16, w=P[2], b=None, cu=P[3], n=2, T=10, C=512, K=4,
+             st=None, l2=2, hd=128, eps=1e-6)
+    a.update(kw)
+    return lib.agnes_gdn_conv(a["x"], a["xs"], a["y"], a["ys"], a["dt"], a["w"], a["b"], a["cu"], a["n"], a["T"],
+                              a["C"], a["K"], a["st"], a["l2"], a["hd"], a["eps"], None)
+
+
+def test_conv_checks(lib):
+    assert conv(lib, x=None) == INV
+    assert conv(lib, dt=7) == INV
+    assert conv(lib, x=P[0] + 8) == INV                 # misaligned
+    assert conv(lib, C=500, xs=500, ys=500) == INV      # channels % 8
+    assert conv(lib, xs=256) == INV                     # stride < channels
+    assert conv(lib, K=3) == UNS
+    assert conv(lib, hd=64) == UNS                      # L2 step needs 128-channel heads
+    assert conv(lib, l2=5) == INV                       # 5 * 128 > 512 channels
+    assert conv(lib, eps=float("nan")) == INV
+    assert conv(lib, cu=None, n=10, T=10) == INV        # decode mode needs conv_state
+    assert conv(lib, cu=None, n=4, T=10, st=P[4]) == INV  # decode: one token per sequence
+    assert conv(lib, n=0, T=10) == INV
+    assert conv(lib, y=P[0] + 512) == INV               # y overlaps x
+    assert lib.agnes_gdn_last_hip_error() == 0
+
+
+def prefill(lib, **kw):
+    a = dict(q=P[0], k=P[1], v=P[2], dt=BF16, qs=2 * 128, vs=6 * 128, g=P[3], b=P[4], cu=P[5], n=1, T=64,
+             hk=2, hv=6, hd=128, sc=1.0, s0=P[6], s1=P[7], o=P[8], odt=F32, ws=None, wsb=0)
+    a.update(kw)
+    return lib.agnes_gdn_prefill_chunked(a["q"], a["k"], a["v"], a["dt"], a["qs"], a["vs"], a["g"], a["b"],
+                                         a["cu"], a["n"], a["T"], a["hk"], a["hv"], a["hd"], a["sc"], a["s0"],
+                                         a["s1"], a["o"], a["odt"], a["ws"], a["wsb"], None)
+
+
+def test_prefill_checks(lib):
+    assert prefill(lib, hd=64) == UNS
+    assert prefill(lib, hv=5) == UNS                    # Hv % Hk
+    assert prefill(lib, q=None) == INV
+    assert prefill(lib, cu=None) == INV
+    assert prefill(lib, q=P[0] + 2) == INV              # misaligned
+    assert prefill(lib, qs=100) == INV                  # stride < Hk * 128
+    assert prefill(lib, qs=2 * 128 + 4) == INV          # stride % 8
+    assert prefill(lib, n=0) == INV                     # tokens without sequences
+    assert prefill(lib, n=-1) == INV
+    assert prefill(lib, s1=P[6] + 1024) == INV          # partial overlap of the two states
+    assert prefill(lib, o=P[0] + 64) == INV             # o overlaps q
+    assert prefill(lib, sc=float("inf")) == INV
+    assert prefill(lib, odt=3) == INV
+    assert lib.agnes_gdn_prefill_workspace_size(1, 64, 2, 6, 64, BF16) == 0
+    assert lib.agnes_gdn_prefill_workspace_size(1, 64, 2, 5, 128, BF16) == 0
+
+
+def decode(lib, **kw):
+    a = dict(q=P[0], k=P[1], v=P[2], dt=BF16, qs=2 * 128, vs=6 * 128, g=P[3], b=P[4], B=4, hk=2, hv=6, hd=128,
+             sc=1.0, st=P[5], o=P[6], odt=F32)
+    a.update(kw)
+    return lib.agnes_gdn_decode_step(a["q"], a["k"], a["v"], a["dt"], a["qs"], a["vs"], a["g"], a["b"], a["B"],
+                                     a["hk"], a["hv"], a["hd"], a["sc"], a["st"], a["o"], a["odt"], None)
+
+
+def test_decode_checks(lib):
+    assert decode(lib, hd=96) == UNS
+    assert decode(lib, hv=7) == UNS
+    assert decode(lib, st=None) == INV
+    assert decode(lib, st=P[5] + 4) == INV              # state must be 16-byte aligned
+    assert decode(lib, o=P[5] + 4096) == INV            # o inside the state
+    assert decode(lib, B=-1) == INV
+    assert decode(lib, vs=100) == INV
+
+
+def norm(lib, **kw):
+    a = dict(o=P[0], odt=BF16, z=P[1], w=P[2], zdt=BF16, eps=1e-6, rows=100, dim=128, y=P[3], ydt=BF16)
+    a.update(kw)
+    return lib.agnes_gdn_gated_rmsnorm(a["o"], a["odt"], a["z"], a["w"], a["zdt"], a["eps"], a["rows"], a["dim"],
+                                       a["y"], a["ydt"], None)
+
+
+def test_norm_checks(lib):
+    assert norm(lib, dim=64) == UNS
+    assert norm(lib, rows=-1) == INV
+    assert norm(lib, o=None) == INV
+    assert norm(lib, y=P[0] + 256) == INV               # partial overlap of o and y
+    assert norm(lib, y=P[0], ydt=F32) == INV            # aliasing needs equal dtypes
+    assert norm(lib, y=P[1] + 16) == INV                # y overlaps z
+    assert norm(lib, eps=-1.0) == INV
