@@ -1,0 +1,212 @@
+"""Benchmark of the gated delta-rule layer on one MI355X.
+
+One step = the full-layer prefill chain on T = 8192 tokens of one sequence with the layer's
+shapes (16 key / 48 value heads of 128, hidden 5120): kernel-4 causal conv + SiLU + L2 norm of
+q/k over the 10240 q|k|v channels -> chunked gated delta rule (chunk 64, fp32 state) -> gated
+RMSNorm.  `value` is tokens/s of that chain.  The same run also times the batched decode step
+(256 sequences, one token each, fp32 states updated in place) and reports its state HBM GB/s.
+
+Inputs are synthetic (seeded), generated on the host and resident in HBM before timing.
+
+    python bench.py [--steps K] [--warmup W] [--decode-steps D] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "delta-layer prefill tokens/s (T=8192) + decode state HBM GB/s, 1 MI355X"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense fp16/bf16 matrix cores, TFLOP/s
+
+T = 8192
+HK, HV, D, CH = 16, 48, 128, 64
+# Canonical chunked-recurrence FLOPs per token (WY/UT form, per 64-token chunk and key group:
+# Gram K K^T and Q K^T, then per value head two C x C x d products for the WY factors, plus
+# per value head three C x d x d state products and one C x C x d intra-chunk product).
+FLOP_PER_CHUNK_GROUP = 2 * (2 * CH * CH * D + 3 * 2 * CH * CH * D) + 3 * 2 * (3 * CH * D * D + CH * CH * D)
+FLOP_PER_TOKEN = FLOP_PER_CHUNK_GROUP * HK // CH                      # 7,602,176
+PREFILL_BYTES = T * (2 * HK * D * 2 + HV * D * 2 + HV * D * 2 + 2 * HV * 4) + HV * D * D * 4  # q,k,v,o,g,beta + final state
+CONV_BYTES = T * 10240 * 2 * 2 + 10240 * 4 * 2                        # x in, y out, weights
+NORM_BYTES = T * HV * D * 2 * 3 + D * 2                               # o, z in, y out, weight
+DECODE_B = 256
+DECODE_BYTES = DECODE_B * HV * D * D * 4 * 2 + DECODE_B * (2 * HK * D * 2 + HV * D * 2 + HV * D * 2 + 2 * HV * 4)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--decode-steps", type=int, default=200)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=1024, help="tokens of the oracle CPU sample")
+    return p.parse_args()
+
+
+def to_dev(a, torch):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def cpu_baseline(cfg, ntok):
+    """The fp64 oracle (as it stands) on the first `ntok` tokens of the same chain."""
+    import oracle
+    t0 = time.perf_counter()
+    x = cfg["x"][:ntok]
+    y, _ = oracle.causal_conv(x, cfg["conv_w"], np.array([0, ntok]), None, l2_heads=32)
+    q = y[:, :2048].reshape(ntok, HK, D)
+    k = y[:, 2048:4096].reshape(ntok, HK, D)
+    v = y[:, 4096:].reshape(ntok, HV, D)
+    o, _ = oracle.recurrence(q, k, v, cfg["g"][:ntok], cfg["beta"][:ntok])
+    oracle.gated_rmsnorm(o, cfg["z"][:ntok], cfg["norm_w"])
+    dt = time.perf_counter() - t0
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {ntok} of {T} tokens of the same chain (conv+L2, recurrence over all 48 "
+                      f"value heads, gated RMSNorm), numpy fp64, single-threaded token loop; "
+                      f"{dt:.1f} s; host cpu_count={os.cpu_count()}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer shards by heads or sequences with no collective; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gated_delta_rule_35_amd as gdn
+    from synth import make_config, decode_step_inputs
+
+    t_gen = time.perf_counter()
+    cfg = make_config(1)
+    dec = make_config(3)
+    print(f"# inputs generated in {time.perf_counter() - t_gen:.1f} s", file=sys.stderr, flush=True)
+
+    x = to_dev(cfg["x"], torch)
+    w = to_dev(cfg["conv_w"], torch)
+    g = to_dev(cfg["g"], torch)
+    beta = to_dev(cfg["beta"], torch)
+    z = to_dev(cfg["z"], torch)
+    nw = to_dev(cfg["norm_w"], torch)
+    cu = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    y = torch.empty((T, 10240), dtype=torch.bfloat16, device="cuda")
+    o = torch.empty((T, HV, D), dtype=torch.bfloat16, device="cuda")
+    fin = torch.empty((1, HV, D, D), dtype=torch.float32, device="cuda")
+    out = torch.empty((T, HV, D), dtype=torch.bfloat16, device="cuda")
+    q = y[:, :2048].view(T, HK, D)
+    k = y[:, 2048:4096].view(T, HK, D)
+    v = y[:, 4096:].view(T, HV, D)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        gdn.conv(x, w, y=y, cu_seqlens=cu, l2norm_heads=32)
+        if ev is not None:
+            ev[1].record()
+        gdn.prefill_chunked(q, k, v, g, beta, cu, final_state=fin, o=o)
+        if ev is not None:
+            ev[2].record()
+        gdn.gated_rmsnorm(o, z, nw, y=out)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_conv = np.mean([e[0].elapsed_time(e[1]) for e in evs])
+    ms_pre = np.mean([e[1].elapsed_time(e[2]) for e in evs])
+    ms_norm = np.mean([e[2].elapsed_time(e[3]) for e in evs])
+    ms_step = np.mean([e[0].elapsed_time(e[3]) for e in evs])
+    value = T * args.steps / wall
+
+    # ---- decode: 256 sequences, fp32 states in place
+    state = to_dev(dec["state"], torch)
+    cache = to_dev(dec["conv_cache"], torch)
+    cw = to_dev(dec["conv_w"], torch)
+    ring = []
+    for s in range(4):
+        d = decode_step_inputs(s)
+        ring.append({kk: to_dev(vv, torch) for kk, vv in d.items()})
+    yd = torch.empty((DECODE_B, 10240), dtype=torch.bfloat16, device="cuda")
+    od = torch.empty((DECODE_B, HV, D), dtype=torch.bfloat16, device="cuda")
+
+    def dstep(i, ev=None):
+        d = ring[i % len(ring)]
+        if ev is not None:
+            ev[0].record()
+        gdn.conv(d["x"], cw, y=yd, cu_seqlens=None, conv_state=cache, l2norm_heads=32)
+        if ev is not None:
+            ev[1].record()
+        gdn.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, o=od)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(5):
+        dstep(i)
+    torch.cuda.synchronize()
+    devs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.decode_steps)]
+    for i in range(args.decode_steps):
+        dstep(i, devs[i])
+    torch.cuda.synchronize()
+    ms_dconv = np.mean([e[0].elapsed_time(e[1]) for e in devs])
+    ms_dec = np.mean([e[1].elapsed_time(e[2]) for e in devs])
+    dec_gbs = DECODE_BYTES / (ms_dec * 1e-3) / 1e9
+
+    pre_tflops = FLOP_PER_TOKEN * T / (ms_pre * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "delta-layer prefill chain, T=8192, 1 sequence: conv(k=4)+SiLU+L2 -> "
+                               "chunked gated delta rule (chunk 64) -> gated RMSNorm",
+                   "T": T, "num_k_heads": HK, "num_v_heads": HV, "head_dim": D, "chunk": CH,
+                   "io_dtype": "bf16", "matrix_core_operands": "fp16", "accumulate": "fp32",
+                   "state": "fp32", "parallelism": "none (1 GPU)"},
+        "kernels_ms": {"conv": round(ms_conv, 4), "prefill_chunked": round(ms_pre, 4),
+                       "gated_rmsnorm": round(ms_norm, 4), "chain_events": round(ms_step, 4)},
+        "roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel", "achieved": round(pre_tflops, 2),
+                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(pre_tflops / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": None, "flops_per_launch": FLOP_PER_TOKEN * T,
+                     "hbm_GBps_algorithmic": round(PREFILL_BYTES / (ms_pre * 1e-3) / 1e9, 1)},
+        "streaming_kernels": {
+            "conv_GBps": round(CONV_BYTES / (ms_conv * 1e-3) / 1e9, 1),
+            "gated_rmsnorm_GBps": round(NORM_BYTES / (ms_norm * 1e-3) / 1e9, 1)},
+        "decode": {"batch": DECODE_B, "steps": args.decode_steps, "us_per_step": round(ms_dec * 1e3, 2),
+                   "tokens_per_s": round(DECODE_B / (ms_dec * 1e-3), 1),
+                   "conv_decode_us": round(ms_dconv * 1e3, 2),
+                   "roofline": {"bound": "hbm", "kernel": "decode_step_kernel", "achieved": round(dec_gbs, 1),
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                                "traffic": None, "bytes_per_launch": DECODE_BYTES}},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -9,13 +9,16 @@ import numpy as np
 def f32_to_bf16_bits(x):
     """Round fp32 values to bf16 (RNE) and return the uint16 bit patterns."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = ((u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)) & np.uint64(0xFFFF)
+    u = x.view(np.uint32)
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u                      # wraps only for NaN patterns, which are replaced below
+    r >>= np.uint32(16)
+    out = r.astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
-        r = np.where(nan, ((u >> np.uint64(16)) | np.uint64(0x40)) & np.uint64(0xFFFF), r)
-    return r.astype(np.uint16)
+        out[nan] = ((u[nan] >> np.uint32(16)) | np.uint32(0x40)).astype(np.uint16)
+    return out
 
 
 def bf16_bits_to_f32(bits):
