@@ -102,6 +102,7 @@ def main():
     o = torch.empty((T, HV, D), dtype=torch.bfloat16, device="cuda")
     fin = torch.empty((1, HV, D, D), dtype=torch.float32, device="cuda")
     out = torch.empty((T, HV, D), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(gdn.prefill_workspace_size(1, T, HK, HV, torch.bfloat16), dtype=torch.uint8, device="cuda")
     q = y[:, :2048].view(T, HK, D)
     k = y[:, 2048:4096].view(T, HK, D)
     v = y[:, 4096:].view(T, HV, D)
@@ -112,7 +113,7 @@ def main():
         gdn.conv(x, w, y=y, cu_seqlens=cu, l2norm_heads=32)
         if ev is not None:
             ev[1].record()
-        gdn.prefill_chunked(q, k, v, g, beta, cu, final_state=fin, o=o)
+        gdn.prefill_chunked(q, k, v, g, beta, cu, final_state=fin, o=o, workspace=ws)
         if ev is not None:
             ev[2].record()
         gdn.gated_rmsnorm(o, z, nw, y=out)

@@ -24,6 +24,10 @@ HIP_FLAGS = [
     # gfx950 packed fp32 arithmetic is disabled: scalar fp32 code only.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
+    # Schedule for instruction-level parallelism: the kernels run one or two waves per SIMD
+    # (LDS-bound occupancy), so hiding LDS and matrix-core latency inside a wave matters more
+    # than keeping register counts low.
+    "-mllvm", "-amdgpu-sched-strategy=max-ilp",
 ]
 
 

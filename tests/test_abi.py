@@ -104,6 +104,14 @@ def test_prefill_checks(lib):
     assert prefill(lib, o=P[0] + 64) == INV             # o overlaps q
     assert prefill(lib, sc=float("inf")) == INV
     assert prefill(lib, odt=3) == INV
+    # bf16 inputs need a workspace: missing, too small or misaligned -> AGNES_ERR_WORKSPACE
+    need = lib.agnes_gdn_prefill_workspace_size(1, 64, 2, 6, 128, BF16)
+    assert need > 0 and need % 256 == 0
+    assert prefill(lib) == WS
+    assert prefill(lib, ws=P[9], wsb=need - 1) == WS
+    assert prefill(lib, ws=P[9] + 16, wsb=need) == WS
+    assert lib.agnes_gdn_prefill_workspace_size(3, 1000, 2, 6, 128, BF16) > need
+    assert lib.agnes_gdn_prefill_workspace_size(1, 64, 2, 6, 128, F32) == 0
     assert lib.agnes_gdn_prefill_workspace_size(1, 64, 2, 6, 64, BF16) == 0
     assert lib.agnes_gdn_prefill_workspace_size(1, 64, 2, 5, 128, BF16) == 0
 
