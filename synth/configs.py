@@ -140,9 +140,9 @@ def decode_state_inputs(rng, batch):
     return dict(state=state, conv_cache=conv_cache, conv_w=conv_w, batch=batch, **L)
 
 
-def decode_step_inputs(step, batch=256, seed=1003):
+def decode_step_inputs(step, batch=256, seed=1003, conv_input=True):
     """Inputs of decode step ``step`` (seeded by (seed, step)): q,k unit bf16, v bf16,
-    g/beta fp32 and the raw conv input x [batch, 10240] bf16."""
+    g/beta fp32 and (``conv_input``) the raw conv input x [batch, 10240] bf16."""
     L = LAYER
     rng = np.random.default_rng([seed, step])
     q = f32_to_bf16_bits(unit_vectors(rng, (batch, L["num_k_heads"], L["head_dim"])))
@@ -150,9 +150,11 @@ def decode_step_inputs(step, batch=256, seed=1003):
     v = f32_to_bf16_bits(rng.standard_normal((batch, L["num_v_heads"], L["head_dim"]),
                                              dtype=np.float32))
     g, beta = gate_draws(rng, (batch, L["num_v_heads"]))
-    x = f32_to_bf16_bits(rng.standard_normal((batch, L["conv_channels"]), dtype=np.float32)
-                         * np.float32(PROJ_STD))
-    return dict(q=q, k=k, v=v, g=g, beta=beta, x=x)
+    out = dict(q=q, k=k, v=v, g=g, beta=beta)
+    if conv_input:
+        out["x"] = f32_to_bf16_bits(rng.standard_normal((batch, L["conv_channels"]), dtype=np.float32)
+                                    * np.float32(PROJ_STD))
+    return out
 
 
 def make_config(index, seed=None):

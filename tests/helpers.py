@@ -45,3 +45,19 @@ def bf16_ulps(gpu_bits, ref):
     """Distance in bf16 ulps between GPU bf16 results and the round-to-nearest-even of ref."""
     rb = f32_to_bf16_bits(np.asarray(ref, np.float64).astype(np.float32))
     return np.abs(_ordered(np.asarray(gpu_bits, np.uint16)) - _ordered(rb))
+
+
+def check_bf16_out(gpu_bits, ref, abs_tol=0.0, exact_frac=0.999):
+    """bf16 results against the fp64 reference: bit-exact (equal to RNE(ref)) for at least
+    ``exact_frac`` of the elements, and each element within one bf16 ulp of RNE(ref) or within
+    ``abs_tol`` of ref.  ``abs_tol`` covers results that fp32 arithmetic cannot round correctly
+    (cancellation in a short fp32 sum leaves an absolute, not a relative, error)."""
+    ref = np.asarray(ref, np.float64)
+    u = bf16_ulps(gpu_bits, ref)
+    exact = float((u == 0).mean())
+    bad = u > 1
+    if bad.any():
+        err = np.abs(as_f64(np.asarray(gpu_bits)[bad]) - ref[bad])
+        assert err.max() <= abs_tol, f"{int(bad.sum())} elements > 1 ulp, max abs err {err.max():.3e}"
+    assert exact >= exact_frac, f"bit-exact fraction {exact}"
+    return exact

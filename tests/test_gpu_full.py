@@ -1,0 +1,145 @@
+"""GPU parity at the layer's full workload sizes (same launch configuration as bench.py).
+
+Every call is checked on identical input bytes; the inputs of a later call in the layer chain
+come from the oracle's result of the earlier call (rounded to the stored dtype), never from the
+GPU.  Large workloads are checked on sampled sequences / value heads that the fp64 oracle
+computes one by one.  Tolerances as in test_gpu_parity.py (rel-L2 2e-3 on an fp32 output for
+bf16 inputs; bf16 outputs within one ulp of the correctly rounded value).
+"""
+import concurrent.futures as cf
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import f32_to_bf16_bits, make_config, decode_step_inputs, LAYER
+from tests.helpers import dev, host, rel_l2, bf16_ulps, check_bf16_out
+
+# fp32 sum of 4 conv taps (|w| <= 1/2, |x| < 8): rounding error <= 16 * 4 * 2^-24 ~ 4e-6 before
+# SiLU (slope <= 1.1) and the L2 scaling; near-cancelling sums are exact only to this absolute level.
+CONV_ABS_TOL = 1e-5
+
+torch = pytest.importorskip("torch")
+import gated_delta_rule_35_amd as gdn  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+HK, HV, D = LAYER["num_k_heads"], LAYER["num_v_heads"], LAYER["head_dim"]
+HEADS10 = list(range(0, HV, 5))  # every position in a key group is covered (0, 5, 10 -> 0, 2, 1 mod 3)
+
+
+def _views(y, T):
+    return y[:, :2048].reshape(T, HK, D), y[:, 2048:4096].reshape(T, HK, D), y[:, 4096:].reshape(T, HV, D)
+
+
+def _prefill(q, k, v, g, beta, cu, s0=None, o_dtype=torch.float32):
+    o, fin = gdn.prefill_chunked(dev(q), dev(k), dev(v), dev(g), dev(beta), dev(cu),
+                                 initial_state=None if s0 is None else dev(s0), o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    return host(o), host(fin)
+
+
+def test_full_layer_prefill_chain_t8192():
+    """Layer chain at T = 8192: conv + SiLU + L2, chunked prefill, gated RMSNorm; each call on the
+    oracle's inputs, plus the all-GPU chain against the fp64 chain (bf16 hand-offs between calls)."""
+    cfg = make_config(1)
+    T = 8192
+    cu = cfg["cu_seqlens"]
+    # ---- conv call (all 10240 channels)
+    yg = gdn.conv(dev(cfg["x"]), dev(cfg["conv_w"]), cu_seqlens=dev(cu), l2norm_heads=32)
+    torch.cuda.synchronize()
+    yr, _ = oracle.causal_conv(cfg["x"], cfg["conv_w"], cu, None, l2_heads=32)
+    ex = check_bf16_out(host(yg), yr, CONV_ABS_TOL)
+    print(f"conv T=8192: bit-exact fraction {ex:.6f}")
+    # ---- prefill call on the oracle's conv output (rounded to bf16)
+    yb = f32_to_bf16_bits(yr.astype(np.float32))
+    q, k, v = _views(yb, T)
+    heads = [0, 1, 2, 23, 46, 47]
+    o, fin = _prefill(q, k, v, cfg["g"], cfg["beta"], cu)
+    ro, rf = oracle.recurrence(q, k, v, cfg["g"], cfg["beta"], cu, heads=heads)
+    eo, ef = rel_l2(o[:, heads], ro[:, heads]), rel_l2(fin[:, heads], rf[:, heads])
+    print(f"prefill T=8192 rel-L2 o={eo:.3e} state={ef:.3e}")
+    assert eo <= 2e-3 and ef <= 2e-3
+    # ---- gated RMSNorm call on the oracle's output (rounded to bf16)
+    ob = f32_to_bf16_bits(ro[:, heads].astype(np.float32))
+    zs = np.ascontiguousarray(cfg["z"][:, heads])
+    yn = gdn.gated_rmsnorm(dev(ob), dev(zs), dev(cfg["norm_w"]))
+    torch.cuda.synchronize()
+    rn = oracle.gated_rmsnorm(ob, zs, cfg["norm_w"])
+    check_bf16_out(host(yn), rn)
+    # ---- the all-GPU chain against the fp64 chain (three bf16 hand-offs)
+    y2 = gdn.conv(dev(cfg["x"]), dev(cfg["conv_w"]), cu_seqlens=dev(cu), l2norm_heads=32)
+    qg, kg, vg = y2[:, :2048].view(T, HK, D), y2[:, 2048:4096].view(T, HK, D), y2[:, 4096:].view(T, HV, D)
+    og, _ = gdn.prefill_chunked(qg, kg, vg, dev(cfg["g"]), dev(cfg["beta"]), dev(cu))
+    yc = gdn.gated_rmsnorm(og, dev(cfg["z"]), dev(cfg["norm_w"]))
+    torch.cuda.synchronize()
+    chain_ref = oracle.gated_rmsnorm(ro[:, heads], zs, cfg["norm_w"])
+    ec = rel_l2(host(yc)[:, heads], chain_ref)
+    print(f"all-GPU chain vs fp64 chain rel-L2 = {ec:.3e}")
+    assert ec <= 1e-2  # three bf16 roundings (~1.7e-3 each) plus the recurrence's own error
+
+
+def test_long_prefill_t65536_with_initial_state():
+    s = make_config(2)
+    o, fin = _prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["cu_seqlens"], s["initial_state"])
+    ro, rf = oracle.recurrence(s["q"], s["k"], s["v"], s["g"], s["beta"], s["cu_seqlens"],
+                               s["initial_state"], heads=HEADS10)
+    eo, ef = rel_l2(o[:, HEADS10], ro[:, HEADS10]), rel_l2(fin[:, HEADS10], rf[:, HEADS10])
+    ew = rel_l2(o[:128, HEADS10], ro[:128, HEADS10])  # where the initial state still dominates
+    print(f"T=65536 rel-L2 o={eo:.3e} state={ef:.3e} first-128={ew:.3e}")
+    assert eo <= 2e-3 and ef <= 2e-3 and ew <= 2e-3
+
+
+def test_varlen_prefill_32_sequences():
+    s = make_config(4)
+    cu = s["cu_seqlens"]
+    lens = np.diff(cu)
+    o, fin = _prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], cu, s["initial_state"])
+    picks = sorted({0, 1, int(np.argmin(lens)), int(np.argmax(lens))})
+    for n in picks:
+        a, b = cu[n], cu[n + 1]
+        ro, rf = oracle.recurrence(s["q"][a:b], s["k"][a:b], s["v"][a:b], s["g"][a:b], s["beta"][a:b],
+                                   None, s["initial_state"][n:n + 1], heads=HEADS10)
+        eo = rel_l2(o[a:b, HEADS10], ro[:, HEADS10])
+        ef = rel_l2(fin[n, HEADS10], rf[0, HEADS10])
+        ew = rel_l2(o[a:a + 128, HEADS10], ro[:128, HEADS10])
+        print(f"seq {n} len {b - a}: rel-L2 o={eo:.3e} state={ef:.3e} first-128={ew:.3e}")
+        assert eo <= 2e-3 and ef <= 2e-3 and ew <= 2e-3
+
+
+def test_batched_decode_1000_steps():
+    """256 sequences, 1000 consecutive seeded steps, fp32 states updated in place; the oracle
+    follows sequences 0, 85, 170, 255 (all 48 heads) through every step."""
+    d = make_config(3)
+    picks = [0, 85, 170, 255]
+    state = dev(d["state"])
+    ref_state = d["state"][picks].astype(np.float64)
+    worst = 0.0
+    with cf.ThreadPoolExecutor(8) as ex:
+        for s0 in range(0, 1000, 100):
+            steps = list(ex.map(lambda i: decode_step_inputs(i, conv_input=False), range(s0, s0 + 100)))
+            for inp in steps:
+                o = gdn.decode_step(dev(inp["q"]), dev(inp["k"]), dev(inp["v"]), dev(inp["g"]), dev(inp["beta"]),
+                                    state, o_dtype=torch.float32)
+                ro, ref_state = oracle.decode_step(inp["q"][picks], inp["k"][picks], inp["v"][picks],
+                                                   inp["g"][picks], inp["beta"][picks], ref_state)
+                worst = max(worst, rel_l2(host(o)[picks], ro))
+    torch.cuda.synchronize()
+    es = rel_l2(host(state)[picks], ref_state)
+    print(f"decode 1000 steps: worst per-step o rel-L2 {worst:.3e}, final state rel-L2 {es:.3e}")
+    assert worst <= 1e-5 and es <= 1e-5
+
+
+def test_decode_conv_cache_full_size():
+    """Decode-mode conv at the decode workload's shape: [256, 10240] inputs, [256, 10240, 3] cache."""
+    d = make_config(3)
+    cache = dev(d["conv_cache"])
+    ref_cache = d["conv_cache"]
+    for step in range(3):
+        x = decode_step_inputs(step)["x"]
+        y = gdn.conv(dev(x), dev(d["conv_w"]), cu_seqlens=None, conv_state=cache, l2norm_heads=32)
+        torch.cuda.synchronize()
+        ry, rc = oracle.causal_conv(x, d["conv_w"], np.arange(257), ref_cache, l2_heads=32)
+        check_bf16_out(host(y), ry, CONV_ABS_TOL)
+        np.testing.assert_array_equal(oracle.as_f64(host(cache)), rc)
+        ref_cache = host(cache)

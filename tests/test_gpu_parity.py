@@ -4,8 +4,9 @@ Shapes span several 64-token chunks and ragged tails; tolerances (rel-L2 against
   * bf16-input recurrence (fp16 matrix-core operands, fp32 state): 2e-3, on an fp32 `o`;
     the bf16 `o` of the same call must be the round-to-nearest-even of the fp32 `o`, bit for bit;
   * fp32-input recurrence and every decode step (fp32 arithmetic throughout): 1e-5;
-  * conv / gated RMSNorm with bf16 outputs: within 1 bf16 ulp of the correctly rounded fp64
-    value everywhere and bit-exact for >= 99.9 % of elements; fp32 outputs: 1e-6.
+  * conv / gated RMSNorm with bf16 outputs: bit-exact (the correctly rounded fp64 value) for
+    >= 99.9 % of elements and within 1 bf16 ulp elsewhere, except where a near-cancelling fp32
+    sum of the 4 conv taps leaves an absolute error <= 1e-5 (CONV_ABS_TOL); fp32 outputs: 1e-6.
 """
 import numpy as np
 import pytest
@@ -13,7 +14,11 @@ import pytest
 import oracle
 from synth import f32_to_bf16_bits, unit_vectors
 from synth.configs import sequence_inputs, make_config
-from tests.helpers import dev, host, rel_l2, bf16_ulps
+from tests.helpers import dev, host, rel_l2, bf16_ulps, check_bf16_out
+
+# fp32 sum of 4 conv taps (|w| <= 1/2, |x| < 8): rounding error <= 16 * 4 * 2^-24 ~ 4e-6 before
+# SiLU (slope <= 1.1) and the L2 scaling; near-cancelling sums are exact only to this absolute level.
+CONV_ABS_TOL = 1e-5
 
 torch = pytest.importorskip("torch")
 import gated_delta_rule_35_amd as gdn  # noqa: E402
@@ -91,11 +96,8 @@ def _conv_case(rng, lens, C, dtype, with_state, l2):
     return conv(x), conv(w), (conv(st) if st is not None else None), cu
 
 
-def _check_bf16_out(gpu_bits, ref):
-    u = bf16_ulps(gpu_bits, ref)
-    exact = float((u == 0).mean())
-    assert u.max() <= 1, f"max ulp {u.max()}"
-    assert exact >= 0.999, f"bit-exact fraction {exact}"
+def _check_bf16_out(gpu_bits, ref, abs_tol=CONV_ABS_TOL):
+    check_bf16_out(gpu_bits, ref, abs_tol)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
