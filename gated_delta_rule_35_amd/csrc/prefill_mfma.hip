@@ -11,32 +11,34 @@
 //   O  = diag(exp gamma) Q S^T + P U,  P = lower_incl(exp(gamma_r - gamma_s) q_r.k_s)
 //   S <- exp(gamma_63) S + (diag(exp(gamma_63 - gamma)) U)^T K
 // Rows past the end of a partial chunk are zero with beta = g = 0 and contribute nothing.
-// (I + A) U = R' is solved by block forward substitution over four 16-row blocks,
-//   U_i = X_ii (R'_i - sum_{k<i} A_ik U_k),  X_ii = (I + A_ii)^-1.
+// X = (I + A)^-1 is lower triangular and depends only on the inputs, so U = X R' is one
+// product; X is built by blocks of 16: X_ii = (I + A_ii)^-1 by forward substitution, then
+// X_ij = -X_ii sum_{k=j..i-1} A_ik X_kj for i > j, by increasing i - j.
 //
 // Three launches on the caller's stream:
 //  1. chunk_offsets: first chunk index of every sequence (prefix sum of ceil(len / 64)).
-//  2. prep (all chunks in parallel, one workgroup per chunk and key group): the Gram matrices
-//     K K^T and Q K^T once per key group on matrix cores, then per value head of the group the
-//     decay-scaled P, the blocks -A_ik, the fp32 forward-substitution inverses X_ii and the
-//     per-row gates, written as one 14 KiB record per (chunk, value head) in the workspace.
-//     Everything in it depends only on the inputs, not on the state.
+//  2. prep (all chunks in parallel, one workgroup per chunk and value head): the Gram matrices
+//     K K^T and Q K^T on matrix cores, then in fp32 the decay-scaled P, A and X (the blocks
+//     of X off the diagonal on fp32 matrix cores), written as
+//     one 19 KiB record per (chunk, value head), and (first value head of a key group) the
+//     fp16 image of the chunk's q and k rows, 34 KiB per (chunk, key group).  Everything in
+//     them depends only on the inputs, not on the state.
 //  3. scan (serial over chunks): one workgroup of 4 waves per (sequence, value head, block of
 //     32 value rows); the value rows of S are independent, so each workgroup scans its own
 //     [32 x 128] fp32 slice of the state.  Waves 0 and 1 own one 16-wide value tile each and
 //     keep their slice of S^T in matrix-core accumulators for the whole sequence; per chunk
-//     they run Q S^T, K S^T, the block substitution for U, P U and the state update.  A 16x16
-//     result fragment is reused as the next product's operand without leaving registers: the
-//     contraction index of a 16x16x32 product may be permuted as long as both operands use
-//     the same permutation, so two result fragments side by side form a B operand and the
-//     matching A operand is read from LDS as two 8-byte pieces (K^T pieces come straight from
-//     the row-major K tile through the gfx950 transposing LDS read).  Waves 2 and 3 only load:
-//     they stage chunk c+1 (Q, K; the record and the V slice) into double-buffered LDS while
-//     waves 0 and 1 work on chunk c, with their global loads issued a further chunk ahead,
-//     so each chunk costs one workgroup barrier.  Each role runs its own loop with the same
-//     barrier count, so registers are allocated per role.
+//     they run Q S^T, K S^T, U = X R', P U and the state update.  A 16x16 result fragment is
+//     reused as the next product's operand without leaving registers: the contraction index
+//     of a 16x16x32 product may be permuted as long as both operands use the same
+//     permutation, so two result fragments side by side form a B operand and the matching A
+//     operand is read from LDS as two 8-byte pieces (K^T pieces come straight from the
+//     row-major K tile through the gfx950 transposing LDS read).  Wave 2 copies chunk c+1
+//     (q/k image, record, V slice) into double-buffered LDS with direct global -> LDS loads
+//     while waves 0 and 1 work on chunk c; wave 3 writes out the output of chunk c-1.  Each
+//     chunk costs one workgroup barrier; each role runs its own loop with the same barrier
+//     count, so registers are allocated per role.
 // Number formats: bf16 inputs widen exactly to fp16 (normal range); fp32 intermediates
-// (S, R', U, P, A, X) are rounded to fp16 once per use (2^-11 relative); every product
+// (S, R', U, P, X) are rounded to fp16 once per use (2^-11 relative); every product
 // accumulates in fp32 and the state itself stays fp32.
 #include "common.h"
 #include "launch.h"
@@ -48,8 +50,9 @@ constexpr int C = 64;        // chunk
 constexpr int D = 128;       // head dim (key and value)
 constexpr int LDQ = D + 8;   // fp16 row stride of staged Q/K rows
 constexpr int LDT = C + 8;   // fp16 row stride of [*, chunk] tiles
-constexpr int LDB = 16 + 8;  // fp16 row stride of 16x16 blocks
 constexpr int NCW = 2;       // consumer waves, one 16-wide value tile each
+constexpr int NCP = 5;       // copy waves
+constexpr int NWAVES = NCW + NCP + 1;  // + one output wave
 constexpr int DVB = 16 * NCW;
 constexpr int NB = D / DVB;  // scan workgroups per value head
 constexpr int LDV = DVB + 8; // bf16 row stride of the staged V slice
@@ -59,21 +62,31 @@ constexpr int LDV = DVB + 8; // bf16 row stride of the staged V slice
 // is laid out as the padded LDS image the consumers read (rows padded against bank conflicts).
 struct RecImage {
   _Float16 P[mp::C][mp::LDT];      // P, row-major, zero above the diagonal
-  _Float16 Ln[6][16][mp::LDB];     // -A_ik (i > k), row-major blocks
-  _Float16 Xd[4][16][mp::LDB];     // X_ii = (I + A_ii)^-1, row-major blocks
+  _Float16 X[mp::C][mp::LDT];      // X = (I + A)^-1, row-major, zero above the diagonal
   float gt[3][mp::C];              // beta, exp(gamma), exp(gamma_63 - gamma)
-  float pad[192];                  // to a whole number of 1 KiB copy steps
+  float pad[64];                   // to a whole number of 1 KiB copy steps
 };
-static_assert(sizeof(RecImage) == 18 * 1024, "record image is copied in 1 KiB steps");
+static_assert(sizeof(RecImage) == 19 * 1024, "record image is copied in 1 KiB steps");
+// Per (chunk, key group) image of the fp16 q and k rows (rows past the chunk end are zero).
+struct QKImage {
+  _Float16 Q[mp::C][mp::LDQ];
+  _Float16 K[mp::C][mp::LDQ];
+};
+static_assert(sizeof(QKImage) == 34 * 1024, "q/k image is copied in 1 KiB steps");
 namespace mp {
 constexpr int REC_BYTES = sizeof(RecImage);
-constexpr int REC_P = offsetof(RecImage, P);
-constexpr int REC_L = offsetof(RecImage, Ln);
-constexpr int REC_X = offsetof(RecImage, Xd);
-constexpr int REC_G = offsetof(RecImage, gt);
+constexpr int QK_BYTES = sizeof(QKImage);
 }  // namespace mp
 
-__host__ __device__ constexpr int lblk(int i, int k) { return i * (i - 1) / 2 + k; }
+// Workspace: [chunk offsets (N+1) int32, 256-aligned] [records: Hv x maxch] [q/k images: Hk x maxch]
+struct WsLayout {
+  size_t rec, qk, bytes;
+  __host__ __device__ WsLayout(int num_seqs, int hv, int hk, int64_t maxch) {
+    rec = (4 * (size_t)(num_seqs + 1) + 255) & ~size_t(255);
+    qk = rec + (size_t)hv * (size_t)maxch * mp::REC_BYTES;
+    bytes = qk + (size_t)hk * (size_t)maxch * mp::QK_BYTES;
+  }
+};
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 static inline int64_t max_chunks(int64_t total, int num_seqs) { return (total + mp::C - 1) / mp::C + num_seqs; }
@@ -116,6 +129,15 @@ typedef __attribute__((address_space(3))) s4v lds_s4v;
 __device__ __forceinline__ h4 lds_tr4(const _Float16* p) {
   const s4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(p));
   return __builtin_bit_cast(h4, v);
+}
+
+// Workgroup barrier ordering LDS only: global stores issued before it may still be in flight
+// (a full __syncthreads would wait for them).  Direct global -> LDS copies are not covered:
+// the issuing wave waits for them (s_waitcnt) before the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // ---------------------------------------------------------------- 1. chunk offsets
@@ -163,141 +185,231 @@ __device__ __forceinline__ int seq_of_chunk(const int32_t* off, int num_seqs, in
 }
 
 // ---------------------------------------------------------------- 2. prep
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
 struct PrepSmem {
-  _Float16 Qs[mp::C][mp::LDQ];
-  _Float16 Ks[mp::C][mp::LDQ];
-  float Gk[mp::C][mp::C + 1];   // K K^T (lower blocks)
-  float Gq[mp::C][mp::C + 1];   // Q K^T (lower blocks)
+  union {
+    struct {
+      uint16_t Q[mp::C][mp::LDQ];   // bf16 q rows as stored (rows >= L: copies of row 0)
+      uint16_t K[mp::C][mp::LDQ];   // bf16 k rows as stored
+    } qk;                           // until the Gram products are done
+    struct {
+      float A[mp::C][mp::C + 1];    // A, fp32 (lower blocks)
+      float X[mp::C][mp::C + 1];    // X = (I + A)^-1, fp32 (lower blocks)
+    } ax;
+  } u;
+  _Float16 P[mp::C][mp::LDT];       // P (lower blocks)
   float gam[mp::C], bet[mp::C];
-  float Ad[4][16][17];          // A_ii, fp32
-  _Float16 Xs[4][16][16];       // X_ii staged for a coalesced copy
 };
 
-__global__ __launch_bounds__(256) void prep_kernel(PrefillArgs a, int64_t maxch) {
+// Lower 16x16 block pair p = 0..9 -> (bi, bj), bi >= bj: (0,0) (1,0) (1,1) (2,0) (2,1) ...
+__device__ __forceinline__ void pair_of(int p, int& bi, int& bj) {
+  bi = 0;
+  while (p > bi) {
+    p -= bi + 1;
+    ++bi;
+  }
+  bj = p;
+}
+
+__device__ __forceinline__ f4 mfma_bf(bf8 a, bf8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mfma_f32(float a, float b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// z + A_ik X_kj on fp32 matrix cores (four 16x16x4 steps; lane (m, g) of step s holds
+// A[m][4s+g] and X[4s+g][m]).
+__device__ __forceinline__ f4 blk_ax(const PrepSmem& sm, int i, int k, int j, int ln, int lg, f4 z) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) z = mfma_f32(sm.u.ax.A[16 * i + ln][16 * k + 4 * s + lg], sm.u.ax.X[16 * k + 4 * s + lg][16 * j + ln], z);
+  return z;
+}
+// -X_ii z with z in result layout (lane (n, g) holds z[4g+e][n]): step s contracts over the
+// rows 4g+s of z, which are the lanes' own element s.
+__device__ __forceinline__ f4 blk_xz(const PrepSmem& sm, int i, int ln, int lg, f4 z) {
+  f4 r = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) r = mfma_f32(-sm.u.ax.X[16 * i + ln][16 * i + 4 * lg + s], z[s], r);
+  return r;
+}
+
+// One workgroup per (chunk, value head); the value heads of a key group are consecutive so
+// that they share the q/k rows in L2.
+__global__ __launch_bounds__(256, 3) void prep_kernel(PrefillArgs a, int64_t maxch) {
   using namespace mp;
   __shared__ PrepSmem sm;
   const int32_t* off = static_cast<const int32_t*>(a.workspace);
-  unsigned char* recs = static_cast<unsigned char*>(a.workspace) + align256(4 * (size_t)(a.num_seqs + 1));
-  const int j = blockIdx.x;
-  const int kh = blockIdx.y;
+  const WsLayout ws(a.num_seqs, a.hv, a.hk, maxch);
+  unsigned char* base = static_cast<unsigned char*>(a.workspace);
+  const unsigned nblk = gridDim.x;
+  unsigned lid = blockIdx.x;
+  if ((nblk & 7u) == 0) lid = (blockIdx.x & 7u) * (nblk >> 3) + (blockIdx.x >> 3);
+  const int grp = a.hv / a.hk;
+  const int z = (int)(lid % (unsigned)grp);
+  const int j = (int)((lid / (unsigned)grp) % (unsigned)maxch);
+  const int kh = (int)(lid / ((unsigned)grp * (unsigned)maxch));
+  const int h = kh * grp + z;
   if (j >= off[a.num_seqs]) return;
   const int n = seq_of_chunk(off, a.num_seqs, j);
   const int64_t start = cu_at(a.cu, n, a.total);
   const int64_t c0 = start + (int64_t)(j - off[n]) * C;
-  int64_t end = cu_at(a.cu, n + 1, a.total);
+  const int64_t end = cu_at(a.cu, n + 1, a.total);
   const int L = (int)((end - c0) < C ? (end - c0) : C);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+  unsigned char* rec = base + ws.rec + ((size_t)h * maxch + j) * REC_BYTES;
 
-  // ---- Q, K rows of the key group -> fp16 LDS
-  const uint16_t* qb = static_cast<const uint16_t*>(a.q) + (int64_t)kh * D;
-  const uint16_t* kb = static_cast<const uint16_t*>(a.k) + (int64_t)kh * D;
+  // ---- q, k rows of the chunk -> LDS (direct copies, 17 x 1 KiB per matrix, spread over the
+  // four waves; the 17th 16-byte piece of a row is padding and re-reads the row's start)
+  {
+    constexpr int QPR = LDQ / 8;
+    const uint16_t* qb = static_cast<const uint16_t*>(a.q) + c0 * a.qk_stride + (int64_t)kh * D;
+    const uint16_t* kb = static_cast<const uint16_t*>(a.k) + c0 * a.qk_stride + (int64_t)kh * D;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int task = tid + 256 * i;
-    const int r = task >> 4, sg = task & 15;
-    const int64_t rr = r < L ? r : 0;
-    const uint4 qv = *reinterpret_cast<const uint4*>(qb + (c0 + rr) * a.qk_stride + 8 * sg);
-    const uint4 kv = *reinterpret_cast<const uint4*>(kb + (c0 + rr) * a.qk_stride + 8 * sg);
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<h8*>(&sm.Qs[r][8 * sg]) = cvt8(r < L ? qv : z);
-    *reinterpret_cast<h8*>(&sm.Ks[r][8 * sg]) = cvt8(r < L ? kv : z);
+    for (int t = 0; t < (2 * QPR + 3) / 4; ++t) {
+      const int i = w + 4 * t;
+      if (i >= 2 * QPR) break;
+      const int ii = i < QPR ? i : i - QPR;
+      const int jj = 64 * ii + lane, r = jj / QPR, pc = jj % QPR;
+      const int64_t o = (int64_t)(r < L ? r : 0) * a.qk_stride + (pc < D / 8 ? 8 * pc : 0);
+      const uint16_t* src = (i < QPR ? qb : kb) + o;
+      uint16_t* dst = (i < QPR ? &sm.u.qk.Q[0][0] : &sm.u.qk.K[0][0]) + 512 * ii;
+      __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)dst, 16, 0, 0);
+    }
   }
-  __syncthreads();
-
-  // ---- Gram tiles (lower blocks): 10 of K K^T, 10 of Q K^T, five per wave
+  if (w == 0) {  // gates: inclusive prefix sum of log-decays; rows >= L get g = beta = 0
+    float gv = lane < L ? a.g[(c0 + lane) * a.hv + h] : 0.f;
+    const float bv = lane < L ? a.beta[(c0 + lane) * a.hv + h] : 0.f;
 #pragma unroll
-  for (int ti = 0; ti < 5; ++ti) {
-    const int tix = w + 4 * ti;
-    const bool isq = tix >= 10;
-    int rem = isq ? tix - 10 : tix, bi = 0;
-    while (rem > bi) { rem -= bi + 1; ++bi; }
-    const int bj = rem;
-    const _Float16 (*Arow)[LDQ] = isq ? sm.Qs : sm.Ks;
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      acc = mfma_16x16x32(*reinterpret_cast<const h8*>(&Arow[16 * bi + ln][32 * ks + 8 * lg]),
-                          *reinterpret_cast<const h8*>(&sm.Ks[16 * bj + ln][32 * ks + 8 * lg]), acc);
-    float (*G)[C + 1] = isq ? sm.Gq : sm.Gk;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) G[16 * bi + 4 * lg + i][16 * bj + ln] = acc[i];
+    for (int o = 1; o < 64; o <<= 1) {
+      const float t = __shfl_up(gv, o, 64);
+      if (lane >= o) gv += t;
+    }
+    sm.gam[lane] = gv;
+    sm.bet[lane] = bv;
+    float* gr = reinterpret_cast<float*>(rec + offsetof(RecImage, gt));
+    gr[lane] = bv;
+    gr[64 + lane] = __expf(gv);
+    gr[128 + lane] = __expf(__shfl(gv, 63, 64) - gv);
   }
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0);
+  lds_barrier();
 
-  const int grp = a.hv / a.hk;
-  for (int hh = 0; hh < grp; ++hh) {
-    const int h = kh * grp + hh;
-    unsigned char* rec = recs + ((size_t)h * (size_t)maxch + (size_t)j) * REC_BYTES;
-    if (w == 0) {  // gates: inclusive prefix sum of log-decays; rows >= L get g = beta = 0
-      float gv = lane < L ? a.g[(c0 + lane) * a.hv + h] : 0.f;
-      const float bv = lane < L ? a.beta[(c0 + lane) * a.hv + h] : 0.f;
+  // ---- Gram blocks K K^T and Q K^T (bf16 matrix cores): wave w takes the lower block pairs
+  // w, w+4, w+8.  The first value head of a key group also writes the fp16 q/k image.
+  f4 gk[3], gq[3];
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float t = __shfl_up(gv, o, 64);
-        if (lane >= o) gv += t;
-      }
-      sm.gam[lane] = gv;
-      sm.bet[lane] = bv;
-      float* gr = reinterpret_cast<float*>(rec + REC_G);
-      gr[lane] = bv;
-      gr[64 + lane] = __expf(gv);
-      gr[128 + lane] = __expf(__shfl(gv, 63, 64) - gv);
+  for (int pi = 0; pi < 3; ++pi) {
+    gk[pi] = gq[pi] = f4{0.f, 0.f, 0.f, 0.f};
+    const int p = w + 4 * pi;
+    if (p >= 10) break;
+    int bi, bj;
+    pair_of(p, bi, bj);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int col = 32 * ks + 8 * lg;
+      const bf8 kbv = *reinterpret_cast<const bf8*>(&sm.u.qk.K[16 * bj + ln][col]);
+      gk[pi] = mfma_bf(*reinterpret_cast<const bf8*>(&sm.u.qk.K[16 * bi + ln][col]), kbv, gk[pi]);
+      gq[pi] = mfma_bf(*reinterpret_cast<const bf8*>(&sm.u.qk.Q[16 * bi + ln][col]), kbv, gq[pi]);
     }
-    __syncthreads();
-    {  // P row r, columns s0..s0+15; A for the same positions
-      const int r = tid >> 2, s0 = 16 * (tid & 3);
-      const int bi = r >> 4, bs = s0 >> 4;
-      const float gr = sm.gam[r], br = sm.bet[r];
-      h8 p0, p1, l0, l1;
+  }
+  if (z == 0) {
+    QKImage* img = reinterpret_cast<QKImage*>(base + ws.qk + ((size_t)kh * maxch + j) * QK_BYTES);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int s = s0 + e;
-        const float d = s <= r ? __expf(gr - sm.gam[s]) : 0.f;
-        const float pv = s <= r ? d * sm.Gq[r][s] : 0.f;
-        const float av = s < r ? br * d * sm.Gk[r][s] : 0.f;
-        if (e < 8) { p0[e] = (_Float16)pv; l0[e] = (_Float16)(-av); }
-        else { p1[e - 8] = (_Float16)pv; l1[e - 8] = (_Float16)(-av); }
-        if (bs == bi) sm.Ad[bi][r & 15][e] = av;
-      }
-      h8* pp = reinterpret_cast<h8*>(rec + REC_P + (r * LDT + s0) * 2);
-      pp[0] = p0;
-      pp[1] = p1;
-      if (bs < bi) {
-        h8* lp = reinterpret_cast<h8*>(rec + REC_L + ((lblk(bi, bs) * 16 + (r & 15)) * LDB) * 2);
-        lp[0] = l0;
-        lp[1] = l1;
-      }
+    for (int t = 0; t < 2 * C * (D / 8) / 256; ++t) {
+      const int i = tid + 256 * t;
+      const bool isk = i >= C * (D / 8);
+      const int r = (i >> 4) & (C - 1), col = 8 * (i & 15);
+      const uint4 v = *reinterpret_cast<const uint4*>(isk ? &sm.u.qk.K[r][col] : &sm.u.qk.Q[r][col]);
+      *reinterpret_cast<h8*>(isk ? &img->K[r][col] : &img->Q[r][col]) = cvt8(r < L ? v : make_uint4(0, 0, 0, 0));
     }
-    __syncthreads();
-    if (w == 0) {  // X_ii = (I + A_ii)^-1: block lg, column ln, right-looking substitution
-      float x[16];
+  }
+  lds_barrier();  // q/k rows are dead from here: their space holds A and X
+
+  // ---- decay-scaled A (fp32) and P (fp16) of the same blocks into LDS
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = r == ln ? 1.f : 0.f;
+  for (int pi = 0; pi < 3; ++pi) {
+    const int p = w + 4 * pi;
+    if (p >= 10) break;
+    int bi, bj;
+    pair_of(p, bi, bj);
+    const int s2 = 16 * bj + ln;
+    const float gs = sm.gam[s2];
 #pragma unroll
-      for (int s = 0; s < 16; ++s)
-#pragma unroll
-        for (int r = s + 1; r < 16; ++r) x[r] = fmaf(-sm.Ad[lg][r][s], x[s], x[r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sm.Xs[lg][r][ln] = (_Float16)x[r];
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * bi + 4 * lg + e;
+      const float d = s2 <= r ? __expf(sm.gam[r] - gs) : 0.f;
+      sm.u.ax.A[r][s2] = s2 < r ? sm.bet[r] * d * gk[pi][e] : 0.f;
+      sm.P[r][s2] = (_Float16)(s2 <= r ? d * gq[pi][e] : 0.f);
     }
-    __syncthreads();
-    if (tid < 128) {  // 64 block rows of 16 fp16 (two 16-byte halves), row stride LDB
-      const int q = tid >> 1, hf = tid & 1;
-      *reinterpret_cast<uint4*>(rec + REC_X + (q * LDB + 8 * hf) * 2) =
-          reinterpret_cast<const uint4*>(&sm.Xs[q >> 4][q & 15][0])[hf];
+  }
+  lds_barrier();
+
+  if (w == 0) {  // diagonal blocks X_bb = (I + A_bb)^-1: block lg, column ln, right-looking
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] = r == ln ? 1.f : 0.f;
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2)
+#pragma unroll
+      for (int r = s2 + 1; r < 16; ++r) x[r] = fmaf(-sm.u.ax.A[16 * lg + r][16 * lg + s2], x[s2], x[r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sm.u.ax.X[16 * lg + r][16 * lg + ln] = x[r];
+  } else {  // P -> record (fp16 rows, zero above the diagonal)
+    for (int t = tid - 64; t < C * C / 8; t += 192) {
+      const int r = t >> 3, s0 = 8 * (t & 7);
+      h8 v = *reinterpret_cast<const h8*>(&sm.P[r][s0]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (s0 + e > r) v[e] = (_Float16)0.f;
+      *reinterpret_cast<h8*>(rec + offsetof(RecImage, P) + (r * LDT + s0) * 2) = v;
     }
+  }
+  lds_barrier();
+  // off-diagonal blocks by levels d = i - j: X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj (fp32)
+  const f4 zf = {0.f, 0.f, 0.f, 0.f};
+  if (w < 3) {  // d = 1: blocks (w+1, w)
+    const int i = w + 1;
+    const f4 x = blk_xz(sm, i, ln, lg, blk_ax(sm, i, w, w, ln, lg, zf));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.u.ax.X[16 * i + 4 * lg + e][16 * w + ln] = x[e];
+  }
+  lds_barrier();
+  if (w < 2) {  // d = 2: blocks (w+2, w)
+    const int i = w + 2;
+    f4 zz = blk_ax(sm, i, w, w, ln, lg, zf);
+    zz = blk_ax(sm, i, w + 1, w, ln, lg, zz);
+    const f4 x = blk_xz(sm, i, ln, lg, zz);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.u.ax.X[16 * i + 4 * lg + e][16 * w + ln] = x[e];
+  }
+  lds_barrier();
+  if (w == 0) {  // d = 3: block (3, 0)
+    f4 zz = blk_ax(sm, 3, 0, 0, ln, lg, zf);
+    zz = blk_ax(sm, 3, 1, 0, ln, lg, zz);
+    zz = blk_ax(sm, 3, 2, 0, ln, lg, zz);
+    const f4 x = blk_xz(sm, 3, ln, lg, zz);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.u.ax.X[48 + 4 * lg + e][ln] = x[e];
+  }
+  lds_barrier();
+  // X -> record (fp16 rows, zero above the diagonal)
+  for (int t = tid; t < C * C / 8; t += 256) {
+    const int r = t >> 3, s0 = 8 * (t & 7);
+    h8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (_Float16)(s0 + e <= r ? sm.u.ax.X[r][s0 + e] : 0.f);
+    *reinterpret_cast<h8*>(rec + offsetof(RecImage, X) + (r * LDT + s0) * 2) = v;
   }
 }
 
 // ---------------------------------------------------------------- 3. scan
-typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
-typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
 
 struct ScanBuf {            // one chunk, filled by direct global -> LDS copies
-  uint16_t Qs[mp::C][mp::LDQ];   // bf16 q rows as stored
-  uint16_t Ks[mp::C][mp::LDQ];   // bf16 k rows as stored
+  QKImage QK;                    // fp16 q, k rows of the key group
   RecImage R;                    // prep record of (chunk, value head)
   uint16_t Vs[mp::C][mp::LDV];   // bf16 v slice [row][value col]
 };
@@ -306,210 +418,212 @@ struct ScanSmem {
   float Os[2][mp::C][mp::DVB + 4];  // output tile, written out by the output wave
 };
 
-__device__ __forceinline__ uint32_t fbits(float x) { return __float_as_uint(x); }
-
-// Split fp32 fragment pairs into bf16 hi + lo parts: x = hi + lo with hi = x truncated to
-// bf16 and lo = bf16(x - hi), 16 significant bits in all (relative error <= 2^-16).
-__device__ __forceinline__ void split_pair(f4 a, f4 b, bf8& hi, bf8& lo) {
-  uint32_t h[4], l[4];
-  const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t u0 = fbits(x[2 * i]), u1 = fbits(x[2 * i + 1]);
-    const float r0 = x[2 * i] - __uint_as_float(u0 & 0xffff0000u);
-    const float r1 = x[2 * i + 1] - __uint_as_float(u1 & 0xffff0000u);
-    h[i] = (u0 >> 16) | (u1 & 0xffff0000u);
-    l[i] = (fbits(r0) >> 16) | (fbits(r1) & 0xffff0000u);
-  }
-  const uint4 hv = make_uint4(h[0], h[1], h[2], h[3]), lv = make_uint4(l[0], l[1], l[2], l[3]);
-  hi = __builtin_bit_cast(bf8, hv);
-  lo = __builtin_bit_cast(bf8, lv);
-}
-
-__device__ __forceinline__ f4 mfma_bf(bf8 a, bf8 b, f4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// bf16 A operand matching a B operand made of two result fragments (see a_perm).
-__device__ __forceinline__ bf8 a_perm_bf(const uint16_t* row, int k0, int lg) {
-  const u16x4 lo = *reinterpret_cast<const u16x4*>(row + k0 + 4 * lg);
-  const u16x4 hi = *reinterpret_cast<const u16x4*>(row + k0 + 16 + 4 * lg);
-  const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-  return __builtin_bit_cast(bf8, make_uint4(l2.x, l2.y, h2.x, h2.y));
-}
-
-// Transposing read of 4 bf16 values (see lds_tr4) -> 64 raw bits.
-__device__ __forceinline__ uint2 lds_tr4_bits(const uint16_t* p) {
-  const s4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(p));
-  return __builtin_bit_cast(uint2, v);
-}
-
 struct Geo {
   int64_t start, end;
   int nchunks, h, kh, dv0, w, lane, ln, lg;
   int64_t sbase;
-  size_t rec0;  // byte offset of this sequence's first record for value head h
+  size_t rec0;  // workspace byte offset of this sequence's first record for value head h
+  size_t qk0;   // workspace byte offset of this sequence's first q/k image for key group kh
   __device__ int len(int c) const {
     const int64_t r = end - start - (int64_t)c * mp::C;
     return (int)(r < mp::C ? r : mp::C);
   }
 };
 
-// Consumer: chunk in buffer B for value tile G.w; sacc holds S^T fragments [key tile].
-__device__ __forceinline__ void consume(const ScanBuf& B, float (*Os)[mp::DVB + 4], const PrefillArgs& a,
-                                        const Geo& G, f4 (&sacc)[8]) {
-  using namespace mp;
-  const int ln = G.ln, lg = G.lg, w = G.w;
-  const RecImage& R = B.R;
-  f4 bet[4], eg[4], egl[4];
-  float vv[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    bet[i] = *reinterpret_cast<const f4*>(&R.gt[0][16 * i + 4 * lg]);
-    eg[i] = *reinterpret_cast<const f4*>(&R.gt[1][16 * i + 4 * lg]);
-    egl[i] = *reinterpret_cast<const f4*>(&R.gt[2][16 * i + 4 * lg]);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) vv[i][e] = bf16_to_f32(B.Vs[16 * i + 4 * lg + e][16 * w + ln]);
-  }
-  h4 lf[6], xf[4];
-#pragma unroll
-  for (int b = 0; b < 6; ++b) lf[b] = *reinterpret_cast<const h4*>(&R.Ln[b][ln][4 * lg]);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) xf[i] = *reinterpret_cast<const h4*>(&R.Xd[i][ln][4 * lg]);
+// Transposing read of 4 bf16 values (same lane pattern as lds_tr4), widened to fp32.
+__device__ __forceinline__ f4 lds_tr4_bf16(const uint16_t* p) {
+  const s4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(p));
+  const uint2 u = __builtin_bit_cast(uint2, v);
+  return f4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+            __uint_as_float(u.y & 0xffff0000u)};
+}
 
-  // Q S^T and K S^T on bf16 matrix cores: q, k exact, S as hi + lo
-  bf8 shi[4], slo[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) split_pair(sacc[2 * ks], sacc[2 * ks + 1], shi[ks], slo[ks]);
-  f4 qs[4], kq[4];
+// K^T operand of the state update for key tile kt, token half ks (see lds_tr4).
+__device__ __forceinline__ h8 kt_operand(const ScanBuf& B, int kt, int ks, int trow, int tcol) {
+  return cat(lds_tr4(&B.QK.K[32 * ks + trow][16 * kt + tcol]), lds_tr4(&B.QK.K[32 * ks + 16 + trow][16 * kt + tcol]));
+}
+
+// Consumer: chunk in buffer B for value tile w; sacc holds S^T fragments [key tile].
+// 60 products of 16x16x32 per chunk: 32 for Q S^T and K S^T, 6 for U = X R', 6 for P U and
+// 16 for the state update; the only dependent steps are R' -> U -> (O, state).  LDS operands
+// are read one step ahead of the products that use them (sched_barrier keeps the order).
+__device__ __forceinline__ void consume(const ScanBuf& B, float (*Os)[mp::DVB + 4], float scale, int w, int ln,
+                                        int lg, f4 (&sacc)[8]) {
+  using namespace mp;
+  const RecImage& R = B.R;
+  const f4 zero = {0.f, 0.f, 0.f, 0.f};
+  h8 qa[2][4], ka[2][4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
-    qs[rt] = f4{0.f, 0.f, 0.f, 0.f};
-    kq[rt] = f4{0.f, 0.f, 0.f, 0.f};
+    qa[0][rt] = a_perm(&B.QK.Q[16 * rt + ln][0], 0, lg);
+    ka[0][rt] = a_perm(&B.QK.K[16 * rt + ln][0], 0, lg);
   }
+  // Q S^T and K S^T: the S^T fragments of key tiles 2ks, 2ks+1 form the B operand of step ks
+  h8 sb[4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
+  for (int ks = 0; ks < 4; ++ks) sb[ks] = b_pair(sacc[2 * ks], sacc[2 * ks + 1]);
+  f4 qs[4], kq[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) qs[rt] = kq[rt] = zero;
+  __builtin_amdgcn_sched_barrier(0);
+  f4 vv[4], bet[4], eg[4];
+  h8 xa[6];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (ks < 3) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        qa[(ks + 1) & 1][rt] = a_perm(&B.QK.Q[16 * rt + ln][0], 32 * (ks + 1), lg);
+        ka[(ks + 1) & 1][rt] = a_perm(&B.QK.K[16 * rt + ln][0], 32 * (ks + 1), lg);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vv[i] = lds_tr4_bf16(&B.Vs[16 * i + 4 * lg + (ln >> 2)][16 * w + 4 * (ln & 3)]);
+        bet[i] = *reinterpret_cast<const f4*>(&R.gt[0][16 * i + 4 * lg]);
+        eg[i] = *reinterpret_cast<const f4*>(&R.gt[1][16 * i + 4 * lg]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xa[i] = a_perm(&R.X[16 * i + ln][0], 0, lg);
+      xa[4] = a_perm(&R.X[32 + ln][0], 32, lg);
+      xa[5] = a_perm(&R.X[48 + ln][0], 32, lg);
+    }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) {
-      const bf8 qa = a_perm_bf(&B.Qs[16 * rt + ln][0], 32 * ks, lg);
-      const bf8 ka = a_perm_bf(&B.Ks[16 * rt + ln][0], 32 * ks, lg);
-      qs[rt] = mfma_bf(qa, shi[ks], qs[rt]);
-      qs[rt] = mfma_bf(qa, slo[ks], qs[rt]);
-      kq[rt] = mfma_bf(ka, shi[ks], kq[rt]);
-      kq[rt] = mfma_bf(ka, slo[ks], kq[rt]);
+      kq[rt] = mfma_16x16x32(ka[ks & 1][rt], sb[ks], kq[rt]);
+      qs[rt] = mfma_16x16x32(qa[ks & 1][rt], sb[ks], qs[rt]);
     }
-  // R' = beta (V - exp(gamma) K S^T), then block substitution for U (fp16 matrix cores)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // R' = beta (V - exp(gamma) K S^T); U = X R' with X = (I + A)^-1 lower triangular
+  f4 rp[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rp[i][e] = bet[i][e] * (vv[i][e] - eg[i][e] * kq[i][e]);
+  const h8 rb0 = b_pair(rp[0], rp[1]), rb1 = b_pair(rp[2], rp[3]);
+  const int trow = 4 * lg + (ln >> 2), tcol = 4 * (ln & 3);
+  h8 pa[6], kta[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pa[i] = a_perm(&R.P[16 * i + ln][0], 0, lg);
+  pa[4] = a_perm(&R.P[32 + ln][0], 32, lg);
+  pa[5] = a_perm(&R.P[48 + ln][0], 32, lg);
+  f4 egl[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) egl[i] = *reinterpret_cast<const f4*>(&R.gt[2][16 * i + 4 * lg]);
+  kta[0] = kt_operand(B, 0, 0, trow, tcol);
+  kta[1] = kt_operand(B, 0, 1, trow, tcol);
   f4 u[4];
-  const f4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f4 wv;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) wv[e] = bet[i][e] * (vv[i][e] - eg[i][e] * kq[i][e]);
-#pragma unroll
-    for (int k = 0; k < i; ++k) wv = mfma_16x16x16(lf[lblk(i, k)], to_h4(u[k]), wv);
-    u[i] = mfma_16x16x16(xf[i], to_h4(wv), zero);
-  }
-  // O = diag(exp gamma) Q S^T + P U, staged in LDS for the output wave
-  const h8 ub0 = b_pair(u[0], u[1]), ub1 = b_pair(u[2], u[3]);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f4 o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = qs[i][e] * eg[i][e];
-    o = mfma_16x16x32(a_perm(&R.P[16 * i + ln][0], 0, lg), ub0, o);
-    if (i >= 2) o = mfma_16x16x32(a_perm(&R.P[16 * i + ln][0], 32, lg), ub1, o);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Os[16 * i + 4 * lg + e][16 * w + ln] = a.scale * o[e];
-  }
-  // S^T <- exp(gamma_63) S^T + K^T (diag(exp(gamma_63 - gamma)) U): bf16, U as hi + lo
+  for (int i = 0; i < 4; ++i) u[i] = mfma_16x16x32(xa[i], rb0, zero);
+  u[2] = mfma_16x16x32(xa[4], rb1, u[2]);
+  u[3] = mfma_16x16x32(xa[5], rb1, u[3]);
+  __builtin_amdgcn_sched_barrier(0);
+  // S^T <- exp(gamma_63) S^T + K^T (diag(exp(gamma_63 - gamma)) U); K^T pieces by transposing reads.
+  // O = diag(exp gamma) Q S^T + P U is interleaved with it and staged in LDS for the output wave.
   f4 ud[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) ud[i][e] = u[i][e] * egl[i][e];
-  bf8 dhi[2], dlo[2];
-  split_pair(ud[0], ud[1], dhi[0], dlo[0]);
-  split_pair(ud[2], ud[3], dhi[1], dlo[1]);
+  const h8 db0 = b_pair(ud[0], ud[1]), db1 = b_pair(ud[2], ud[3]);
+  const h8 ub0 = b_pair(u[0], u[1]), ub1 = b_pair(u[2], u[3]);
   const float dec = R.gt[1][C - 1];
-  const int trow = 4 * lg + (ln >> 2), tcol = 4 * (ln & 3);
 #pragma unroll
   for (int kt = 0; kt < 8; ++kt) {
+    h8 nk0, nk1;
+    if (kt < 7) {
+      nk0 = kt_operand(B, kt + 1, 0, trow, tcol);
+      nk1 = kt_operand(B, kt + 1, 1, trow, tcol);
+    }
     f4 s = sacc[kt];
 #pragma unroll
     for (int e = 0; e < 4; ++e) s[e] *= dec;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const uint2 p0 = lds_tr4_bits(&B.Ks[32 * ks + trow][16 * kt + tcol]);
-      const uint2 p1 = lds_tr4_bits(&B.Ks[32 * ks + 16 + trow][16 * kt + tcol]);
-      const bf8 kta = __builtin_bit_cast(bf8, make_uint4(p0.x, p0.y, p1.x, p1.y));
-      s = mfma_bf(kta, dhi[ks], s);
-      s = mfma_bf(kta, dlo[ks], s);
-    }
+    s = mfma_16x16x32(kta[(2 * kt) & 3], db0, s);
+    s = mfma_16x16x32(kta[(2 * kt + 1) & 3], db1, s);
     sacc[kt] = s;
+    if (kt < 4) {
+      const int i = kt;
+      f4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = qs[i][e] * eg[i][e];
+      o = mfma_16x16x32(pa[i], ub0, o);
+      if (i >= 2) o = mfma_16x16x32(pa[i + 2], ub1, o);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Os[16 * i + 4 * lg + e][16 * w + ln] = scale * o[e];
+    }
+    if (kt < 7) {
+      kta[(2 * kt + 2) & 3] = nk0;
+      kta[(2 * kt + 3) & 3] = nk1;
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Copy wave: issue the direct global -> LDS loads of chunk c into buffer B (no registers).
-// Q/K rows and the V slice are gathered from the strided tensors into padded rows; rows past
-// the end of the chunk re-read its first row (finite values that only ever meet zero weights).
+// Copy waves: issue the direct global -> LDS loads of chunk c into buffer B (no registers).
+// A chunk is 58 copies of 1 KiB (q/k image 34, record 19, V slice 5) landing back to back in
+// the buffer; copy wave q of NCP issues the copies u = q, q + NCP, ...  The q/k image and the
+// record are contiguous; the V slice is gathered from the strided tensor into padded rows,
+// rows past the end of the chunk re-reading its first row (finite values that only ever meet
+// beta = 0).  Each wave issues at most about one direct copy per 100 cycles, hence several.
 __device__ __forceinline__ void issue_chunk(ScanBuf& B, const PrefillArgs& a, const Geo& G,
-                                            const unsigned char* recs, int c) {
+                                            const unsigned char* ws, int c, int q) {
   using namespace mp;
+  constexpr int NQK = QK_BYTES / 1024, NREC = REC_BYTES / 1024, NV = C * (LDV / 8) / 64;
+  static_assert(sizeof(ScanBuf) == (NQK + NREC + NV) * 1024, "chunk buffer is a whole number of copies");
   const int lane = G.lane;
+  const unsigned char* qk = ws + G.qk0 + (size_t)c * QK_BYTES + 16 * lane;
+  const unsigned char* rec = ws + G.rec0 + (size_t)c * REC_BYTES + 16 * lane;
   const int L = G.len(c);
-  const int64_t c0 = G.start + (int64_t)c * C;
-  const uint16_t* qb = static_cast<const uint16_t*>(a.q) + c0 * a.qk_stride + (int64_t)G.kh * D;
-  const uint16_t* kb = static_cast<const uint16_t*>(a.k) + c0 * a.qk_stride + (int64_t)G.kh * D;
-  constexpr int QPR = LDQ / 8;  // 16-byte pieces per padded Q/K row (17)
+  const uint16_t* vb = static_cast<const uint16_t*>(a.v) + (G.start + (int64_t)c * C) * a.v_stride +
+                       (int64_t)G.h * D + G.dv0;
+  unsigned char* dst = reinterpret_cast<unsigned char*>(&B);
 #pragma unroll
-  for (int i = 0; i < C * QPR / 64; ++i) {
-    const int j = 64 * i + lane, r = j / QPR, pc = j % QPR;
-    const int64_t off = (r < L && pc < D / 8) ? (int64_t)r * a.qk_stride + 8 * pc : 0;
-    __builtin_amdgcn_global_load_lds((glb_void*)(qb + off), (lds_void*)(&B.Qs[0][0] + 512 * i), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds((glb_void*)(kb + off), (lds_void*)(&B.Ks[0][0] + 512 * i), 16, 0, 0);
-  }
-  const unsigned char* rec = recs + G.rec0 + (size_t)c * REC_BYTES;
-#pragma unroll
-  for (int i = 0; i < REC_BYTES / 1024; ++i)
-    __builtin_amdgcn_global_load_lds((glb_void*)(rec + 1024 * i + 16 * lane),
-                                     (lds_void*)(reinterpret_cast<unsigned char*>(&B.R) + 1024 * i), 16, 0, 0);
-  const uint16_t* vb = static_cast<const uint16_t*>(a.v) + c0 * a.v_stride + (int64_t)G.h * D + G.dv0;
-  constexpr int VPR = LDV / 8;  // 16-byte pieces per padded V row (5)
-#pragma unroll
-  for (int i = 0; i < C * VPR / 64; ++i) {
-    const int j = 64 * i + lane, r = j / VPR, pc = j % VPR;
-    const int64_t off = (r < L && pc < DVB / 8) ? (int64_t)r * a.v_stride + 8 * pc : 0;
-    __builtin_amdgcn_global_load_lds((glb_void*)(vb + off), (lds_void*)(&B.Vs[0][0] + 512 * i), 16, 0, 0);
+  for (int k = 0; k < (NQK + NREC + NV + NCP - 1) / NCP; ++k) {
+    const int u = q + NCP * k;
+    if (u >= NQK + NREC + NV) break;
+    const void* src;
+    if (u < NQK) {
+      src = qk + 1024 * u;
+    } else if (u < NQK + NREC) {
+      src = rec + 1024 * (u - NQK);
+    } else {
+      constexpr int VPR = LDV / 8;  // 16-byte pieces per padded V row (5)
+      const int j = 64 * (u - NQK - NREC) + lane, r = j / VPR, pc = j % VPR;
+      src = vb + ((r < L && pc < DVB / 8) ? (int64_t)r * a.v_stride + 8 * pc : 0);
+    }
+    __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(dst + 1024 * u), 16, 0, 0);
   }
 }
 
-// Output wave: write out the output tile of chunk c (rows < L), staged in Os.
+// Output wave: write out the output tile of chunk c (rows < L), staged in Os; four lanes per
+// row, eight values each.
 template <int O_DT>
 __device__ __forceinline__ void write_out(const float (*Os)[mp::DVB + 4], const PrefillArgs& a, const Geo& G,
                                           int c) {
   using namespace mp;
-  const int lane = G.lane;
-  if (lane >= G.len(c)) return;
-  const float* row = &Os[lane][0];
-  const int64_t base = ((G.start + (int64_t)c * C + lane) * a.hv + G.h) * (int64_t)D + G.dv0;
+  const int L = G.len(c);
+  const int part = G.lane & 3;
 #pragma unroll
-  for (int j = 0; j < DVB / 8; ++j) {
-    float v[8];
-    const f4 x0 = *reinterpret_cast<const f4*>(row + 8 * j), x1 = *reinterpret_cast<const f4*>(row + 8 * j + 4);
-    v[0] = x0[0]; v[1] = x0[1]; v[2] = x0[2]; v[3] = x0[3];
-    v[4] = x1[0]; v[5] = x1[1]; v[6] = x1[2]; v[7] = x1[3];
-    store8<O_DT>(a.o, base + 8 * j, v);
+  for (int rg = 0; rg < C / 16; ++rg) {
+    const int r = 16 * rg + (G.lane >> 2);
+    if (r < L) {
+      const f4 x0 = *reinterpret_cast<const f4*>(&Os[r][8 * part]);
+      const f4 x1 = *reinterpret_cast<const f4*>(&Os[r][8 * part + 4]);
+      const float v[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      store8<O_DT>(a.o, ((G.start + (int64_t)c * C + r) * a.hv + G.h) * (int64_t)D + G.dv0 + 8 * part, v);
+    }
   }
 }
 
 template <int O_DT>
-__global__ __launch_bounds__(256) void scan_kernel(PrefillArgs a, int64_t maxch) {
+__global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, int64_t maxch) {
   using namespace mp;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   ScanSmem& sm = *reinterpret_cast<ScanSmem*>(smem_raw);
   const int32_t* off = static_cast<const int32_t*>(a.workspace);
-  const unsigned char* recs = static_cast<const unsigned char*>(a.workspace) + align256(4 * (size_t)(a.num_seqs + 1));
+  const unsigned char* ws = static_cast<const unsigned char*>(a.workspace);
+  const WsLayout wl(a.num_seqs, a.hv, a.hk, maxch);
 
   // Workgroups sharing a key group are consecutive in `lid`; the hardware deals block ids
   // round-robin over the 8 XCDs, so give each XCD a contiguous run of lid (shared L2).
@@ -531,12 +645,13 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillArgs a, int64_t maxch)
   if (G.end < G.start) G.end = G.start;
   G.nchunks = (int)((G.end - G.start + C - 1) / C);
   G.sbase = ((int64_t)n * a.hv + G.h) * (D * D);
-  G.rec0 = ((size_t)G.h * (size_t)maxch + (size_t)off[n]) * REC_BYTES;
+  G.rec0 = wl.rec + ((size_t)G.h * (size_t)maxch + (size_t)off[n]) * REC_BYTES;
+  G.qk0 = wl.qk + ((size_t)G.kh * (size_t)maxch + (size_t)off[n]) * QK_BYTES;
   const int ln = G.ln, lg = G.lg;
 
   // Every role runs its own loop with one workgroup barrier per chunk after a common
-  // prologue barrier.  Iteration c: consumers on chunk c (buffer c & 1), the copy wave
-  // fills buffer (c+1) & 1 and waits for its copies before the barrier, the output wave
+  // prologue barrier.  Iteration c: consumers on chunk c (buffer c & 1), the copy waves
+  // fill buffer (c+1) & 1 and wait for their copies before the barrier, the output wave
   // writes out chunk c-1.
   if (G.w < NCW) {
     f4 sacc[8];
@@ -549,10 +664,10 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillArgs a, int64_t maxch)
       }
       sacc[kt] = v;
     }
-    __syncthreads();
+    lds_barrier();
     for (int c = 0; c < G.nchunks; ++c) {
-      consume(sm.B[c & 1], sm.Os[c & 1], a, G, sacc);
-      __syncthreads();
+      consume(sm.B[c & 1], sm.Os[c & 1], a.scale, G.w, ln, lg, sacc);
+      lds_barrier();
     }
     if (a.s1) {
 #pragma unroll
@@ -562,33 +677,34 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillArgs a, int64_t maxch)
             make_float4(v[0], v[1], v[2], v[3]);
       }
     }
-  } else if (G.w == NCW) {
+  } else if (G.w < NCW + NCP) {
+    const int q = G.w - NCW;
     if (G.nchunks > 0) {
-      issue_chunk(sm.B[0], a, G, recs, 0);
+      issue_chunk(sm.B[0], a, G, ws, 0, q);
       __builtin_amdgcn_s_waitcnt(0);
     }
-    __syncthreads();
+    lds_barrier();
     for (int c = 0; c < G.nchunks; ++c) {
       if (c + 1 < G.nchunks) {
-        issue_chunk(sm.B[(c + 1) & 1], a, G, recs, c + 1);
+        issue_chunk(sm.B[(c + 1) & 1], a, G, ws, c + 1, q);
         __builtin_amdgcn_s_waitcnt(0);
       }
-      __syncthreads();
+      lds_barrier();
     }
   } else {
-    __syncthreads();
+    lds_barrier();
     for (int c = 0; c < G.nchunks; ++c) {
-      if (G.w == NCW + 1 && c >= 1) write_out<O_DT>(sm.Os[(c - 1) & 1], a, G, c - 1);
-      __syncthreads();
+      if (c >= 1) write_out<O_DT>(sm.Os[(c - 1) & 1], a, G, c - 1);
+      lds_barrier();
     }
-    if (G.w == NCW + 1 && G.nchunks > 0) write_out<O_DT>(sm.Os[(G.nchunks - 1) & 1], a, G, G.nchunks - 1);
+    if (G.nchunks > 0) write_out<O_DT>(sm.Os[(G.nchunks - 1) & 1], a, G, G.nchunks - 1);
   }
 }
 
 // ---------------------------------------------------------------- host side
-size_t prefill_mfma_workspace(int num_seqs, int64_t total, int, int hv) {
+size_t prefill_mfma_workspace(int num_seqs, int64_t total, int hk, int hv) {
   if (num_seqs <= 0) return 0;
-  return align256(4 * (size_t)(num_seqs + 1)) + (size_t)hv * (size_t)max_chunks(total, num_seqs) * mp::REC_BYTES;
+  return WsLayout(num_seqs, hv, hk, max_chunks(total, num_seqs)).bytes;
 }
 
 template <int O_DT>
@@ -600,7 +716,7 @@ static hipError_t launch_o(const PrefillArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.total > 0) {
-    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)maxch, (unsigned)a.hk), dim3(256), 0, st, a, maxch);
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(maxch * a.hv)), dim3(256), 0, st, a, maxch);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -609,7 +725,8 @@ static hipError_t launch_o(const PrefillArgs& a, hipStream_t st) {
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(k, dim3((unsigned)((int64_t)a.num_seqs * a.hv * mp::NB)), dim3(256), smem, st, a, maxch);
+  hipLaunchKernelGGL(k, dim3((unsigned)((int64_t)a.num_seqs * a.hv * mp::NB)), dim3(64 * mp::NWAVES), smem, st, a,
+                     maxch);
   return hipGetLastError();
 }
 
