@@ -17,11 +17,12 @@
 //
 // Three launches on the caller's stream:
 //  1. chunk_offsets: first chunk index of every sequence (prefix sum of ceil(len / 64)).
-//  2. prep (all chunks in parallel, one workgroup per chunk and value head): the Gram matrices
-//     K K^T and Q K^T on matrix cores, then in fp32 the decay-scaled P, A and X (the blocks
-//     of X off the diagonal on fp32 matrix cores), written as
-//     one 19 KiB record per (chunk, value head), and (first value head of a key group) the
-//     fp16 image of the chunk's q and k rows, 34 KiB per (chunk, key group).  Everything in
+//  2. prep (all chunks in parallel, one workgroup per chunk and key group, four waves per
+//     value head of the group): the Gram matrices K K^T and Q K^T on matrix cores, then per
+//     value head in fp32 the decay-scaled P, A and X (the blocks of X off the diagonal on
+//     fp32 matrix cores), written as
+//     one 19 KiB record per (chunk, value head), and the fp16 image of the chunk's q and k
+//     rows, 34 KiB per (chunk, key group).  Everything in
 //     them depends only on the inputs, not on the state.
 //  3. scan (serial over chunks): one workgroup of 4 waves per (sequence, value head, block of
 //     32 value rows); the value rows of S are independent, so each workgroup scans its own
@@ -189,19 +190,25 @@ typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
+namespace mp {
+constexpr int PH = 3;       // value heads per prep workgroup (four waves each)
+}
+
+// Lower 16x16 block (i, j), i >= j, of a [chunk, chunk] matrix stored block by block.
+__host__ __device__ constexpr int tri(int i, int j) { return i * (i + 1) / 2 + j; }
+
 struct PrepSmem {
-  union {
+  union U {
     struct {
       uint16_t Q[mp::C][mp::LDQ];   // bf16 q rows as stored (rows >= L: copies of row 0)
       uint16_t K[mp::C][mp::LDQ];   // bf16 k rows as stored
     } qk;                           // until the Gram products are done
-    struct {
-      float A[mp::C][mp::C + 1];    // A, fp32 (lower blocks)
-      float X[mp::C][mp::C + 1];    // X = (I + A)^-1, fp32 (lower blocks)
-    } ax;
+    struct Head {
+      float A[10][16][17];          // lower blocks of A, fp32
+      float X[10][16][17];          // lower blocks of X = (I + A)^-1, fp32
+    } hd[mp::PH];
   } u;
-  _Float16 P[mp::C][mp::LDT];       // P (lower blocks)
-  float gam[mp::C], bet[mp::C];
+  float gam[mp::PH][mp::C], bet[mp::PH][mp::C];
 };
 
 // Lower 16x16 block pair p = 0..9 -> (bi, bj), bi >= bj: (0,0) (1,0) (1,1) (2,0) (2,1) ...
@@ -223,36 +230,43 @@ __device__ __forceinline__ f4 mfma_f32(float a, float b, f4 c) {
 
 // z + A_ik X_kj on fp32 matrix cores (four 16x16x4 steps; lane (m, g) of step s holds
 // A[m][4s+g] and X[4s+g][m]).
-__device__ __forceinline__ f4 blk_ax(const PrepSmem& sm, int i, int k, int j, int ln, int lg, f4 z) {
+__device__ __forceinline__ f4 blk_ax(const PrepSmem::U::Head& hd, int i, int k, int j, int ln, int lg, f4 z) {
+  float av[4], xv[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) z = mfma_f32(sm.u.ax.A[16 * i + ln][16 * k + 4 * s + lg], sm.u.ax.X[16 * k + 4 * s + lg][16 * j + ln], z);
+  for (int s = 0; s < 4; ++s) {
+    av[s] = hd.A[tri(i, k)][ln][4 * s + lg];
+    xv[s] = hd.X[tri(k, j)][4 * s + lg][ln];
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) z = mfma_f32(av[s], xv[s], z);
   return z;
 }
 // -X_ii z with z in result layout (lane (n, g) holds z[4g+e][n]): step s contracts over the
 // rows 4g+s of z, which are the lanes' own element s.
-__device__ __forceinline__ f4 blk_xz(const PrepSmem& sm, int i, int ln, int lg, f4 z) {
+__device__ __forceinline__ f4 blk_xz(const PrepSmem::U::Head& hd, int i, int ln, int lg, f4 z) {
   f4 r = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int s = 0; s < 4; ++s) r = mfma_f32(-sm.u.ax.X[16 * i + ln][16 * i + 4 * lg + s], z[s], r);
+  for (int s = 0; s < 4; ++s) r = mfma_f32(-hd.X[tri(i, i)][ln][4 * lg + s], z[s], r);
   return r;
 }
 
-// One workgroup per (chunk, value head); the value heads of a key group are consecutive so
-// that they share the q/k rows in L2.
-__global__ __launch_bounds__(256, 3) void prep_kernel(PrefillArgs a, int64_t maxch) {
+// One workgroup per (chunk, key group, round of up to PH value heads of the group): the q/k
+// rows, the Gram products and the fp16 q/k image are shared; each value head of the round
+// has four waves of its own for the decay-scaled A, P and X.
+__global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6))) void prep_kernel(PrefillArgs a, int64_t maxch) {
   using namespace mp;
   __shared__ PrepSmem sm;
   const int32_t* off = static_cast<const int32_t*>(a.workspace);
   const WsLayout ws(a.num_seqs, a.hv, a.hk, maxch);
   unsigned char* base = static_cast<unsigned char*>(a.workspace);
+  const int grp = a.hv / a.hk;
+  const unsigned rounds = (unsigned)((grp + PH - 1) / PH);
   const unsigned nblk = gridDim.x;
   unsigned lid = blockIdx.x;
   if ((nblk & 7u) == 0) lid = (blockIdx.x & 7u) * (nblk >> 3) + (blockIdx.x >> 3);
-  const int grp = a.hv / a.hk;
-  const int z = (int)(lid % (unsigned)grp);
-  const int j = (int)((lid / (unsigned)grp) % (unsigned)maxch);
-  const int kh = (int)(lid / ((unsigned)grp * (unsigned)maxch));
-  const int h = kh * grp + z;
+  const int rd = (int)(lid % rounds);
+  const int j = (int)((lid / rounds) % (unsigned)maxch);
+  const int kh = (int)(lid / (rounds * (unsigned)maxch));
   if (j >= off[a.num_seqs]) return;
   const int n = seq_of_chunk(off, a.num_seqs, j);
   const int64_t start = cu_at(a.cu, n, a.total);
@@ -260,17 +274,22 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrefillArgs a, int64_t max
   const int64_t end = cu_at(a.cu, n + 1, a.total);
   const int L = (int)((end - c0) < C ? (end - c0) : C);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+  const int slot = w >> 2, v = w & 3, ts = tid & 255;
+  const int z = rd * PH + slot;
+  const bool act = z < grp;
+  const int h = kh * grp + (act ? z : 0);
   unsigned char* rec = base + ws.rec + ((size_t)h * maxch + j) * REC_BYTES;
+  PrepSmem::U::Head& hd = sm.u.hd[slot];
 
-  // ---- q, k rows of the chunk -> LDS (direct copies, 17 x 1 KiB per matrix, spread over the
-  // four waves; the 17th 16-byte piece of a row is padding and re-reads the row's start)
+  // ---- q, k rows of the chunk -> LDS (direct copies, 17 x 1 KiB per matrix, spread over
+  // the waves; the 17th 16-byte piece of a row is padding and re-reads the row's start)
   {
     constexpr int QPR = LDQ / 8;
     const uint16_t* qb = static_cast<const uint16_t*>(a.q) + c0 * a.qk_stride + (int64_t)kh * D;
     const uint16_t* kb = static_cast<const uint16_t*>(a.k) + c0 * a.qk_stride + (int64_t)kh * D;
 #pragma unroll
-    for (int t = 0; t < (2 * QPR + 3) / 4; ++t) {
-      const int i = w + 4 * t;
+    for (int t = 0; t < (2 * QPR + 4 * PH - 1) / (4 * PH); ++t) {
+      const int i = w + 4 * PH * t;
       if (i >= 2 * QPR) break;
       const int ii = i < QPR ? i : i - QPR;
       const int jj = 64 * ii + lane, r = jj / QPR, pc = jj % QPR;
@@ -280,129 +299,138 @@ __global__ __launch_bounds__(256, 3) void prep_kernel(PrefillArgs a, int64_t max
       __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)dst, 16, 0, 0);
     }
   }
-  if (w == 0) {  // gates: inclusive prefix sum of log-decays; rows >= L get g = beta = 0
-    float gv = lane < L ? a.g[(c0 + lane) * a.hv + h] : 0.f;
-    const float bv = lane < L ? a.beta[(c0 + lane) * a.hv + h] : 0.f;
+  // gates: inclusive prefix sum of log-decays; rows >= L get g = beta = 0.  The record's copy
+  // is stored after the barrier so that the wait below covers loads only.
+  float gv = 0.f, bv = 0.f;
+  if (v == 0 && act) {
+    gv = lane < L ? a.g[(c0 + lane) * a.hv + h] : 0.f;
+    bv = lane < L ? a.beta[(c0 + lane) * a.hv + h] : 0.f;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const float t = __shfl_up(gv, o, 64);
       if (lane >= o) gv += t;
     }
-    sm.gam[lane] = gv;
-    sm.bet[lane] = bv;
+    sm.gam[slot][lane] = gv;
+    sm.bet[slot][lane] = bv;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  lds_barrier();
+  if (v == 0 && act) {
     float* gr = reinterpret_cast<float*>(rec + offsetof(RecImage, gt));
     gr[lane] = bv;
     gr[64 + lane] = __expf(gv);
     gr[128 + lane] = __expf(__shfl(gv, 63, 64) - gv);
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  lds_barrier();
 
-  // ---- Gram blocks K K^T and Q K^T (bf16 matrix cores): wave w takes the lower block pairs
-  // w, w+4, w+8.  The first value head of a key group also writes the fp16 q/k image.
-  f4 gk[3], gq[3];
-#pragma unroll
-  for (int pi = 0; pi < 3; ++pi) {
-    gk[pi] = gq[pi] = f4{0.f, 0.f, 0.f, 0.f};
-    const int p = w + 4 * pi;
-    if (p >= 10) break;
-    int bi, bj;
-    pair_of(p, bi, bj);
+  // ---- Gram blocks K K^T and Q K^T (bf16 matrix cores): wave w < 10 takes lower block pair w.
+  // The first round of a key group also writes the fp16 q/k image (rows >= L zero).
+  f4 gk = {0.f, 0.f, 0.f, 0.f}, gq = gk;
+  int bi = 0, bj = 0;
+  if (w < 10) {
+    pair_of(w, bi, bj);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int col = 32 * ks + 8 * lg;
       const bf8 kbv = *reinterpret_cast<const bf8*>(&sm.u.qk.K[16 * bj + ln][col]);
-      gk[pi] = mfma_bf(*reinterpret_cast<const bf8*>(&sm.u.qk.K[16 * bi + ln][col]), kbv, gk[pi]);
-      gq[pi] = mfma_bf(*reinterpret_cast<const bf8*>(&sm.u.qk.Q[16 * bi + ln][col]), kbv, gq[pi]);
+      gk = mfma_bf(*reinterpret_cast<const bf8*>(&sm.u.qk.K[16 * bi + ln][col]), kbv, gk);
+      gq = mfma_bf(*reinterpret_cast<const bf8*>(&sm.u.qk.Q[16 * bi + ln][col]), kbv, gq);
     }
   }
-  if (z == 0) {
+  if (rd == 0) {
     QKImage* img = reinterpret_cast<QKImage*>(base + ws.qk + ((size_t)kh * maxch + j) * QK_BYTES);
-#pragma unroll
-    for (int t = 0; t < 2 * C * (D / 8) / 256; ++t) {
-      const int i = tid + 256 * t;
+    for (int i = tid; i < 2 * C * (D / 8); i += 256 * PH) {
       const bool isk = i >= C * (D / 8);
       const int r = (i >> 4) & (C - 1), col = 8 * (i & 15);
-      const uint4 v = *reinterpret_cast<const uint4*>(isk ? &sm.u.qk.K[r][col] : &sm.u.qk.Q[r][col]);
-      *reinterpret_cast<h8*>(isk ? &img->K[r][col] : &img->Q[r][col]) = cvt8(r < L ? v : make_uint4(0, 0, 0, 0));
+      const uint4 u = *reinterpret_cast<const uint4*>(isk ? &sm.u.qk.K[r][col] : &sm.u.qk.Q[r][col]);
+      *reinterpret_cast<h8*>(isk ? &img->K[r][col] : &img->Q[r][col]) = cvt8(r < L ? u : make_uint4(0, 0, 0, 0));
     }
   }
-  lds_barrier();  // q/k rows are dead from here: their space holds A and X
+  lds_barrier();  // q/k rows are dead from here
 
-  // ---- decay-scaled A (fp32) and P (fp16) of the same blocks into LDS
+  // ---- per value head of the round, straight from the Gram fragments of block pair (bi, bj):
+  // A (fp32, LDS) and P (fp16, record, zero above the diagonal).  Waves 10, 11 write the two
+  // blocks of P above the diagonal that the scan reads, (0,1) and (2,3), as zeros.
+  if (w < 10) {
+    const int s2 = 16 * bj + ln, r0 = 16 * bi + 4 * lg;
 #pragma unroll
-  for (int pi = 0; pi < 3; ++pi) {
-    const int p = w + 4 * pi;
-    if (p >= 10) break;
-    int bi, bj;
-    pair_of(p, bi, bj);
-    const int s2 = 16 * bj + ln;
-    const float gs = sm.gam[s2];
+    for (int zz = 0; zz < PH; ++zz) {
+      if (rd * PH + zz >= grp) break;
+      const int hz = kh * grp + rd * PH + zz;
+      unsigned char* rz = base + ws.rec + ((size_t)hz * maxch + j) * REC_BYTES;
+      const f4 gr = *reinterpret_cast<const f4*>(&sm.gam[zz][r0]);
+      const f4 br = *reinterpret_cast<const f4*>(&sm.bet[zz][r0]);
+      const float gs = sm.gam[zz][s2];
+      _Float16* pz = reinterpret_cast<_Float16*>(rz + offsetof(RecImage, P));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * bi + 4 * lg + e;
-      const float d = s2 <= r ? __expf(sm.gam[r] - gs) : 0.f;
-      sm.u.ax.A[r][s2] = s2 < r ? sm.bet[r] * d * gk[pi][e] : 0.f;
-      sm.P[r][s2] = (_Float16)(s2 <= r ? d * gq[pi][e] : 0.f);
+      for (int e = 0; e < 4; ++e) {
+        const int r = r0 + e;
+        const float d = s2 <= r ? __expf(gr[e] - gs) : 0.f;
+        sm.u.hd[zz].A[w][4 * lg + e][ln] = s2 < r ? br[e] * d * gk[e] : 0.f;
+        pz[r * LDT + s2] = (_Float16)(s2 <= r ? d * gq[e] : 0.f);
+      }
+    }
+  } else {
+    for (int i = tid - 640; i < PH * 2 * 16 * 2; i += 128) {  // (head, block, row, half row)
+      const int zz = i >> 6, blk = (i >> 5) & 1, r = 32 * blk + ((i >> 1) & 15), c = 16 + 32 * blk + 8 * (i & 1);
+      if (rd * PH + zz < grp) {
+        const int hz = kh * grp + rd * PH + zz;
+        unsigned char* rz = base + ws.rec + ((size_t)hz * maxch + j) * REC_BYTES;
+        *reinterpret_cast<uint4*>(rz + offsetof(RecImage, P) + (r * LDT + c) * 2) = make_uint4(0, 0, 0, 0);
+      }
     }
   }
   lds_barrier();
-
-  if (w == 0) {  // diagonal blocks X_bb = (I + A_bb)^-1: block lg, column ln, right-looking
+  if (v == 0 && act) {  // diagonal blocks X_bb = (I + A_bb)^-1: block lg, column ln, right-looking
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r] = r == ln ? 1.f : 0.f;
+    const int tb = tri(lg, lg);
 #pragma unroll
     for (int s2 = 0; s2 < 16; ++s2)
 #pragma unroll
-      for (int r = s2 + 1; r < 16; ++r) x[r] = fmaf(-sm.u.ax.A[16 * lg + r][16 * lg + s2], x[s2], x[r]);
+      for (int r = s2 + 1; r < 16; ++r) x[r] = fmaf(-hd.A[tb][r][s2], x[s2], x[r]);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sm.u.ax.X[16 * lg + r][16 * lg + ln] = x[r];
-  } else {  // P -> record (fp16 rows, zero above the diagonal)
-    for (int t = tid - 64; t < C * C / 8; t += 192) {
-      const int r = t >> 3, s0 = 8 * (t & 7);
-      h8 v = *reinterpret_cast<const h8*>(&sm.P[r][s0]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (s0 + e > r) v[e] = (_Float16)0.f;
-      *reinterpret_cast<h8*>(rec + offsetof(RecImage, P) + (r * LDT + s0) * 2) = v;
-    }
+    for (int r = 0; r < 16; ++r) hd.X[tb][r][ln] = x[r];
   }
   lds_barrier();
   // off-diagonal blocks by levels d = i - j: X_ij = -X_ii sum_{k=j}^{i-1} A_ik X_kj (fp32)
   const f4 zf = {0.f, 0.f, 0.f, 0.f};
-  if (w < 3) {  // d = 1: blocks (w+1, w)
-    const int i = w + 1;
-    const f4 x = blk_xz(sm, i, ln, lg, blk_ax(sm, i, w, w, ln, lg, zf));
+  if (v < 3 && act) {  // d = 1: blocks (v+1, v)
+    const int i = v + 1;
+    const f4 x = blk_xz(hd, i, ln, lg, blk_ax(hd, i, v, v, ln, lg, zf));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sm.u.ax.X[16 * i + 4 * lg + e][16 * w + ln] = x[e];
+    for (int e = 0; e < 4; ++e) hd.X[tri(i, v)][4 * lg + e][ln] = x[e];
   }
   lds_barrier();
-  if (w < 2) {  // d = 2: blocks (w+2, w)
-    const int i = w + 2;
-    f4 zz = blk_ax(sm, i, w, w, ln, lg, zf);
-    zz = blk_ax(sm, i, w + 1, w, ln, lg, zz);
-    const f4 x = blk_xz(sm, i, ln, lg, zz);
+  if (v < 2 && act) {  // d = 2: blocks (v+2, v)
+    const int i = v + 2;
+    f4 zz = blk_ax(hd, i, v, v, ln, lg, zf);
+    zz = blk_ax(hd, i, v + 1, v, ln, lg, zz);
+    const f4 x = blk_xz(hd, i, ln, lg, zz);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sm.u.ax.X[16 * i + 4 * lg + e][16 * w + ln] = x[e];
+    for (int e = 0; e < 4; ++e) hd.X[tri(i, v)][4 * lg + e][ln] = x[e];
   }
   lds_barrier();
-  if (w == 0) {  // d = 3: block (3, 0)
-    f4 zz = blk_ax(sm, 3, 0, 0, ln, lg, zf);
-    zz = blk_ax(sm, 3, 1, 0, ln, lg, zz);
-    zz = blk_ax(sm, 3, 2, 0, ln, lg, zz);
-    const f4 x = blk_xz(sm, 3, ln, lg, zz);
+  if (v == 0 && act) {  // d = 3: block (3, 0)
+    f4 zz = blk_ax(hd, 3, 0, 0, ln, lg, zf);
+    zz = blk_ax(hd, 3, 1, 0, ln, lg, zz);
+    zz = blk_ax(hd, 3, 2, 0, ln, lg, zz);
+    const f4 x = blk_xz(hd, 3, ln, lg, zz);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sm.u.ax.X[48 + 4 * lg + e][ln] = x[e];
+    for (int e = 0; e < 4; ++e) hd.X[tri(3, 0)][4 * lg + e][ln] = x[e];
   }
   lds_barrier();
   // X -> record (fp16 rows, zero above the diagonal)
-  for (int t = tid; t < C * C / 8; t += 256) {
-    const int r = t >> 3, s0 = 8 * (t & 7);
-    h8 v;
+  if (act) {
+    for (int t = ts; t < C * C / 8; t += 256) {
+      const int r = t >> 3, s0 = 8 * (t & 7);
+      const int bi = r >> 4, bj = s0 >> 4;
+      const float* xr = &hd.X[bj <= bi ? tri(bi, bj) : 0][r & 15][s0 & 15];
+      h8 xv;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (_Float16)(s0 + e <= r ? sm.u.ax.X[r][s0 + e] : 0.f);
-    *reinterpret_cast<h8*>(rec + offsetof(RecImage, X) + (r * LDT + s0) * 2) = v;
+      for (int e = 0; e < 8; ++e) xv[e] = (_Float16)(s0 + e <= r ? xr[e] : 0.f);
+      *reinterpret_cast<h8*>(rec + offsetof(RecImage, X) + (r * LDT + s0) * 2) = xv;
+    }
   }
 }
 
@@ -716,7 +744,8 @@ static hipError_t launch_o(const PrefillArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.total > 0) {
-    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(maxch * a.hv)), dim3(256), 0, st, a, maxch);
+    const int64_t rounds = (a.hv / a.hk + mp::PH - 1) / mp::PH;
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(maxch * a.hk * rounds)), dim3(256 * mp::PH), 0, st, a, maxch);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
