@@ -15,13 +15,15 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------- bf16 storage
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Round to nearest even; NaN stays a (quiet) NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to nearest even into packed bf16 (low half = lo); NaN stays NaN.
+// One hardware conversion on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
 // 8 consecutive elements of a DT tensor as fp32 (16-byte aligned for bf16, 32 for f32).
 template <int DT>
@@ -46,10 +48,10 @@ template <int DT>
 __device__ __forceinline__ void store8(void* base, int64_t idx, const float v[8]) {
   if constexpr (DT == DT_BF16) {
     uint4 u;
-    u.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-    u.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
-    u.z = f32_to_bf16(v[4]) | (f32_to_bf16(v[5]) << 16);
-    u.w = f32_to_bf16(v[6]) | (f32_to_bf16(v[7]) << 16);
+    u.x = pack_bf16x2(v[0], v[1]);
+    u.y = pack_bf16x2(v[2], v[3]);
+    u.z = pack_bf16x2(v[4], v[5]);
+    u.w = pack_bf16x2(v[6], v[7]);
     *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + idx) = u;
   } else {
     float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + idx);

@@ -24,20 +24,20 @@
 //     one 19 KiB record per (chunk, value head), and the fp16 image of the chunk's q and k
 //     rows, 34 KiB per (chunk, key group).  Everything in
 //     them depends only on the inputs, not on the state.
-//  3. scan (serial over chunks): one workgroup of 4 waves per (sequence, value head, block of
+//  3. scan (serial over chunks): one workgroup of 8 waves per (sequence, value head, block of
 //     32 value rows); the value rows of S are independent, so each workgroup scans its own
-//     [32 x 128] fp32 slice of the state.  Waves 0 and 1 own one 16-wide value tile each and
-//     keep their slice of S^T in matrix-core accumulators for the whole sequence; per chunk
-//     they run Q S^T, K S^T, U = X R', P U and the state update.  A 16x16 result fragment is
-//     reused as the next product's operand without leaving registers: the contraction index
-//     of a 16x16x32 product may be permuted as long as both operands use the same
-//     permutation, so two result fragments side by side form a B operand and the matching A
-//     operand is read from LDS as two 8-byte pieces (K^T pieces come straight from the
-//     row-major K tile through the gfx950 transposing LDS read).  Wave 2 copies chunk c+1
-//     (q/k image, record, V slice) into double-buffered LDS with direct global -> LDS loads
-//     while waves 0 and 1 work on chunk c; wave 3 writes out the output of chunk c-1.  Each
-//     chunk costs one workgroup barrier; each role runs its own loop with the same barrier
-//     count, so registers are allocated per role.
+//     [32 x 128] fp32 slice of the state.  The chain wave keeps that slice of S^T in matrix-core
+//     accumulators for the whole sequence and per chunk runs K S^T, U = X R' and the state
+//     update (the serial path); the output wave computes Q S^T and, one chunk later, P U and
+//     the output rows, with the fp16 state and U operands handed over through LDS.  A 16x16
+//     result fragment is reused as the next product's operand without leaving registers: the
+//     contraction index of a 16x16x32 product may be permuted as long as both operands use
+//     the same permutation, so two result fragments side by side form a B operand and the
+//     matching A operand is read from LDS as two 8-byte pieces (K^T pieces come straight from
+//     the row-major K tile through the gfx950 transposing LDS read).  Six copy waves fill the
+//     other half of a double buffer with the next chunk (q/k image, record, V slice) by direct
+//     global -> LDS loads.  Each chunk costs one workgroup barrier; each role runs its own
+//     loop with the same barrier count, so registers are allocated per role.
 // Number formats: bf16 inputs widen exactly to fp16 (normal range); fp32 intermediates
 // (S, R', U, P, X) are rounded to fp16 once per use (2^-11 relative); every product
 // accumulates in fp32 and the state itself stays fp32.
@@ -51,10 +51,10 @@ constexpr int C = 64;        // chunk
 constexpr int D = 128;       // head dim (key and value)
 constexpr int LDQ = D + 8;   // fp16 row stride of staged Q/K rows
 constexpr int LDT = C + 8;   // fp16 row stride of [*, chunk] tiles
-constexpr int NCW = 2;       // consumer waves, one 16-wide value tile each
-constexpr int NCP = 5;       // copy waves
-constexpr int NWAVES = NCW + NCP + 1;  // + one output wave
-constexpr int DVB = 16 * NCW;
+constexpr int NVT = 2;       // 16-wide value tiles per scan workgroup
+constexpr int NCP = 6;       // copy waves
+constexpr int NWAVES = 2 + NCP;  // chain wave, output wave, copy waves
+constexpr int DVB = 16 * NVT;
 constexpr int NB = D / DVB;  // scan workgroups per value head
 constexpr int LDV = DVB + 8; // bf16 row stride of the staged V slice
 }  // namespace mp
@@ -435,16 +435,23 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
 }
 
 // ---------------------------------------------------------------- 3. scan
-
 struct ScanBuf {            // one chunk, filled by direct global -> LDS copies
   QKImage QK;                    // fp16 q, k rows of the key group
   RecImage R;                    // prep record of (chunk, value head)
   uint16_t Vs[mp::C][mp::LDV];   // bf16 v slice [row][value col]
 };
-struct ScanSmem {
-  ScanBuf B[2];
-  float Os[2][mp::C][mp::DVB + 4];  // output tile, written out by the output wave
+// Hand-over from the chain wave of a value tile to its output wave (lane-major 16-byte
+// pieces): the fp16 operands of S^T entering a chunk and of U.
+struct ExBuf {
+  h8 s[mp::NVT][4][64];
+  h8 u[mp::NVT][2][64];
 };
+struct ScanSmem {
+  ScanBuf B[2];                      // by chunk parity
+  float Os[mp::C][mp::DVB + 4];      // output tile staging of the output wave
+  ExBuf X[2];                        // by chunk parity
+};
+static_assert(sizeof(ScanSmem) <= 160 * 1024, "scan LDS");
 
 struct Geo {
   int64_t start, end;
@@ -471,120 +478,250 @@ __device__ __forceinline__ h8 kt_operand(const ScanBuf& B, int kt, int ks, int t
   return cat(lds_tr4(&B.QK.K[32 * ks + trow][16 * kt + tcol]), lds_tr4(&B.QK.K[32 * ks + 16 + trow][16 * kt + tcol]));
 }
 
-// Consumer: chunk in buffer B for value tile w; sacc holds S^T fragments [key tile].
-// 60 products of 16x16x32 per chunk: 32 for Q S^T and K S^T, 6 for U = X R', 6 for P U and
-// 16 for the state update; the only dependent steps are R' -> U -> (O, state).  LDS operands
-// are read one step ahead of the products that use them (sched_barrier keeps the order).
-__device__ __forceinline__ void consume(const ScanBuf& B, float (*Os)[mp::DVB + 4], float scale, int w, int ln,
-                                        int lg, f4 (&sacc)[8]) {
+// Per-row gates in result layout.  Lane (n, g) of a 16x16 result fragment of tile i holds
+// rows 16i + 4g + e; a lane reads the single gate of row 16(n/4) + 4g + n%4 and the row
+// broadcast of the DPP unit (lane k of each 16-lane row to the whole row) hands lane
+// (n, g) the gate of row 16i + 4g + e from lane 4i + e.
+__device__ __forceinline__ int gate_row(int ln, int lg) { return 16 * (ln >> 2) + 4 * lg + (ln & 3); }
+template <int K>
+__device__ __forceinline__ float rowb(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + K, 0xf, 0xf, false));
+}
+__device__ __forceinline__ void row_bcast16(float v, float (&o)[16]) {
+  o[0] = rowb<0>(v); o[1] = rowb<1>(v); o[2] = rowb<2>(v); o[3] = rowb<3>(v);
+  o[4] = rowb<4>(v); o[5] = rowb<5>(v); o[6] = rowb<6>(v); o[7] = rowb<7>(v);
+  o[8] = rowb<8>(v); o[9] = rowb<9>(v); o[10] = rowb<10>(v); o[11] = rowb<11>(v);
+  o[12] = rowb<12>(v); o[13] = rowb<13>(v); o[14] = rowb<14>(v); o[15] = rowb<15>(v);
+}
+
+// Raw transposing read of 4 bf16 values (see lds_tr4); widened later by bf16x4_to_f4.
+__device__ __forceinline__ uint2 lds_tr4_raw(const uint16_t* p) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(p)));
+}
+__device__ __forceinline__ f4 bf16x4_to_f4(uint2 u) {
+  return f4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+            __uint_as_float(u.y & 0xffff0000u)};
+}
+
+// Chain wave on the chunk in buffer B, for both value tiles at once (every LDS operand feeds
+// one product per tile): K S^T, R' = beta (V - exp(gamma) K S^T), U = X R', and the state
+// update S^T <- exp(gamma_63) S^T + K^T diag(exp(gamma_63 - gamma)) U.  sb holds the fp16
+// B operands of S^T entering the chunk and leaves with those of the next chunk; U goes to exU
+// and the next chunk's S^T operands to exS for the output wave.  76 products of 16x16x32.
+// The wave issues in order, so the code is laid out by hand: operands are read a step ahead,
+// and the results of a product are first used several products later.
+__device__ __forceinline__ void chain_step(const ScanBuf& B, ExBuf& exU, ExBuf& exS, int lane, int ln, int lg,
+                                           f4 (&sacc)[mp::NVT][8], h8 (&sb)[mp::NVT][4]) {
   using namespace mp;
   const RecImage& R = B.R;
   const f4 zero = {0.f, 0.f, 0.f, 0.f};
-  h8 qa[2][4], ka[2][4];
+  const int gi = gate_row(ln, lg);
+  const int trow = 4 * lg + (ln >> 2), tcol = 4 * (ln & 3);
+  h8 ka[2][4];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    qa[0][rt] = a_perm(&B.QK.Q[16 * rt + ln][0], 0, lg);
-    ka[0][rt] = a_perm(&B.QK.K[16 * rt + ln][0], 0, lg);
-  }
-  // Q S^T and K S^T: the S^T fragments of key tiles 2ks, 2ks+1 form the B operand of step ks
-  h8 sb[4];
+  for (int rt = 0; rt < 4; ++rt) ka[0][rt] = a_perm(&B.QK.K[16 * rt + ln][0], 0, lg);
+  const float dec = R.gt[1][C - 1];
+  const float gb = R.gt[0][gi], ge = R.gt[1][gi], gl = R.gt[2][gi];
+  f4 kq[NVT][4];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) sb[ks] = b_pair(sacc[2 * ks], sacc[2 * ks + 1]);
-  f4 qs[4], kq[4];
+  for (int t = 0; t < NVT; ++t)
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) qs[rt] = kq[rt] = zero;
+    for (int rt = 0; rt < 4; ++rt) kq[t][rt] = zero;
   __builtin_amdgcn_sched_barrier(0);
-  f4 vv[4], bet[4], eg[4];
+  // K S^T; alongside, the V slices, X operands and the decay of the state (sacc is not an
+  // operand until the update: the products use the fp16 copy sb)
   h8 xa[6];
+  uint2 vr[NVT][4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     if (ks < 3) {
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        qa[(ks + 1) & 1][rt] = a_perm(&B.QK.Q[16 * rt + ln][0], 32 * (ks + 1), lg);
-        ka[(ks + 1) & 1][rt] = a_perm(&B.QK.K[16 * rt + ln][0], 32 * (ks + 1), lg);
-      }
-    } else {
+      for (int rt = 0; rt < 4; ++rt) ka[(ks + 1) & 1][rt] = a_perm(&B.QK.K[16 * rt + ln][0], 32 * (ks + 1), lg);
+    }
+    if (ks == 1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        vv[i] = lds_tr4_bf16(&B.Vs[16 * i + 4 * lg + (ln >> 2)][16 * w + 4 * (ln & 3)]);
-        bet[i] = *reinterpret_cast<const f4*>(&R.gt[0][16 * i + 4 * lg]);
-        eg[i] = *reinterpret_cast<const f4*>(&R.gt[1][16 * i + 4 * lg]);
-      }
+      for (int t = 0; t < NVT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vr[t][i] = lds_tr4_raw(&B.Vs[16 * i + 4 * lg + (ln >> 2)][16 * t + 4 * (ln & 3)]);
+    }
+    if (ks == 2) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) xa[i] = a_perm(&R.X[16 * i + ln][0], 0, lg);
       xa[4] = a_perm(&R.X[32 + ln][0], 32, lg);
       xa[5] = a_perm(&R.X[48 + ln][0], 32, lg);
     }
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      kq[rt] = mfma_16x16x32(ka[ks & 1][rt], sb[ks], kq[rt]);
-      qs[rt] = mfma_16x16x32(qa[ks & 1][rt], sb[ks], qs[rt]);
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int t = 0; t < NVT; ++t) kq[t][rt] = mfma_16x16x32(ka[ks & 1][rt], sb[t][ks], kq[t][rt]);
+#pragma unroll
+    for (int t = 0; t < NVT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sacc[t][2 * ks][e] *= dec;
+        sacc[t][2 * ks + 1][e] *= dec;
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // K^T operands of the first two key tiles, then R' and U for both tiles
+  h8 kta[2][2];
+  kta[0][0] = kt_operand(B, 0, 0, trow, tcol);
+  kta[0][1] = kt_operand(B, 0, 1, trow, tcol);
+  float bb[16], gg[16];
+  row_bcast16(gb, bb);
+  row_bcast16(ge, gg);
+  h8 rb[NVT][2];
+#pragma unroll
+  for (int t = 0; t < NVT; ++t) {
+    f4 rp[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f4 vv = bf16x4_to_f4(vr[t][i]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rp[i][e] = bb[4 * i + e] * (vv[e] - gg[4 * i + e] * kq[t][i][e]);
+    }
+    rb[t][0] = b_pair(rp[0], rp[1]);
+    rb[t][1] = b_pair(rp[2], rp[3]);
+  }
+  f4 u[NVT][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < NVT; ++t) u[t][i] = mfma_16x16x32(xa[i], rb[t][0], zero);
+#pragma unroll
+  for (int t = 0; t < NVT; ++t) {
+    u[t][2] = mfma_16x16x32(xa[4], rb[t][1], u[t][2]);
+    u[t][3] = mfma_16x16x32(xa[5], rb[t][1], u[t][3]);
+  }
+  kta[1][0] = kt_operand(B, 1, 0, trow, tcol);
+  kta[1][1] = kt_operand(B, 1, 1, trow, tcol);
+  float ll[16];
+  row_bcast16(gl, ll);
+  __builtin_amdgcn_sched_barrier(0);
+  h8 db[NVT][2];
+#pragma unroll
+  for (int t = 0; t < NVT; ++t) {
+    f4 ud[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ud[i][e] = u[t][i][e] * ll[4 * i + e];
+    db[t][0] = b_pair(ud[0], ud[1]);
+    db[t][1] = b_pair(ud[2], ud[3]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // state update, K^T operands two key tiles ahead; the hand-over of U meanwhile
+#pragma unroll
+  for (int kt = 0; kt < 8; ++kt) {
+    h8 n0, n1;
+    if (kt < 6) {
+      n0 = kt_operand(B, kt + 2, 0, trow, tcol);
+      n1 = kt_operand(B, kt + 2, 1, trow, tcol);
+    }
+#pragma unroll
+    for (int t = 0; t < NVT; ++t) {
+      sacc[t][kt] = mfma_16x16x32(kta[kt & 1][0], db[t][0], sacc[t][kt]);
+      sacc[t][kt] = mfma_16x16x32(kta[kt & 1][1], db[t][1], sacc[t][kt]);
+    }
+    if (kt == 1) {
+#pragma unroll
+      for (int t = 0; t < NVT; ++t) {
+        exU.u[t][0][lane] = b_pair(u[t][0], u[t][1]);
+        exU.u[t][1][lane] = b_pair(u[t][2], u[t][3]);
+      }
+    }
+    if (kt < 6) {
+      kta[kt & 1][0] = n0;
+      kta[kt & 1][1] = n1;
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  // R' = beta (V - exp(gamma) K S^T); U = X R' with X = (I + A)^-1 lower triangular
-  f4 rp[4];
+  // fp16 operands of the new state for the next chunk (and the output wave)
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) rp[i][e] = bet[i][e] * (vv[i][e] - eg[i][e] * kq[i][e]);
-  const h8 rb0 = b_pair(rp[0], rp[1]), rb1 = b_pair(rp[2], rp[3]);
-  const int trow = 4 * lg + (ln >> 2), tcol = 4 * (ln & 3);
-  h8 pa[6], kta[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) pa[i] = a_perm(&R.P[16 * i + ln][0], 0, lg);
-  pa[4] = a_perm(&R.P[32 + ln][0], 32, lg);
-  pa[5] = a_perm(&R.P[48 + ln][0], 32, lg);
-  f4 egl[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) egl[i] = *reinterpret_cast<const f4*>(&R.gt[2][16 * i + 4 * lg]);
-  kta[0] = kt_operand(B, 0, 0, trow, tcol);
-  kta[1] = kt_operand(B, 0, 1, trow, tcol);
-  f4 u[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) u[i] = mfma_16x16x32(xa[i], rb0, zero);
-  u[2] = mfma_16x16x32(xa[4], rb1, u[2]);
-  u[3] = mfma_16x16x32(xa[5], rb1, u[3]);
-  __builtin_amdgcn_sched_barrier(0);
-  // S^T <- exp(gamma_63) S^T + K^T (diag(exp(gamma_63 - gamma)) U); K^T pieces by transposing reads.
-  // O = diag(exp gamma) Q S^T + P U is interleaved with it and staged in LDS for the output wave.
-  f4 ud[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) ud[i][e] = u[i][e] * egl[i][e];
-  const h8 db0 = b_pair(ud[0], ud[1]), db1 = b_pair(ud[2], ud[3]);
-  const h8 ub0 = b_pair(u[0], u[1]), ub1 = b_pair(u[2], u[3]);
-  const float dec = R.gt[1][C - 1];
-#pragma unroll
-  for (int kt = 0; kt < 8; ++kt) {
-    h8 nk0, nk1;
-    if (kt < 7) {
-      nk0 = kt_operand(B, kt + 1, 0, trow, tcol);
-      nk1 = kt_operand(B, kt + 1, 1, trow, tcol);
+    for (int t = 0; t < NVT; ++t) {
+      sb[t][ks] = b_pair(sacc[t][2 * ks], sacc[t][2 * ks + 1]);
+      exS.s[t][ks][lane] = sb[t][ks];
     }
-    f4 s = sacc[kt];
+}
+
+// Output wave, part 1 (chunk c in buffer B, both value tiles): Q S^T with the S^T operands the
+// chain wave handed over, and the operands of P and the gates exp(gamma) kept for part 2.
+__device__ __forceinline__ void qs_step(const ScanBuf& B, const ExBuf& exS, int lane, int ln, int lg,
+                                        f4 (&qs)[mp::NVT][4], h8 (&pa)[6], float& ge) {
+  using namespace mp;
+  const f4 zero = {0.f, 0.f, 0.f, 0.f};
+  h8 sb[NVT][4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) s[e] *= dec;
-    s = mfma_16x16x32(kta[(2 * kt) & 3], db0, s);
-    s = mfma_16x16x32(kta[(2 * kt + 1) & 3], db1, s);
-    sacc[kt] = s;
-    if (kt < 4) {
-      const int i = kt;
+  for (int t = 0; t < NVT; ++t)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) sb[t][ks] = exS.s[t][ks][lane];
+  h8 qa[2][4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) qa[0][rt] = a_perm(&B.QK.Q[16 * rt + ln][0], 0, lg);
+#pragma unroll
+  for (int t = 0; t < NVT; ++t)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) qs[t][rt] = zero;
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    if (ks < 3) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) qa[(ks + 1) & 1][rt] = a_perm(&B.QK.Q[16 * rt + ln][0], 32 * (ks + 1), lg);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pa[i] = a_perm(&B.R.P[16 * i + ln][0], 0, lg);
+      pa[4] = a_perm(&B.R.P[32 + ln][0], 32, lg);
+      pa[5] = a_perm(&B.R.P[48 + ln][0], 32, lg);
+      ge = B.R.gt[1][gate_row(ln, lg)];
+    }
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int t = 0; t < NVT; ++t) qs[t][rt] = mfma_16x16x32(qa[ks & 1][rt], sb[t][ks], qs[t][rt]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Output wave, part 2 (the chunk c of part 1, one iteration later): O = diag(exp gamma) Q S^T
+// + P U for both tiles, staged in Os by this wave and written out from there (rows < L, four
+// lanes per row, eight values each).
+template <int O_DT>
+__device__ __forceinline__ void o_step(const ExBuf& exU, float (*Os)[mp::DVB + 4], const PrefillArgs& a,
+                                       const Geo& G, int c, const f4 (&qs)[mp::NVT][4], const h8 (&pa)[6],
+                                       float ge) {
+  using namespace mp;
+  const int lane = G.lane, ln = G.ln, lg = G.lg;
+  float gg[16];
+  row_bcast16(ge, gg);
+#pragma unroll
+  for (int t = 0; t < NVT; ++t) {
+    const h8 ub0 = exU.u[t][0][lane], ub1 = exU.u[t][1][lane];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
       f4 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = qs[i][e] * eg[i][e];
+      for (int e = 0; e < 4; ++e) o[e] = qs[t][i][e] * gg[4 * i + e];
       o = mfma_16x16x32(pa[i], ub0, o);
       if (i >= 2) o = mfma_16x16x32(pa[i + 2], ub1, o);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Os[16 * i + 4 * lg + e][16 * w + ln] = scale * o[e];
+      for (int e = 0; e < 4; ++e) Os[16 * i + 4 * lg + e][16 * t + ln] = a.scale * o[e];
     }
-    if (kt < 7) {
-      kta[(2 * kt + 2) & 3] = nk0;
-      kta[(2 * kt + 3) & 3] = nk1;
+  }
+  // Os is written and read back by this wave only: LDS keeps a wave's accesses in order.
+  const int L = G.len(c);
+  const int part = lane & 3;
+#pragma unroll
+  for (int rg = 0; rg < C / 16; ++rg) {
+    const int r = 16 * rg + (lane >> 2);
+    if (r < L) {
+      const f4 x0 = *reinterpret_cast<const f4*>(&Os[r][8 * part]);
+      const f4 x1 = *reinterpret_cast<const f4*>(&Os[r][8 * part + 4]);
+      const float v[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      store8<O_DT>(a.o, ((G.start + (int64_t)c * C + r) * a.hv + G.h) * (int64_t)D + G.dv0 + 8 * part, v);
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -624,26 +761,10 @@ __device__ __forceinline__ void issue_chunk(ScanBuf& B, const PrefillArgs& a, co
   }
 }
 
-// Output wave: write out the output tile of chunk c (rows < L), staged in Os; four lanes per
-// row, eight values each.
-template <int O_DT>
-__device__ __forceinline__ void write_out(const float (*Os)[mp::DVB + 4], const PrefillArgs& a, const Geo& G,
-                                          int c) {
-  using namespace mp;
-  const int L = G.len(c);
-  const int part = G.lane & 3;
-#pragma unroll
-  for (int rg = 0; rg < C / 16; ++rg) {
-    const int r = 16 * rg + (G.lane >> 2);
-    if (r < L) {
-      const f4 x0 = *reinterpret_cast<const f4*>(&Os[r][8 * part]);
-      const f4 x1 = *reinterpret_cast<const f4*>(&Os[r][8 * part + 4]);
-      const float v[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-      store8<O_DT>(a.o, ((G.start + (int64_t)c * C + r) * a.hv + G.h) * (int64_t)D + G.dv0 + 8 * part, v);
-    }
-  }
-}
-
+// Waves: 0 chain wave, 1 output wave (both for all NVT value tiles), then NCP copy waves.
+// Iteration c (one LDS barrier each, n + 1 in all): the chain wave on chunk c; the output wave
+// finishes and writes out chunk c-1 and starts chunk c; the copy waves fill the other buffer
+// with chunk c+1.
 template <int O_DT>
 __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, int64_t maxch) {
   using namespace mp;
@@ -675,57 +796,69 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
   G.sbase = ((int64_t)n * a.hv + G.h) * (D * D);
   G.rec0 = wl.rec + ((size_t)G.h * (size_t)maxch + (size_t)off[n]) * REC_BYTES;
   G.qk0 = wl.qk + ((size_t)G.kh * (size_t)maxch + (size_t)off[n]) * QK_BYTES;
-  const int ln = G.ln, lg = G.lg;
+  const int ln = G.ln, lg = G.lg, lane = G.lane;
+  const int nc = G.nchunks;
 
-  // Every role runs its own loop with one workgroup barrier per chunk after a common
-  // prologue barrier.  Iteration c: consumers on chunk c (buffer c & 1), the copy waves
-  // fill buffer (c+1) & 1 and wait for their copies before the barrier, the output wave
-  // writes out chunk c-1.
-  if (G.w < NCW) {
-    f4 sacc[8];
+  if (G.w == 0) {  // chain wave
+    f4 sacc[NVT][8];
+    h8 sb[NVT][4];
 #pragma unroll
-    for (int kt = 0; kt < 8; ++kt) {
-      f4 v = {0.f, 0.f, 0.f, 0.f};
-      if (a.s0) {
-        const float4 t = *reinterpret_cast<const float4*>(a.s0 + G.sbase + (int64_t)(G.dv0 + 16 * G.w + ln) * D + 16 * kt + 4 * lg);
-        v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    for (int t = 0; t < NVT; ++t) {
+#pragma unroll
+      for (int kt = 0; kt < 8; ++kt) {
+        f4 v = {0.f, 0.f, 0.f, 0.f};
+        if (a.s0) {
+          const float4 x =
+              *reinterpret_cast<const float4*>(a.s0 + G.sbase + (int64_t)(G.dv0 + 16 * t + ln) * D + 16 * kt + 4 * lg);
+          v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+        }
+        sacc[t][kt] = v;
       }
-      sacc[kt] = v;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        sb[t][ks] = b_pair(sacc[t][2 * ks], sacc[t][2 * ks + 1]);
+        sm.X[0].s[t][ks][lane] = sb[t][ks];
+      }
     }
     lds_barrier();
-    for (int c = 0; c < G.nchunks; ++c) {
-      consume(sm.B[c & 1], sm.Os[c & 1], a.scale, G.w, ln, lg, sacc);
+    for (int c = 0; c < nc + 1; ++c) {
+      if (c < nc) chain_step(sm.B[c & 1], sm.X[c & 1], sm.X[(c + 1) & 1], lane, ln, lg, sacc, sb);
       lds_barrier();
     }
     if (a.s1) {
 #pragma unroll
-      for (int kt = 0; kt < 8; ++kt) {
-        const f4 v = sacc[kt];
-        *reinterpret_cast<float4*>(a.s1 + G.sbase + (int64_t)(G.dv0 + 16 * G.w + ln) * D + 16 * kt + 4 * lg) =
-            make_float4(v[0], v[1], v[2], v[3]);
-      }
+      for (int t = 0; t < NVT; ++t)
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) {
+          const f4 v = sacc[t][kt];
+          *reinterpret_cast<float4*>(a.s1 + G.sbase + (int64_t)(G.dv0 + 16 * t + ln) * D + 16 * kt + 4 * lg) =
+              make_float4(v[0], v[1], v[2], v[3]);
+        }
     }
-  } else if (G.w < NCW + NCP) {
-    const int q = G.w - NCW;
-    if (G.nchunks > 0) {
+  } else if (G.w == 1) {  // output wave
+    f4 qs[NVT][4];
+    h8 pa[6];
+    float ge = 0.f;
+    lds_barrier();
+    for (int c = 0; c < nc + 1; ++c) {
+      if (c >= 1) o_step<O_DT>(sm.X[(c - 1) & 1], sm.Os, a, G, c - 1, qs, pa, ge);
+      if (c < nc) qs_step(sm.B[c & 1], sm.X[c & 1], lane, ln, lg, qs, pa, ge);
+      lds_barrier();
+    }
+  } else {  // copy wave
+    const int q = G.w - 2;
+    if (nc > 0) {
       issue_chunk(sm.B[0], a, G, ws, 0, q);
       __builtin_amdgcn_s_waitcnt(0);
     }
     lds_barrier();
-    for (int c = 0; c < G.nchunks; ++c) {
-      if (c + 1 < G.nchunks) {
+    for (int c = 0; c < nc + 1; ++c) {
+      if (c + 1 < nc) {
         issue_chunk(sm.B[(c + 1) & 1], a, G, ws, c + 1, q);
         __builtin_amdgcn_s_waitcnt(0);
       }
       lds_barrier();
     }
-  } else {
-    lds_barrier();
-    for (int c = 0; c < G.nchunks; ++c) {
-      if (c >= 1) write_out<O_DT>(sm.Os[(c - 1) & 1], a, G, c - 1);
-      lds_barrier();
-    }
-    if (G.nchunks > 0) write_out<O_DT>(sm.Os[(G.nchunks - 1) & 1], a, G, G.nchunks - 1);
   }
 }
 
