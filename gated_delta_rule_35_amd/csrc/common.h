@@ -44,6 +44,40 @@ __device__ __forceinline__ void load8(const void* base, int64_t idx, float out[8
   }
 }
 
+// 8 consecutive elements kept as loaded (bf16: one 16-byte vector, f32: two), so that many
+// can be in flight in few registers; widen8 converts to fp32 at the point of use.
+template <int DT>
+struct Raw8 {
+  uint4 u[DT == DT_BF16 ? 1 : 2];
+};
+template <int DT>
+__device__ __forceinline__ Raw8<DT> load_raw8(const void* base, int64_t idx) {
+  Raw8<DT> r;
+  if constexpr (DT == DT_BF16) {
+    r.u[0] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + idx);
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + idx);
+    r.u[0] = p[0];
+    r.u[1] = p[1];
+  }
+  return r;
+}
+template <int DT>
+__device__ __forceinline__ void widen8(const Raw8<DT>& r, float out[8]) {
+  if constexpr (DT == DT_BF16) {
+    const uint32_t w[4] = {r.u[0].x, r.u[0].y, r.u[0].z, r.u[0].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  } else {
+    const uint32_t w[8] = {r.u[0].x, r.u[0].y, r.u[0].z, r.u[0].w, r.u[1].x, r.u[1].y, r.u[1].z, r.u[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) out[i] = __uint_as_float(w[i]);
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ void store8(void* base, int64_t idx, const float v[8]) {
   if constexpr (DT == DT_BF16) {
@@ -82,7 +116,10 @@ __device__ __forceinline__ float sum16(float v) {
   return v;
 }
 
-__device__ __forceinline__ float silu(float u) { return u / (1.0f + __expf(-u)); }
+// x * sigmoid(x) with the hardware exp2 and reciprocal (each within about 1 ulp).
+__device__ __forceinline__ float silu(float u) { return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u)); }
+// 1 / sqrt(x), hardware estimate (within about 1 ulp).
+__device__ __forceinline__ float rsqrt_fast(float x) { return __builtin_amdgcn_rsqf(x); }
 
 // ---------------------------------------------------------------- matrix cores
 // D = A(16x32) B(32x16) + C.  Lane l holds A[l%16][8(l/16)+e], B[8(l/16)+e][l%16],

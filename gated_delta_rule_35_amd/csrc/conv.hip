@@ -15,7 +15,8 @@
 
 namespace agnes {
 
-constexpr int CONV_TB = 16;       // tokens per block
+constexpr int CONV_TB = 32;       // tokens per block
+constexpr int CONV_BATCH = 4;     // tokens whose loads are issued together
 constexpr int CONV_THREADS = 256;  // 256 x 8 = 2048 channels per block
 
 template <int DT>
@@ -38,12 +39,12 @@ __device__ __forceinline__ void conv_token(const ConvArgs& a, const float w[8][4
     acc = fmaf(w[e][1], h1[e], acc);
     acc = fmaf(w[e][2], h2[e], acc);
     acc = fmaf(w[e][3], xc[e], acc);
-    y[e] = active ? acc / (1.0f + expf(-acc)) : 0.f;
+    y[e] = active ? silu(acc) : 0.f;
     ss = fmaf(y[e], y[e], ss);
   }
   ss = sum16(ss);
   if (l2) {
-    const float r = 1.0f / sqrtf(ss + a.eps);
+    const float r = rsqrt_fast(ss + a.eps);
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] *= r;
   }
@@ -80,6 +81,43 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_prefill_kernel(ConvArgs a) 
   int n = lo;
   int64_t start = cu_at(a.cu, n, a.total);
   int64_t end = cu_at(a.cu, n + 1, a.total);
+
+  // Fast path (the same for the whole block): its tokens and their 3-token halo lie in one
+  // sequence.  Loads are issued a batch of tokens ahead of the arithmetic.
+  if (start <= t0 - 3 && t1 <= end && t1 - t0 == CONV_TB) {
+    float h[3][8] = {};
+    if (active) {
+#pragma unroll
+      for (int j = 0; j < 3; ++j) load8<DT>(a.x, (t0 - 3 + j) * a.x_stride + c0, h[j]);
+    }
+    Raw8<DT> xb[2][CONV_BATCH] = {};
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < CONV_BATCH; ++i) xb[0][i] = load_raw8<DT>(a.x, (t0 + i) * a.x_stride + c0);
+    }
+#pragma unroll
+    for (int b = 0; b < CONV_TB / CONV_BATCH; ++b) {
+      if (active && b + 1 < CONV_TB / CONV_BATCH) {
+#pragma unroll
+        for (int i = 0; i < CONV_BATCH; ++i)
+          xb[(b + 1) & 1][i] = load_raw8<DT>(a.x, (t0 + (b + 1) * CONV_BATCH + i) * a.x_stride + c0);
+      }
+#pragma unroll
+      for (int i = 0; i < CONV_BATCH; ++i) {
+        float xc[8], y[8];
+        widen8<DT>(xb[b & 1][i], xc);
+        conv_token<DT>(a, w, bias, h[0], h[1], h[2], xc, l2, active, y);
+        if (active) store8<DT>(a.y, (t0 + b * CONV_BATCH + i) * a.y_stride + c0, y);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          h[0][e] = h[1][e];
+          h[1][e] = h[2][e];
+          h[2][e] = xc[e];
+        }
+      }
+    }
+    return;
+  }
 
   float h[3][8];
 #pragma unroll

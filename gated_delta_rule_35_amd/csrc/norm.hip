@@ -2,14 +2,14 @@
 // delta-rule row: gated RMS-norm), per row of 128 values:
 //   y = o / sqrt(mean(o^2) + eps) * w * z * sigmoid(z).
 // HBM-bound stream: 16 lanes own one row (8 values each, one 16-byte bf16 vector), a
-// 256-thread block covers 16 rows per pass and walks NORM_PASSES passes with every load
-// of a pass issued before its arithmetic.
+// 256-thread block covers 16 rows per pass and walks NORM_PASSES passes, with the loads of
+// all passes issued (kept as loaded, widened at use) before any arithmetic.
 #include "common.h"
 #include "launch.h"
 
 namespace agnes {
 
-constexpr int NORM_PASSES = 4;
+constexpr int NORM_PASSES = 8;
 constexpr int NORM_ROWS = 16 * NORM_PASSES;  // rows per block
 
 template <int ODT, int ZDT, int YDT>
@@ -19,31 +19,29 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_kernel(NormArgs a) {
   float w[8];
   load8<ZDT>(a.w, c0, w);
   const int64_t row0 = (int64_t)blockIdx.x * NORM_ROWS + (threadIdx.x >> 4);
-  float o[NORM_PASSES][8], z[NORM_PASSES][8];
+  Raw8<ODT> orw[NORM_PASSES] = {};
+  Raw8<ZDT> zrw[NORM_PASSES] = {};
 #pragma unroll
   for (int p = 0; p < NORM_PASSES; ++p) {
     const int64_t r = row0 + p * 16;
     if (r < a.rows) {
-      load8<ODT>(a.o, r * 128 + c0, o[p]);
-      load8<ZDT>(a.z, r * 128 + c0, z[p]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[p][e] = z[p][e] = 0.f;
+      orw[p] = load_raw8<ODT>(a.o, r * 128 + c0);
+      zrw[p] = load_raw8<ZDT>(a.z, r * 128 + c0);
     }
   }
 #pragma unroll
   for (int p = 0; p < NORM_PASSES; ++p) {
+    float o[1][8], z[1][8];
+    widen8<ODT>(orw[p], o[0]);
+    widen8<ZDT>(zrw[p], z[0]);
     float ss = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss = fmaf(o[p][e], o[p][e], ss);
+    for (int e = 0; e < 8; ++e) ss = fmaf(o[0][e], o[0][e], ss);
     ss = sum16(ss);
-    const float r = 1.0f / sqrtf(ss * (1.0f / 128.0f) + a.eps);
+    const float r = rsqrt_fast(ss * (1.0f / 128.0f) + a.eps);
     float y[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float gate = z[p][e] / (1.0f + expf(-z[p][e]));
-      y[e] = o[p][e] * r * w[e] * gate;
-    }
+    for (int e = 0; e < 8; ++e) y[e] = o[0][e] * r * w[e] * silu(z[0][e]);
     const int64_t row = row0 + p * 16;
     if (row < a.rows) store8<YDT>(a.y, row * 128 + c0, y);
   }
