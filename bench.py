@@ -4,7 +4,9 @@ One step = the full-layer prefill chain on T = 8192 tokens of one sequence with 
 shapes (16 key / 48 value heads of 128, hidden 5120): kernel-4 causal conv + SiLU + L2 norm of
 q/k over the 10240 q|k|v channels -> chunked gated delta rule (chunk 64, fp32 state) -> gated
 RMSNorm.  `value` is tokens/s of that chain.  The same run also times the batched decode step
-(256 sequences, one token each, fp32 states updated in place) and reports its state HBM GB/s.
+(256 sequences, one token each, fp32 states updated in place) and reports its state HBM GB/s,
+and the fused decode step (conv-history update + conv + L2 + recurrence + gated norm in one
+launch) beside the three unfused calls it replaces.
 
 Inputs are synthetic (seeded), generated on the host and resident in HBM before timing.
 
@@ -39,6 +41,9 @@ CONV_BYTES = T * 10240 * 2 * 2 + 10240 * 4 * 2                        # x in, y 
 NORM_BYTES = T * HV * D * 2 * 3 + D * 2                               # o, z in, y out, weight
 DECODE_B = 256
 DECODE_BYTES = DECODE_B * HV * D * D * 4 * 2 + DECODE_B * (2 * HK * D * 2 + HV * D * 2 + HV * D * 2 + 2 * HV * 4)
+# fused decode: state read + write, x, conv history read + write, conv weights, z, y, g, beta, norm weight
+FUSED_DECODE_BYTES = (DECODE_B * HV * D * D * 4 * 2 + DECODE_B * 10240 * 2 + DECODE_B * 10240 * 3 * 2 * 2
+                      + 10240 * 4 * 2 + DECODE_B * HV * D * 2 * 2 + DECODE_B * HV * 4 * 2 + D * 2)
 CAL_BYTES = 256 << 20          # device-to-device copy of known size, for the HBM counter scale
 
 # HBM traffic per call from the committed counter summary (FETCH_SIZE and WRITE_SIZE runs, each
@@ -104,7 +109,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer shards by heads or sequences with no collective; see the design notes)",
+              "(the layer shards by heads or by sequences with no collective inside the layer)",
               file=sys.stderr)
         sys.exit(2)
     import torch
@@ -173,10 +178,12 @@ def main():
     cw = to_dev(dec["conv_w"], torch)
     ring = []
     for s in range(4):
-        d = decode_step_inputs(s)
+        d = decode_step_inputs(s, gate_input=True)
         ring.append({kk: to_dev(vv, torch) for kk, vv in d.items()})
     yd = torch.empty((DECODE_B, 10240), dtype=torch.bfloat16, device="cuda")
     od = torch.empty((DECODE_B, HV, D), dtype=torch.bfloat16, device="cuda")
+    yn = torch.empty((DECODE_B, HV, D), dtype=torch.bfloat16, device="cuda")
+    nwd = to_dev(dec["norm_w"], torch)
 
     def dstep(i, ev=None):
         d = ring[i % len(ring)]
@@ -188,17 +195,39 @@ def main():
         gdn.decode_step(d["q"], d["k"], d["v"], d["g"], d["beta"], state, o=od)
         if ev is not None:
             ev[2].record()
+        gdn.gated_rmsnorm(od, d["z"], nwd, y=yn)
+        if ev is not None:
+            ev[3].record()
+
+    def fstep(i, ev=None):
+        d = ring[i % len(ring)]
+        if ev is not None:
+            ev[0].record()
+        gdn.decode_fused(d["x"], cw, cache, d["g"], d["beta"], d["z"], nwd, state, num_k_heads=HK, y=yn)
+        if ev is not None:
+            ev[1].record()
 
     for i in range(5):
         dstep(i)
     torch.cuda.synchronize()
-    devs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.decode_steps)]
+    devs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.decode_steps)]
     for i in range(args.decode_steps):
         dstep(i, devs[i])
     torch.cuda.synchronize()
     ms_dconv = np.mean([e[0].elapsed_time(e[1]) for e in devs])
     ms_dec = np.mean([e[1].elapsed_time(e[2]) for e in devs])
+    ms_dnorm = np.mean([e[2].elapsed_time(e[3]) for e in devs])
+    ms_dchain = np.mean([e[0].elapsed_time(e[3]) for e in devs])
     dec_gbs = DECODE_BYTES / (ms_dec * 1e-3) / 1e9
+    for i in range(5):
+        fstep(i)
+    torch.cuda.synchronize()
+    fevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.decode_steps)]
+    for i in range(args.decode_steps):
+        fstep(i, fevs[i])
+    torch.cuda.synchronize()
+    ms_fused = np.mean([e[0].elapsed_time(e[1]) for e in fevs])
+    fused_gbs = FUSED_DECODE_BYTES / (ms_fused * 1e-3) / 1e9
 
     pre_tflops = FLOP_PER_TOKEN * T / (ms_pre * 1e-3) / 1e12
     res = {
@@ -236,6 +265,15 @@ def main():
                    "roofline": {"bound": "hbm", "kernel": "decode_step_kernel", "achieved": round(dec_gbs, 1),
                                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
                                 "traffic": measured_traffic("decode_step"), "bytes_per_launch": DECODE_BYTES}},
+        "decode_fused": {"batch": DECODE_B, "steps": args.decode_steps, "us_per_step": round(ms_fused * 1e3, 2),
+                         "tokens_per_s": round(DECODE_B / (ms_fused * 1e-3), 1),
+                         "unfused_conv_decode_norm_us": round(ms_dchain * 1e3, 2),
+                         "unfused_norm_us": round(ms_dnorm * 1e3, 2),
+                         "roofline": {"bound": "hbm", "kernel": "decode_fused_kernel", "achieved": round(fused_gbs, 1),
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": round(fused_gbs / HBM_PEAK_GBS, 4),
+                                      "traffic": measured_traffic("decode_fused"),
+                                      "bytes_per_launch": FUSED_DECODE_BYTES}},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -11,12 +11,13 @@ discosf article "Agnes 3.0 Flash 刚上线就刷屏…", section 二.1):
   prefill_chunked chunked gated delta rule (chunk 64) over a packed batch
   decode_step     stepwise gated delta rule, state updated in place
   gated_rmsnorm   y = rmsnorm(o) * w * silu(z)
+  decode_fused    one decode token through conv, recurrence and norm in one launch
 """
 import torch
 
 from . import _lib
 
-__all__ = ["conv", "prefill_chunked", "decode_step", "gated_rmsnorm", "prefill_workspace_size",
+__all__ = ["conv", "prefill_chunked", "decode_step", "gated_rmsnorm", "decode_fused", "prefill_workspace_size",
            "AgnesError", "version", "LIB_PATH"]
 
 LIB_PATH = _lib.LIB_PATH
@@ -199,4 +200,50 @@ def gated_rmsnorm(o, z, weight, *, eps=1e-6, y=None, y_dtype=None):
         _ptr(o), _dt(o), _ptr(z), _ptr(weight), _dt(z), eps, rows, HEAD_DIM, _ptr(y), _dt(y),
         _stream(o.device))
     _check("agnes_gdn_gated_rmsnorm", st)
+    return y
+
+
+def decode_fused(x, conv_weight, conv_state, g, beta, z, norm_weight, state, *, num_k_heads,
+                 conv_bias=None, slots=None, scale=1.0, l2norm_eps=1e-6, norm_eps=1e-6, y=None,
+                 o=None, y_dtype=None):
+    """One decode token per batch entry through conv + SiLU + L2(q, k) + recurrence + gated norm.
+
+    x: [B, (2 Hk + Hv) * 128] (row stride free, inner stride 1); conv_weight: [C, 4];
+    conv_state: [S, C, 3] and state: fp32 [S, Hv, 128, 128] (both updated in place, S slots);
+    g, beta: fp32 [B, Hv]; z: [B, Hv, 128]; norm_weight: [128]; slots: int32 [B] on the device
+    or None (entry b uses slot b).  x, conv_weight, conv_bias, conv_state, z and norm_weight share
+    one dtype.  o: optional [B, Hv, 128] output of the recurrence before the norm.  Returns y.
+    """
+    B, C = x.shape
+    Hk = num_k_heads
+    if state.dim() != 4 or state.shape[2:] != (HEAD_DIM, HEAD_DIM) or state.dtype != torch.float32 \
+            or not state.is_contiguous():
+        raise ValueError("state: expected contiguous fp32 [S, Hv, 128, 128]")
+    S, Hv = state.shape[0], state.shape[1]
+    if C != (2 * Hk + Hv) * HEAD_DIM:
+        raise ValueError(f"x: expected {(2 * Hk + Hv) * HEAD_DIM} channels, got {C}")
+    xs = _rows(x, "x", C)
+    for t, name in ((conv_weight, "conv_weight"), (conv_bias, "conv_bias"), (conv_state, "conv_state"),
+                    (z, "z"), (norm_weight, "norm_weight")):
+        if t is not None and (t.dtype != x.dtype or not t.is_contiguous()):
+            raise ValueError(f"{name}: contiguous, with x's dtype {x.dtype}")
+    if tuple(conv_weight.shape) != (C, 4) or tuple(conv_state.shape) != (S, C, 3):
+        raise ValueError("conv_weight [C, 4] and conv_state [S, C, 3] expected")
+    if tuple(z.shape) != (B, Hv, HEAD_DIM) or norm_weight.numel() != HEAD_DIM:
+        raise ValueError("z [B, Hv, 128] and norm_weight [128] expected")
+    for t, name in ((g, "g"), (beta, "beta")):
+        if t.dtype != torch.float32 or tuple(t.shape) != (B, Hv) or not t.is_contiguous():
+            raise ValueError(f"{name}: expected contiguous fp32 [{B}, {Hv}]")
+    if slots is not None and (slots.dtype != torch.int32 or slots.numel() != B or not slots.is_contiguous()):
+        raise ValueError("slots: contiguous int32 [B]")
+    if y is None:
+        y = torch.empty((B, Hv, HEAD_DIM), dtype=y_dtype or x.dtype, device=x.device)
+    for t, name in ((y, "y"), (o, "o")):
+        if t is not None and (tuple(t.shape) != (B, Hv, HEAD_DIM) or not t.is_contiguous() or t.dtype != y.dtype):
+            raise ValueError(f"{name}: contiguous [B, Hv, 128] of one dtype")
+    st = _lib.load().agnes_gdn_decode_fused(
+        _ptr(x), xs, _dt(x), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state), _ptr(g), _ptr(beta),
+        _ptr(z), _ptr(norm_weight), _ptr(state), _ptr(slots), S, B, Hk, Hv, HEAD_DIM, scale, l2norm_eps,
+        norm_eps, _ptr(y), _ptr(o), _dt(y), _stream(x.device))
+    _check("agnes_gdn_decode_fused", st)
     return y

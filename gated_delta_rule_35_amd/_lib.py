@@ -22,6 +22,10 @@ SIGNATURES = {
                                       c_void_p, c_void_p, c_int, c_void_p]),
     "agnes_gdn_gated_rmsnorm": (c_int, [c_void_p, c_int, c_void_p, c_void_p, c_int, c_float,
                                         c_int64, c_int, c_void_p, c_int, c_void_p]),
+    "agnes_gdn_decode_fused": (c_int, [c_void_p, c_int64, c_int, c_void_p, c_void_p, c_void_p,
+                                       c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                       c_int, c_int, c_int, c_int, c_int, c_float, c_float, c_float,
+                                       c_void_p, c_void_p, c_int, c_void_p]),
     "agnes_gdn_status_string": (ctypes.c_char_p, [c_int]),
     "agnes_gdn_last_hip_error": (c_int, []),
     "agnes_gdn_version": (ctypes.c_char_p, []),

@@ -185,3 +185,53 @@ AGNES_API int agnes_gdn_gated_rmsnorm(const void* o, agnes_dtype o_dtype, const 
   agnes::NormArgs a{o, (int)o_dtype, z, weight, (int)zw_dtype, eps, rows, y, (int)y_dtype};
   return hip_status(agnes::launch_gated_rmsnorm(a, static_cast<hipStream_t>(stream)));
 }
+
+AGNES_API int agnes_gdn_decode_fused(const void* x, int64_t x_token_stride, agnes_dtype dtype, const void* conv_weight,
+                                     const void* conv_bias, void* conv_state, const float* g, const float* beta,
+                                     const void* z, const void* norm_weight, float* state, const int32_t* slots,
+                                     int num_slots, int batch, int num_k_heads, int num_v_heads, int head_dim,
+                                     float scale, float l2norm_eps, float norm_eps, void* y, void* o,
+                                     agnes_dtype o_dtype, void* stream) {
+  if (!valid_dtype(dtype) || !valid_dtype(o_dtype)) return AGNES_ERR_INVALID_ARG;
+  if (batch < 0 || num_slots < 0 || num_k_heads <= 0 || num_v_heads <= 0) return AGNES_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim || num_v_heads % num_k_heads || num_v_heads / num_k_heads > 120)
+    return AGNES_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale) || !(l2norm_eps >= 0.f) || !std::isfinite(l2norm_eps) || !(norm_eps >= 0.f) ||
+      !std::isfinite(norm_eps))
+    return AGNES_ERR_INVALID_ARG;
+  if (batch == 0) return AGNES_OK;
+  if (!x || !conv_weight || !conv_state || !g || !beta || !z || !norm_weight || !state || !y)
+    return AGNES_ERR_INVALID_ARG;
+  if (!slots && num_slots < batch) return AGNES_ERR_INVALID_ARG;
+  const int64_t C = (int64_t)(2 * num_k_heads + num_v_heads) * head_dim;
+  if (x_token_stride < C || x_token_stride % 8) return AGNES_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(conv_weight, 16) || !aligned(conv_bias, 16) || !aligned(conv_state, 16) ||
+      !aligned(g, 4) || !aligned(beta, 4) || !aligned(z, 4) || !aligned(norm_weight, 4) || !aligned(state, 16) ||
+      !aligned(slots, 4) || !aligned(y, 4) || !aligned(o, 4))
+    return AGNES_ERR_INVALID_ARG;
+  if ((int64_t)batch * num_k_heads > INT32_MAX || (int64_t)num_slots * num_v_heads > INT32_MAX / 8)
+    return AGNES_ERR_UNSUPPORTED;
+  const size_t es = esize(dtype), eo = esize(o_dtype);
+  const int64_t rowv = (int64_t)num_v_heads * head_dim;
+  const Span ys = span(y, batch, rowv, rowv, eo);
+  const Span os = o ? span(o, batch, rowv, rowv, eo) : Span{0, 0};
+  const Span ss = span(state, 1, 0, (int64_t)num_slots * rowv * head_dim, 4);
+  const Span cs = span(conv_state, 1, 0, (int64_t)num_slots * C * 3, es);
+  const Span ins[] = {span(x, batch, x_token_stride, C, es), span(conv_weight, 1, 0, C * 4, es),
+                      span(conv_bias, conv_bias ? 1 : 0, 0, C, es), span(g, batch, num_v_heads, num_v_heads, 4),
+                      span(beta, batch, num_v_heads, num_v_heads, 4), span(z, batch, rowv, rowv, es),
+                      span(norm_weight, 1, 0, head_dim, es), span(slots, slots ? 1 : 0, 0, batch, 4)};
+  // outputs and in-place buffers must be disjoint from each other and from every input
+  const Span outs[] = {ys, os, ss, cs};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(outs[i], outs[j])) return AGNES_ERR_INVALID_ARG;
+    for (const Span& in : ins)
+      if (overlap(outs[i], in)) return AGNES_ERR_INVALID_ARG;
+  }
+
+  agnes::FusedDecodeArgs a{x, x_token_stride, (int)dtype, conv_weight, conv_bias, conv_state, g, beta, z,
+                           norm_weight, state, slots, num_slots, batch, num_k_heads, num_v_heads, scale,
+                           l2norm_eps, norm_eps, y, o, (int)o_dtype};
+  return hip_status(agnes::launch_decode_fused(a, static_cast<hipStream_t>(stream)));
+}

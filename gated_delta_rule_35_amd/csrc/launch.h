@@ -66,6 +66,31 @@ struct DecodeArgs {
   int o_dtype;
 };
 
+struct FusedDecodeArgs {
+  const void* x;       // [batch, (2 hk + hv) * 128], channels q | k | v
+  int64_t x_stride;
+  int dtype;           // of x, conv_w, conv_b, conv_state, z, norm_w
+  const void* conv_w;  // [channels, 4]
+  const void* conv_b;  // [channels] or nullptr
+  void* conv_state;    // [num_slots, channels, 3]
+  const float* g;      // [batch, hv]
+  const float* beta;   // [batch, hv]
+  const void* z;       // [batch, hv, 128]
+  const void* norm_w;  // [128]
+  float* state;        // [num_slots, hv, 128, 128]
+  const int32_t* slots;  // [batch] or nullptr (slot = entry)
+  int num_slots;
+  int batch;
+  int hk;
+  int hv;
+  float scale;
+  float l2_eps;
+  float norm_eps;
+  void* y;             // [batch, hv, 128]
+  void* o;             // [batch, hv, 128] or nullptr
+  int o_dtype;         // of y and o
+};
+
 struct NormArgs {
   const void* o;
   int o_dtype;
@@ -84,5 +109,6 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s);
 size_t prefill_mfma_workspace(int num_seqs, int64_t total, int hk, int hv);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_gated_rmsnorm(const NormArgs& a, hipStream_t s);
+hipError_t launch_decode_fused(const FusedDecodeArgs& a, hipStream_t s);
 
 }  // namespace agnes

@@ -176,6 +176,51 @@ int agnes_gdn_gated_rmsnorm(const void* o, agnes_dtype o_dtype, const void* z,
                             const void* weight, agnes_dtype zw_dtype, float eps, int64_t rows,
                             int dim, void* y, agnes_dtype y_dtype, void* stream);
 
+/*
+ * agnes_gdn_decode_fused — one decode token per batch entry through the whole
+ * delta layer in a single launch (discosf article, section 二.1: stepwise
+ * decode; model card 架构 table, delta-rule row: kernel-4 causal conv in front,
+ * gated RMS-norm behind, fp32 state).  For each entry b with slot s:
+ *
+ *   u = SiLU(conv(x[b], conv_state[s]))   over the q | k | v channels, and the
+ *       conv history of slot s advanced by x[b] (oldest first);
+ *   q, k = the q and k heads of u, each divided by sqrt(sum of squares + l2norm_eps);
+ *   the gated delta-rule step of agnes_gdn_decode_step on state[s] (in place),
+ *       giving o (o = scale * S q);
+ *   y = o / sqrt(mean(o^2) + norm_eps) * norm_weight * SiLU(z[b])  per value head.
+ *
+ * The same arithmetic as agnes_gdn_conv (decode mode, l2norm_heads = 2 Hk) ->
+ * agnes_gdn_decode_step -> agnes_gdn_gated_rmsnorm, except that q, k, v and o
+ * stay fp32 between the steps instead of being stored in `dtype`.
+ *
+ *   x            [batch, C] with C = (2 Hk + Hv) * head_dim: channels q (Hk heads),
+ *                k (Hk heads), v (Hv heads); row stride x_token_stride elems, `dtype`
+ *   conv_weight  [C, 4] contiguous, `dtype`;  conv_bias [C] `dtype` or NULL
+ *   conv_state   [num_slots, C, 3] contiguous, `dtype`, oldest first; in place
+ *   g, beta      fp32 [batch, Hv] contiguous
+ *   z            [batch, Hv, head_dim] contiguous, `dtype` (the norm's gate)
+ *   norm_weight  [head_dim], `dtype`
+ *   state        fp32 [num_slots, Hv, head_dim(v), head_dim(k)] contiguous; in place
+ *   slots        device int32 [batch]: the state / conv-history slot of each
+ *                entry, or NULL (slot = entry index; then num_slots >= batch).
+ *                An entry whose slot is negative or >= num_slots is padding: its
+ *                y (and o) rows are written as zeros and nothing else is touched.
+ *                Two entries naming the same slot race (unspecified results).
+ *   y            [batch, Hv, head_dim] contiguous, `o_dtype`
+ *   o            [batch, Hv, head_dim] contiguous, `o_dtype`, or NULL: the
+ *                recurrence output before the norm
+ * Supported: head_dim 128, Hv a multiple of Hk with Hv / Hk <= 120.
+ * Slots exist for a serving pool in which a sequence keeps its caches at a
+ * fixed slot while the batch composition changes from step to step.
+ */
+int agnes_gdn_decode_fused(const void* x, int64_t x_token_stride, agnes_dtype dtype,
+                           const void* conv_weight, const void* conv_bias, void* conv_state,
+                           const float* g, const float* beta, const void* z,
+                           const void* norm_weight, float* state, const int32_t* slots,
+                           int num_slots, int batch, int num_k_heads, int num_v_heads,
+                           int head_dim, float scale, float l2norm_eps, float norm_eps,
+                           void* y, void* o, agnes_dtype o_dtype, void* stream);
+
 /* Human-readable name of an agnes_status value (static string). */
 const char* agnes_gdn_status_string(int status);
 

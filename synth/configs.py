@@ -137,12 +137,15 @@ def decode_state_inputs(rng, batch):
                             dtype=np.float32) * np.float32(PROJ_STD))
     conv_w = f32_to_bf16_bits(
         rng.uniform(-0.5, 0.5, size=(L["conv_channels"], L["conv_kernel"])).astype(np.float32))
-    return dict(state=state, conv_cache=conv_cache, conv_w=conv_w, batch=batch, **L)
+    # gated-norm weight, drawn last so that the draws above do not depend on it
+    norm_w = f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(L["head_dim"])).astype(np.float32))
+    return dict(state=state, conv_cache=conv_cache, conv_w=conv_w, norm_w=norm_w, batch=batch, **L)
 
 
-def decode_step_inputs(step, batch=256, seed=1003, conv_input=True):
+def decode_step_inputs(step, batch=256, seed=1003, conv_input=True, gate_input=False):
     """Inputs of decode step ``step`` (seeded by (seed, step)): q,k unit bf16, v bf16,
-    g/beta fp32 and (``conv_input``) the raw conv input x [batch, 10240] bf16."""
+    g/beta fp32, (``conv_input``) the raw conv input x [batch, 10240] bf16 and
+    (``gate_input``, drawn after x) the norm gate z [batch, 48, 128] bf16 ~ N(0, 1)."""
     L = LAYER
     rng = np.random.default_rng([seed, step])
     q = f32_to_bf16_bits(unit_vectors(rng, (batch, L["num_k_heads"], L["head_dim"])))
@@ -154,6 +157,9 @@ def decode_step_inputs(step, batch=256, seed=1003, conv_input=True):
     if conv_input:
         out["x"] = f32_to_bf16_bits(rng.standard_normal((batch, L["conv_channels"]), dtype=np.float32)
                                     * np.float32(PROJ_STD))
+    if gate_input:
+        out["z"] = f32_to_bf16_bits(rng.standard_normal((batch, L["num_v_heads"], L["head_dim"]),
+                                                        dtype=np.float32))
     return out
 
 

@@ -149,3 +149,35 @@ def test_norm_checks(lib):
     assert norm(lib, y=P[0], ydt=F32) == INV            # aliasing needs equal dtypes
     assert norm(lib, y=P[1] + 16) == INV                # y overlaps z
     assert norm(lib, eps=-1.0) == INV
+
+
+def fused(lib, **kw):
+    a = dict(x=P[0], xs=10 * 128, dt=BF16, w=P[1], b=None, cs=P[2], g=P[3], be=P[4], z=P[5], nw=P[6], st=P[7],
+             sl=None, S=4, B=4, hk=2, hv=6, hd=128, sc=1.0, e1=1e-6, e2=1e-6, y=P[8], o=None, odt=BF16)
+    a.update(kw)
+    return lib.agnes_gdn_decode_fused(a["x"], a["xs"], a["dt"], a["w"], a["b"], a["cs"], a["g"], a["be"], a["z"],
+                                      a["nw"], a["st"], a["sl"], a["S"], a["B"], a["hk"], a["hv"], a["hd"], a["sc"],
+                                      a["e1"], a["e2"], a["y"], a["o"], a["odt"], None)
+
+
+def test_decode_fused_checks(lib):
+    assert fused(lib, B=0, x=None, y=None) == 0         # empty batch: nothing to do
+    assert fused(lib, hd=64) == UNS
+    assert fused(lib, hv=7) == UNS                      # Hv % Hk
+    assert fused(lib, hk=1, hv=121, xs=123 * 128) == UNS  # more than 120 value heads per key head
+    assert fused(lib, x=None) == INV
+    assert fused(lib, cs=None) == INV
+    assert fused(lib, S=3) == INV                       # no slot array: a slot per entry needed
+    assert fused(lib, xs=10 * 128 - 8) == INV           # row stride below the channel count
+    assert fused(lib, xs=10 * 128 + 4) == INV           # row stride % 8
+    assert fused(lib, x=P[0] + 8) == INV                # misaligned
+    assert fused(lib, st=P[7] + 4) == INV
+    assert fused(lib, dt=5) == INV
+    assert fused(lib, e2=float("nan")) == INV
+    assert fused(lib, sc=float("inf")) == INV
+    assert fused(lib, B=-1) == INV
+    assert fused(lib, y=P[7] + 4096) == INV             # y inside the state pool
+    assert fused(lib, o=P[8] + 256) == INV              # o overlaps y
+    assert fused(lib, cs=P[0] + 1024) == INV            # conv history overlaps x
+    assert fused(lib, y=P[5] + 64) == INV               # y overlaps z
+    assert lib.agnes_gdn_last_hip_error() == 0

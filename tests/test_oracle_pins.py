@@ -350,3 +350,92 @@ def test_pin_norm_unit_rms_and_scale_invariance():
 def test_oracle_upcast_of_bf16_patterns_is_exact():
     bits = np.array([0x3F80, 0xBF80, 0x0000, 0x7F80, 0x3E80], np.uint16)
     np.testing.assert_array_equal(oracle.as_f64(bits), [1.0, -1.0, 0.0, np.inf, 0.25])
+
+
+# ---------------------------------------------------------------- whole layer
+
+def _layer_inputs(rng, T, Hk, Hv, d=128):
+    C = (2 * Hk + Hv) * d
+    x = rng.standard_normal((T, C)) * 1.4
+    w = rng.uniform(-0.5, 0.5, (C, 4))
+    g, beta = gate_draws(rng, (T, Hv), 0.05)
+    z = rng.standard_normal((T, Hv, d))
+    nw = 1.0 + 0.1 * rng.standard_normal(d)
+    return x, w, g.astype(np.float64), beta.astype(np.float64), z, nw
+
+
+def test_pin_layer_decode_steps_equal_prefill():
+    """T decode steps of the layer (conv history carried token to token, state carried in
+    its slot) equal one prefill of the layer over the same T tokens: catches a wrong
+    history shift, a history slot mix-up and a state hand-off error."""
+    rng = np.random.default_rng(40)
+    T, Hk, Hv = 12, 1, 3
+    x, w, g, beta, z, nw = _layer_inputs(rng, T, Hk, Hv)
+    C = x.shape[1]
+    cs0 = rng.standard_normal((C, 3))
+    s0 = rng.standard_normal((Hv, 128, 128)) * 0.01
+    y_ref, o_ref, cs_ref, s_ref = oracle.prefill_layer(x, w, cs0, g, beta, z, nw, s0, Hk, Hv)
+    # a pool of 3 slots, the sequence living in slot 2
+    cs_pool = rng.standard_normal((3, C, 3))
+    st_pool = rng.standard_normal((3, Hv, 128, 128))
+    cs_pool[2], st_pool[2] = cs0, s0
+    others = (cs_pool[:2].copy(), st_pool[:2].copy())
+    for t in range(T):
+        y, o, cs_pool, st_pool = oracle.decode_layer_step(
+            x[t:t + 1], w, cs_pool, g[t:t + 1], beta[t:t + 1], z[t:t + 1], nw, st_pool, Hk, Hv,
+            slots=[2])
+        np.testing.assert_allclose(y[0], y_ref[t], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(o[0], o_ref[t], rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(cs_pool[2], cs_ref, rtol=0, atol=0)
+    np.testing.assert_allclose(st_pool[2], s_ref, rtol=1e-10, atol=1e-13)
+    np.testing.assert_array_equal(cs_pool[:2], others[0])
+    np.testing.assert_array_equal(st_pool[:2], others[1])
+
+
+def test_pin_layer_channel_order_and_normalised_heads():
+    """With the current-token tap only (w = [0, 0, 0, 1]) and one token from a zero state,
+    S_1 = beta v k^T and o = beta (k . q) v with q, k the L2-normalised SiLU of the first and
+    second 128-channel groups and v the SiLU of the third (not normalised); y is o's gated
+    RMS-norm.  Catches a swapped q/k/v split or a normalised v."""
+    rng = np.random.default_rng(41)
+    Hk, Hv, d = 1, 1, 128
+    x = rng.standard_normal((1, 3 * d))
+    w = np.zeros((3 * d, 4))
+    w[:, 3] = 1.0
+    g = np.array([[-0.3]])
+    beta = np.array([[0.7]])
+    z = rng.standard_normal((1, Hv, d))
+    nw = 1.0 + 0.1 * rng.standard_normal(d)
+    y, o, _, S = oracle.prefill_layer(x, w, None, g, beta, z, nw, None, Hk, Hv)
+    act = x[0] * expit(x[0])
+    q = act[:d] / np.sqrt(act[:d] @ act[:d] + 1e-6)
+    k = act[d:2 * d] / np.sqrt(act[d:2 * d] @ act[d:2 * d] + 1e-6)
+    v = act[2 * d:]
+    np.testing.assert_allclose(S[0], 0.7 * np.outer(v, k), rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(o[0, 0], 0.7 * (k @ q) * v, rtol=1e-12, atol=1e-15)
+    rms = np.sqrt(np.mean(o[0, 0] ** 2) + 1e-6)
+    np.testing.assert_allclose(y[0, 0], o[0, 0] / rms * nw * z[0, 0] * expit(z[0, 0]), rtol=1e-12)
+
+
+def test_pin_layer_slots_permute_and_padding_is_inert():
+    """Entries mapped to permuted slots give the rows of the identity mapping on a permuted
+    pool; a padding entry (slot -1 or beyond the pool) yields zero rows and changes nothing."""
+    rng = np.random.default_rng(42)
+    B, Hk, Hv, S = 4, 1, 2, 6
+    x, w, g, beta, z, nw = _layer_inputs(rng, B, Hk, Hv)
+    C = x.shape[1]
+    cs = rng.standard_normal((S, C, 3))
+    st = rng.standard_normal((S, Hv, 128, 128)) * 0.01
+    slots = np.array([4, -1, 0, 7])  # entries 1 and 3 are padding
+    y, o, cs1, st1 = oracle.decode_layer_step(x, w, cs, g, beta, z, nw, st, Hk, Hv, slots=slots)
+    live = [0, 2]
+    y2, o2, cs2, st2 = oracle.decode_layer_step(x[live], w, cs[slots[live]], g[live], beta[live], z[live],
+                                                nw, st[slots[live]], Hk, Hv)
+    np.testing.assert_array_equal(y[live], y2)
+    np.testing.assert_array_equal(o[live], o2)
+    np.testing.assert_array_equal(cs1[slots[live]], cs2)
+    np.testing.assert_array_equal(st1[slots[live]], st2)
+    assert not y[[1, 3]].any() and not o[[1, 3]].any()
+    untouched = [1, 2, 3, 5]
+    np.testing.assert_array_equal(cs1[untouched], cs[untouched])
+    np.testing.assert_array_equal(st1[untouched], st[untouched])
