@@ -76,7 +76,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--decode-steps", type=int, default=200)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-tokens", type=int, default=1024, help="tokens of the oracle CPU sample")
+    p.add_argument("--cpu-tokens", type=int, default=8192, help="tokens of the oracle CPU sample")
     return p.parse_args()
 
 

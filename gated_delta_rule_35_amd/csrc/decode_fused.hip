@@ -7,13 +7,16 @@
 //   the gated delta-rule step on the fp32 state (rank-one form, as the unfused decode step),
 //   then y = o / sqrt(mean(o^2) + eps) * w * SiLU(z) per value head.
 //
-// One workgroup per (batch entry, key head): it owns the conv channels of that key head's
-// q and k heads and of its G = Hv / Hk value heads, so the conv history is read and written
-// by one workgroup only, and q, k are convolved and normalised once for the G heads.  Each
-// group of 256 threads (four waves) runs the state update of one value head exactly as the
-// unfused step does (a row over 16 lanes, one read and one write of the 64 KiB state); its
-// state loads are issued before the convolution so that they are in flight meanwhile.  q, k,
-// v and o pass through LDS in fp32: nothing is rounded between the steps.
+// One workgroup of 256 threads per (batch entry, key head): it owns the conv channels of that
+// key head's q and k heads and of its G = Hv / Hk value heads, so the conv history is read and
+// written by one workgroup only, and q, k are convolved and normalised once for the G heads.
+// The workgroup then runs the state updates of the G value heads one after another, each as
+// the unfused step does (a row over 16 lanes, one read and one write of the 64 KiB state); the
+// first head's state loads are issued before the convolution so that they are in flight
+// meanwhile, and two workgroups per CU (the register count allows no more) keep the memory
+// busy between heads.  This runs about 2 % faster than three 256-thread groups in one
+// workgroup (one head each), and on par with a register-capped build at three workgroups per
+// CU.  q, k, v and o pass through LDS in fp32: nothing is rounded between the steps.
 //
 // A slot array maps batch entries to state and conv-history slots of a pool (entries whose
 // slot is negative or beyond the pool are padding: their y and o rows are zero and nothing
@@ -23,32 +26,43 @@
 
 namespace agnes {
 
-constexpr int FD_MAX_GROUPS = 3;  // value heads in flight per workgroup (256 threads each)
+// Element i (0..8n-1) of n consecutive raw 8-element loads, as fp32.
+template <int DT>
+__device__ __forceinline__ float raw_at(const Raw8<DT>* r, int i) {
+  if constexpr (DT == DT_BF16) {
+    const uint4 u = r[i >> 3].u[0];
+    const uint32_t wd = ((i & 7) >> 1) == 0 ? u.x : ((i & 7) >> 1) == 1 ? u.y : ((i & 7) >> 1) == 2 ? u.z : u.w;
+    return __uint_as_float((i & 1) ? (wd & 0xffff0000u) : (wd << 16));
+  } else {
+    const uint4 u = r[i >> 3].u[(i & 7) >> 2];
+    const uint32_t wd = (i & 3) == 0 ? u.x : (i & 3) == 1 ? u.y : (i & 3) == 2 ? u.z : u.w;
+    return __uint_as_float(wd);
+  }
+}
 
+// Conv + SiLU (+ L2 over the 16 lanes of a head) of channels c0..c0+7 of entry b, result to
+// dst (LDS); the history of those channels in slot `slot` advances by the current input.
+// Inputs stay as loaded (raw) and are widened where used, to keep registers free for the
+// state loads in flight.
 template <int DT>
 __device__ __forceinline__ void fd_conv_item(const FusedDecodeArgs& a, int b, int slot, int c0, bool l2, float* dst) {
   const int C = (2 * a.hk + a.hv) * 128;
-  float x[8], hs[24], w[32], bias[8];
-  load8<DT>(a.x, (int64_t)b * a.x_stride + c0, x);
   const int64_t sb = ((int64_t)slot * C + c0) * 3;  // history of channels c0..c0+7, oldest first
-  load8<DT>(a.conv_state, sb, hs);
-  load8<DT>(a.conv_state, sb + 8, hs + 8);
-  load8<DT>(a.conv_state, sb + 16, hs + 16);
+  Raw8<DT> xr[1], hr[3], wr[4], br[1];
+  xr[0] = load_raw8<DT>(a.x, (int64_t)b * a.x_stride + c0);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) load8<DT>(a.conv_w, (int64_t)c0 * 4 + 8 * j, w + 8 * j);
-  if (a.conv_b) load8<DT>(a.conv_b, c0, bias);
-  else {
+  for (int j = 0; j < 3; ++j) hr[j] = load_raw8<DT>(a.conv_state, sb + 8 * j);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) bias[e] = 0.f;
-  }
+  for (int j = 0; j < 4; ++j) wr[j] = load_raw8<DT>(a.conv_w, (int64_t)c0 * 4 + 8 * j);
+  if (a.conv_b) br[0] = load_raw8<DT>(a.conv_b, c0);
   float y[8], ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    float acc = bias[e];
-    acc = fmaf(w[4 * e + 0], hs[3 * e + 0], acc);
-    acc = fmaf(w[4 * e + 1], hs[3 * e + 1], acc);
-    acc = fmaf(w[4 * e + 2], hs[3 * e + 2], acc);
-    acc = fmaf(w[4 * e + 3], x[e], acc);
+    float acc = a.conv_b ? raw_at<DT>(br, e) : 0.f;
+    acc = fmaf(raw_at<DT>(wr, 4 * e + 0), raw_at<DT>(hr, 3 * e + 0), acc);
+    acc = fmaf(raw_at<DT>(wr, 4 * e + 1), raw_at<DT>(hr, 3 * e + 1), acc);
+    acc = fmaf(raw_at<DT>(wr, 4 * e + 2), raw_at<DT>(hr, 3 * e + 2), acc);
+    acc = fmaf(raw_at<DT>(wr, 4 * e + 3), raw_at<DT>(xr, e), acc);
     y[e] = silu(acc);
     ss = fmaf(y[e], y[e], ss);
   }
@@ -56,35 +70,31 @@ __device__ __forceinline__ void fd_conv_item(const FusedDecodeArgs& a, int b, in
   const float r = l2 ? rsqrt_fast(ss + a.l2_eps) : 1.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) dst[e] = y[e] * r;
-  // new history: the two newest old entries, then the current input
-  float nh[24];
+  // new history of channel e: its two newest old entries, then the current input (exact copies)
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    nh[3 * e + 0] = hs[3 * e + 1];
-    nh[3 * e + 1] = hs[3 * e + 2];
-    nh[3 * e + 2] = x[e];
+  for (int k = 0; k < 3; ++k) {
+    float nh[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int n = 8 * k + i, e = n / 3, j = n % 3;
+      nh[i] = j < 2 ? raw_at<DT>(hr, 3 * e + j + 1) : raw_at<DT>(xr, e);
+    }
+    store8<DT>(a.conv_state, sb + 8 * k, nh);
   }
-  store8<DT>(a.conv_state, sb, nh);
-  store8<DT>(a.conv_state, sb + 8, nh + 8);
-  store8<DT>(a.conv_state, sb + 16, nh + 16);
 }
 
 template <int DT, int ODT>
-__global__ __launch_bounds__(256 * FD_MAX_GROUPS) void decode_fused_kernel(FusedDecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_fused_kernel(FusedDecodeArgs a) {
   extern __shared__ __align__(16) float fd_smem[];
   const int G = a.hv / a.hk;
-  const int ng = G < FD_MAX_GROUPS ? G : FD_MAX_GROUPS;
   const int b = blockIdx.x / a.hk;
   const int kh = blockIdx.x - b * a.hk;
   const int tid = threadIdx.x;
-  const int nthr = blockDim.x;
-  const int gi = tid >> 8;  // value-head group
-  const int t = tid & 255;
-  const int w = t >> 6, l = t & 63, sub = l >> 4, c = (l & 15) * 4;
+  const int w = tid >> 6, l = tid & 63, sub = l >> 4, c = (l & 15) * 4;
 
-  int slot = a.slots ? a.slots[b] : b;
+  const int slot = a.slots ? a.slots[b] : b;
   if (slot < 0 || slot >= a.num_slots) {  // padding entry
-    for (int i = tid; i < G * 128; i += nthr) {
+    for (int i = tid; i < G * 128; i += 256) {
       const int64_t idx = ((int64_t)b * a.hv + (int64_t)kh * G) * 128 + i;
       store1<ODT>(a.y, idx, 0.f);
       if (a.o) store1<ODT>(a.o, idx, 0.f);
@@ -92,11 +102,10 @@ __global__ __launch_bounds__(256 * FD_MAX_GROUPS) void decode_fused_kernel(Fused
     return;
   }
 
-  float* qk_s = fd_smem;             // [2][128]: normalised q, k of the key head
-  float* v_s = fd_smem + 256;        // [G][128]
-  float* o_s = v_s + G * 128;        // [ng][128]
+  float* qk_s = fd_smem;       // [2][128]: normalised q, k of the key head
+  float* v_s = fd_smem + 256;  // [G][128]
+  float* o_s = v_s + G * 128;  // [4][128]: o of head j in slot j % 4, normalised by wave j % 4
 
-  // state loads of this group's first value head, in flight during the convolution
   float4 s[8][2];
   auto load_state = [&](int j) {
     const float* S = a.state + ((int64_t)slot * a.hv + (int64_t)kh * G + j) * (128 * 128);
@@ -107,11 +116,11 @@ __global__ __launch_bounds__(256 * FD_MAX_GROUPS) void decode_fused_kernel(Fused
       s[p][1] = *reinterpret_cast<const float4*>(S + row * 128 + 64 + c);
     }
   };
-  if (DT == DT_BF16 && gi < G) load_state(gi);  // (f32 inputs: after the conv, fewer live registers)
+  if (DT == DT_BF16) load_state(0);  // (f32 inputs: after the conv, fewer live registers)
 
   // conv of the q, k and G value heads: 16 items of 8 channels per head
   const int items = (2 + G) * 16;
-  for (int it = tid; it < items; it += nthr) {
+  for (int it = tid; it < items; it += 256) {
     const int hl = it >> 4;  // 0 = q head, 1 = k head, 2 + j = value head kh * G + j
     const int base = hl == 0 ? kh * 128 : (hl == 1 ? (a.hk + kh) * 128 : (2 * a.hk + kh * G + hl - 2) * 128);
     float* dst = hl < 2 ? qk_s + hl * 128 : v_s + (hl - 2) * 128;
@@ -132,43 +141,41 @@ __global__ __launch_bounds__(256 * FD_MAX_GROUPS) void decode_fused_kernel(Fused
   for (int e = 0; e < 8; ++e) kq = fmaf(kv[e], qv[e], kq);
   kq = sum16(kq);
 
-  for (int j0 = 0; j0 < G; j0 += ng) {
-    const int j = j0 + gi;
-    const bool act = gi < ng && j < G;
-    if (act) {
-      if (j0 > 0 || DT != DT_BF16) load_state(j);
-      const int h = kh * G + j;
-      const int64_t bh = (int64_t)b * a.hv + h;
-      float* S = a.state + ((int64_t)slot * a.hv + h) * (128 * 128);
-      const float alpha = __expf(a.g[bh]);
-      const float beta = a.beta[bh];
+  for (int j = 0; j < G; ++j) {
+    if (j > 0 || DT != DT_BF16) load_state(j);
+    const int h = kh * G + j;
+    const int64_t bh = (int64_t)b * a.hv + h;
+    float* S = a.state + ((int64_t)slot * a.hv + h) * (128 * 128);
+    float* oj = o_s + (j & 3) * 128;
+    const float alpha = __expf(a.g[bh]);
+    const float beta = a.beta[bh];
 #pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const int row = p * 16 + w * 4 + sub;
-        const float x[8] = {s[p][0].x, s[p][0].y, s[p][0].z, s[p][0].w,
-                            s[p][1].x, s[p][1].y, s[p][1].z, s[p][1].w};
-        float sk = 0.f, sq = 0.f;
+    for (int p = 0; p < 8; ++p) {
+      const int row = p * 16 + w * 4 + sub;
+      const float x[8] = {s[p][0].x, s[p][0].y, s[p][0].z, s[p][0].w,
+                          s[p][1].x, s[p][1].y, s[p][1].z, s[p][1].w};
+      float sk = 0.f, sq = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          sk = fmaf(x[e], kv[e], sk);
-          sq = fmaf(x[e], qv[e], sq);
-        }
-        sk = sum16(sk);
-        sq = sum16(sq);
-        const float d = beta * (v_s[j * 128 + row] - alpha * sk);
-        float y[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = fmaf(alpha, x[e], d * kv[e]);
-        *reinterpret_cast<float4*>(S + row * 128 + c) = make_float4(y[0], y[1], y[2], y[3]);
-        *reinterpret_cast<float4*>(S + row * 128 + 64 + c) = make_float4(y[4], y[5], y[6], y[7]);
-        if ((l & 15) == 0) o_s[gi * 128 + row] = a.scale * fmaf(alpha, sq, d * kq);
+      for (int e = 0; e < 8; ++e) {
+        sk = fmaf(x[e], kv[e], sk);
+        sq = fmaf(x[e], qv[e], sq);
       }
+      sk = sum16(sk);
+      sq = sum16(sq);
+      const float d = beta * (v_s[j * 128 + row] - alpha * sk);
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = fmaf(alpha, x[e], d * kv[e]);
+      *reinterpret_cast<float4*>(S + row * 128 + c) = make_float4(y[0], y[1], y[2], y[3]);
+      *reinterpret_cast<float4*>(S + row * 128 + 64 + c) = make_float4(y[4], y[5], y[6], y[7]);
+      if ((l & 15) == 0) oj[row] = a.scale * fmaf(alpha, sq, d * kq);
     }
+    // Slot j % 4 is rewritten at head j + 4, after three more barriers that wave j % 4 reaches
+    // only once this norm is done.
     __syncthreads();
-    if (act && w == 0) {  // gated RMS-norm of head h by the group's first wave, two values a lane
-      const int h = kh * G + j;
-      const int64_t rb = ((int64_t)b * a.hv + h) * 128;
-      const float o0 = o_s[gi * 128 + 2 * l], o1 = o_s[gi * 128 + 2 * l + 1];
+    if (w == (j & 3)) {  // gated RMS-norm of head h, two values a lane
+      const int64_t rb = bh * 128;
+      const float o0 = oj[2 * l], o1 = oj[2 * l + 1];
       float ss = fmaf(o0, o0, o1 * o1);
       ss = sum16(ss);
       ss += __shfl_xor(ss, 16);
@@ -183,7 +190,6 @@ __global__ __launch_bounds__(256 * FD_MAX_GROUPS) void decode_fused_kernel(Fused
         store1<ODT>(a.o, rb + 2 * l + 1, o1);
       }
     }
-    if (j0 + ng < G) __syncthreads();  // o_s is refilled by the next round
   }
 }
 
@@ -196,9 +202,8 @@ static void launch_fd_o(const FusedDecodeArgs& a, dim3 grid, dim3 block, size_t 
 hipError_t launch_decode_fused(const FusedDecodeArgs& a, hipStream_t st) {
   if (a.batch == 0) return hipSuccess;
   const int G = a.hv / a.hk;
-  const int ng = G < FD_MAX_GROUPS ? G : FD_MAX_GROUPS;
-  const dim3 grid((unsigned)a.batch * (unsigned)a.hk), block(256 * ng);
-  const size_t smem = (size_t)(2 + G + ng) * 128 * sizeof(float);
+  const dim3 grid((unsigned)a.batch * (unsigned)a.hk), block(256);
+  const size_t smem = (size_t)(2 + G + 4) * 128 * sizeof(float);  // <= 63 KiB for G <= 120
   if (a.dtype == DT_BF16) launch_fd_o<DT_BF16>(a, grid, block, smem, st);
   else launch_fd_o<DT_F32>(a, grid, block, smem, st);
   return hipGetLastError();
