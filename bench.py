@@ -3,7 +3,9 @@
 One step = the full-layer prefill chain on T = 8192 tokens of one sequence with the layer's
 shapes (16 key / 48 value heads of 128, hidden 5120): kernel-4 causal conv + SiLU + L2 norm of
 q/k over the 10240 q|k|v channels -> chunked gated delta rule (chunk 64, fp32 state) -> gated
-RMSNorm.  `value` is tokens/s of that chain.  The same run also times the batched decode step
+RMSNorm.  `value` is tokens/s of that chain as the library runs it fastest: the conv inside the
+prefill call (agnes_gdn_prefill_fused), then the norm.  The same chain as three separate calls
+(conv, prefill, norm) is timed beside it.  The same run also times the batched decode step
 (256 sequences, one token each, fp32 states updated in place) and reports its state HBM GB/s,
 and the fused decode step (conv-history update + conv + L2 + recurrence + gated norm in one
 launch) beside the three unfused calls it replaces.
@@ -37,6 +39,8 @@ HK, HV, D, CH = 16, 48, 128, 64
 FLOP_PER_CHUNK_GROUP = 2 * (2 * CH * CH * D + 3 * 2 * CH * CH * D) + 3 * 2 * (3 * CH * D * D + CH * CH * D)
 FLOP_PER_TOKEN = FLOP_PER_CHUNK_GROUP * HK // CH                      # 7,602,176
 PREFILL_BYTES = T * (2 * HK * D * 2 + HV * D * 2 + HV * D * 2 + 2 * HV * 4) + HV * D * D * 4  # q,k,v,o,g,beta + final state
+# fused call: x (q|k|v channels) in, conv weights, g, beta, o out, final state
+PREFILL_FUSED_BYTES = T * (10240 * 2 + 2 * HV * 4 + HV * D * 2) + 10240 * 4 * 2 + HV * D * D * 4
 CONV_BYTES = T * 10240 * 2 * 2 + 10240 * 4 * 2                        # x in, y out, weights
 NORM_BYTES = T * HV * D * 2 * 3 + D * 2                               # o, z in, y out, weight
 DECODE_B = 256
@@ -137,7 +141,7 @@ def main():
     k = y[:, 2048:4096].view(T, HK, D)
     v = y[:, 4096:].view(T, HV, D)
 
-    def step(ev=None):
+    def step(ev=None):  # the chain as three calls
         if ev is not None:
             ev[0].record()
         gdn.conv(x, w, y=y, cu_seqlens=cu, l2norm_heads=32)
@@ -150,19 +154,37 @@ def main():
         if ev is not None:
             ev[3].record()
 
+    def fstep(ev=None):  # conv inside the prefill call, then the norm
+        if ev is not None:
+            ev[0].record()
+        gdn.prefill_fused(x, w, g, beta, cu, num_k_heads=HK, final_state=fin, o=o, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+        gdn.gated_rmsnorm(o, z, nw, y=out)
+        if ev is not None:
+            ev[2].record()
+
     for _ in range(args.warmup):
         step()
+        fstep()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     ms_conv = np.mean([e[0].elapsed_time(e[1]) for e in evs])
     ms_pre = np.mean([e[1].elapsed_time(e[2]) for e in evs])
     ms_norm = np.mean([e[2].elapsed_time(e[3]) for e in evs])
     ms_step = np.mean([e[0].elapsed_time(e[3]) for e in evs])
+    fevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        fstep(fevs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_fpre = np.mean([e[0].elapsed_time(e[1]) for e in fevs])
+    ms_fnorm = np.mean([e[1].elapsed_time(e[2]) for e in fevs])
+    ms_fstep = np.mean([e[0].elapsed_time(e[2]) for e in fevs])
     value = T * args.steps / wall
 
     # ---- calibration copy of known size (untimed; read by the HBM counter runs)
@@ -229,7 +251,7 @@ def main():
     ms_fused = np.mean([e[0].elapsed_time(e[1]) for e in fevs])
     fused_gbs = FUSED_DECODE_BYTES / (ms_fused * 1e-3) / 1e9
 
-    pre_tflops = FLOP_PER_TOKEN * T / (ms_pre * 1e-3) / 1e12
+    pre_tflops = FLOP_PER_TOKEN * T / (ms_fpre * 1e-3) / 1e12
     res = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -244,18 +266,24 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "delta-layer prefill chain, T=8192, 1 sequence: conv(k=4)+SiLU+L2 -> "
-                               "chunked gated delta rule (chunk 64) -> gated RMSNorm",
+                               "chunked gated delta rule (chunk 64) -> gated RMSNorm; conv and prefill in "
+                               "one call (agnes_gdn_prefill_fused)",
                    "T": T, "num_k_heads": HK, "num_v_heads": HV, "head_dim": D, "chunk": CH,
                    "io_dtype": "bf16", "matrix_core_operands": "fp16", "accumulate": "fp32",
                    "state": "fp32", "parallelism": "none (1 GPU)"},
-        "kernels_ms": {"conv": round(ms_conv, 4), "prefill_chunked": round(ms_pre, 4),
-                       "gated_rmsnorm": round(ms_norm, 4), "chain_events": round(ms_step, 4)},
+        "kernels_ms": {"prefill_fused": round(ms_fpre, 4), "gated_rmsnorm": round(ms_fnorm, 4),
+                       "chain_events": round(ms_fstep, 4)},
+        "unfused_chain": {"conv": round(ms_conv, 4), "prefill_chunked": round(ms_pre, 4),
+                          "gated_rmsnorm": round(ms_norm, 4), "chain_events": round(ms_step, 4),
+                          "tokens_per_s": round(T / (ms_step * 1e-3), 1),
+                          "prefill_chunked_TFLOPs": round(FLOP_PER_TOKEN * T / (ms_pre * 1e-3) / 1e12, 2),
+                          "prefill_chunked_traffic": measured_traffic("prefill_chunked")},
         "roofline": {"bound": "mfma",
-                     "kernel": "agnes_gdn_prefill_chunked call (chunk_offsets + prep + scan launches)",
+                     "kernel": "agnes_gdn_prefill_fused call (chunk_offsets + prep + scan launches)",
                      "achieved": round(pre_tflops, 2),
                      "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(pre_tflops / MFMA_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("prefill_chunked"), "flops_per_launch": FLOP_PER_TOKEN * T,
-                     "hbm_GBps_algorithmic": round(PREFILL_BYTES / (ms_pre * 1e-3) / 1e9, 1)},
+                     "traffic": measured_traffic("prefill_fused"), "flops_per_launch": FLOP_PER_TOKEN * T,
+                     "hbm_GBps_algorithmic": round(PREFILL_FUSED_BYTES / (ms_fpre * 1e-3) / 1e9, 1)},
         "streaming_kernels": {
             "conv_GBps": round(CONV_BYTES / (ms_conv * 1e-3) / 1e9, 1),
             "gated_rmsnorm_GBps": round(NORM_BYTES / (ms_norm * 1e-3) / 1e9, 1)},

@@ -9,6 +9,7 @@ The layer (model card "Agnes-3.0-Flash Preview", 架构 table, delta-rule row;
 discosf article "Agnes 3.0 Flash 刚上线就刷屏…", section 二.1):
   conv            kernel-4 causal depth-wise conv + SiLU (+ L2 norm of q/k heads)
   prefill_chunked chunked gated delta rule (chunk 64) over a packed batch
+  prefill_fused   conv + SiLU + L2 and the chunked prefill in one call, from the raw q|k|v projection
   decode_step     stepwise gated delta rule, state updated in place
   gated_rmsnorm   y = rmsnorm(o) * w * silu(z)
   decode_fused    one decode token through conv, recurrence and norm in one launch
@@ -17,7 +18,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["conv", "prefill_chunked", "decode_step", "gated_rmsnorm", "decode_fused", "prefill_workspace_size",
+__all__ = ["conv", "prefill_chunked", "prefill_fused", "decode_step", "gated_rmsnorm", "decode_fused",
+           "prefill_workspace_size",
            "AgnesError", "version", "LIB_PATH"]
 
 LIB_PATH = _lib.LIB_PATH
@@ -161,6 +163,57 @@ def prefill_chunked(q, k, v, g, beta, cu_seqlens, *, initial_state=None, final_s
         _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
         _stream(q.device))
     _check("agnes_gdn_prefill_chunked", st)
+    return o, final_state
+
+
+def prefill_fused(x, conv_weight, g, beta, cu_seqlens, *, num_k_heads, conv_bias=None, conv_state=None,
+                  initial_state=None, final_state=None, output_final_state=True, scale=1.0, l2norm_eps=1e-6,
+                  o=None, o_dtype=None, workspace=None):
+    """Causal conv (kernel 4) + SiLU + L2(q, k) and the chunked prefill in one call.
+
+    x: bf16 [T, (2 Hk + Hv) * 128] raw projection output, channels q | k | v (row stride free,
+    inner stride 1); conv_weight: [C, 4]; conv_bias: [C] or None; conv_state: [N, C, 3] (updated
+    in place to each sequence's final history) or None; the rest as ``prefill_chunked``.
+    Returns (o [T, Hv, 128], final_state or None).
+    """
+    T, C = x.shape
+    Hk = num_k_heads
+    Hv = C // HEAD_DIM - 2 * Hk
+    if Hv <= 0 or C != (2 * Hk + Hv) * HEAD_DIM:
+        raise ValueError(f"x: {C} channels do not hold 2 x {Hk} key heads and whole value heads")
+    xs = _rows(x, "x", C)
+    for t, name in ((conv_weight, "conv_weight"), (conv_bias, "conv_bias"), (conv_state, "conv_state")):
+        if t is not None and (t.dtype != x.dtype or not t.is_contiguous()):
+            raise ValueError(f"{name}: contiguous, with x's dtype {x.dtype}")
+    if tuple(conv_weight.shape) != (C, 4):
+        raise ValueError("conv_weight: [C, 4] expected")
+    for t, name in ((g, "g"), (beta, "beta")):
+        if t.dtype != torch.float32 or tuple(t.shape) != (T, Hv) or not t.is_contiguous():
+            raise ValueError(f"{name}: expected contiguous fp32 [{T}, {Hv}]")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    n = cu_seqlens.numel() - 1
+    if conv_state is not None and tuple(conv_state.shape) != (n, C, 3):
+        raise ValueError(f"conv_state: expected [{n}, {C}, 3]")
+    if o is None:
+        o = torch.empty((T, Hv, HEAD_DIM), dtype=o_dtype or x.dtype, device=x.device)
+    elif not o.is_contiguous():
+        raise ValueError("o must be contiguous")
+    for s, name in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if s is not None and (s.dtype != torch.float32 or not s.is_contiguous()
+                              or tuple(s.shape) != (n, Hv, HEAD_DIM, HEAD_DIM)):
+            raise ValueError(f"{name}: expected contiguous fp32 [{n}, {Hv}, 128, 128]")
+    if final_state is None and output_final_state:
+        final_state = torch.empty((n, Hv, HEAD_DIM, HEAD_DIM), dtype=torch.float32, device=x.device)
+    need = prefill_workspace_size(n, T, Hk, Hv, torch.bfloat16)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    st = _lib.load().agnes_gdn_prefill_fused(
+        _ptr(x), xs, _dt(x), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state), _ptr(g), _ptr(beta),
+        _ptr(cu_seqlens), n, T, Hk, Hv, HEAD_DIM, scale, l2norm_eps, _ptr(initial_state), _ptr(final_state),
+        _ptr(o), _dt(o), _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(x.device))
+    _check("agnes_gdn_prefill_fused", st)
     return o, final_state
 
 

@@ -17,6 +17,10 @@ SIGNATURES = {
                                           c_void_p, c_void_p, c_void_p, c_int, c_int64, c_int, c_int,
                                           c_int, c_float, c_void_p, c_void_p, c_void_p, c_int,
                                           c_void_p, c_size_t, c_void_p]),
+    "agnes_gdn_prefill_fused": (c_int, [c_void_p, c_int64, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                        c_void_p, c_void_p, c_int, c_int64, c_int, c_int, c_int, c_float,
+                                        c_float, c_void_p, c_void_p, c_void_p, c_int, c_void_p, c_size_t,
+                                        c_void_p]),
     "agnes_gdn_decode_step": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int64, c_int64,
                                       c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_float,
                                       c_void_p, c_void_p, c_int, c_void_p]),

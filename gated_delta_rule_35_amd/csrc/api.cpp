@@ -144,6 +144,52 @@ AGNES_API int agnes_gdn_prefill_chunked(const void* q, const void* k, const void
   return hip_status(in_dtype == AGNES_BF16 ? agnes::launch_prefill_mfma(a, st) : agnes::launch_prefill_f32(a, st));
 }
 
+AGNES_API int agnes_gdn_prefill_fused(const void* x, int64_t x_token_stride, agnes_dtype dtype,
+                                      const void* conv_weight, const void* conv_bias, void* conv_state,
+                                      const float* g, const float* beta, const int32_t* cu_seqlens, int num_seqs,
+                                      int64_t total_tokens, int num_k_heads, int num_v_heads, int head_dim,
+                                      float scale, float l2norm_eps, const float* initial_state, float* final_state,
+                                      void* o, agnes_dtype o_dtype, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (!valid_dtype(dtype) || !valid_dtype(o_dtype)) return AGNES_ERR_INVALID_ARG;
+  if (num_seqs < 0 || total_tokens < 0 || num_k_heads <= 0 || num_v_heads <= 0) return AGNES_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim || num_v_heads % num_k_heads || dtype != AGNES_BF16) return AGNES_ERR_UNSUPPORTED;
+  if (num_seqs == 0 && total_tokens != 0) return AGNES_ERR_INVALID_ARG;
+  if (num_seqs > 0 && (!cu_seqlens || !conv_weight)) return AGNES_ERR_INVALID_ARG;
+  if (total_tokens > 0 && (!x || !g || !beta || !o)) return AGNES_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(conv_weight, 16) || !aligned(conv_bias, 16) || !aligned(conv_state, 4) ||
+      !aligned(o, 16) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(initial_state, 16) ||
+      !aligned(final_state, 16) || !aligned(cu_seqlens, 4))
+    return AGNES_ERR_INVALID_ARG;
+  const int64_t C = (int64_t)(2 * num_k_heads + num_v_heads) * head_dim;
+  if (x_token_stride < C || x_token_stride % 8) return AGNES_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(l2norm_eps >= 0.f) || !std::isfinite(l2norm_eps)) return AGNES_ERR_INVALID_ARG;
+  if ((int64_t)num_seqs * num_v_heads * 8 > INT32_MAX || (int64_t)num_seqs > 65535) return AGNES_ERR_UNSUPPORTED;
+  const int64_t sbytes = (int64_t)num_seqs * num_v_heads * head_dim * head_dim;
+  const Span s0 = span(initial_state, 1, 0, sbytes, 4), s1 = span(final_state, 1, 0, sbytes, 4);
+  if (initial_state && final_state && initial_state != final_state && overlap(s0, s1)) return AGNES_ERR_INVALID_ARG;
+  const int64_t rowo = (int64_t)num_v_heads * head_dim;
+  const Span os = span(o, total_tokens, rowo, rowo, esize(o_dtype));
+  const Span xs = span(x, total_tokens, x_token_stride, C, 2);
+  const Span cs = span(conv_state, conv_state ? 1 : 0, 0, (int64_t)num_seqs * C * 3, 2);
+  const Span ws_span = span(workspace, workspace ? 1 : 0, 0, (int64_t)workspace_bytes, 1);
+  // outputs and in-place buffers must be disjoint from each other and from every input
+  if (overlap(os, xs) || overlap(os, s1) || overlap(os, s0) || overlap(os, cs) || overlap(cs, xs) || overlap(cs, s1) ||
+      overlap(cs, s0) || overlap(s1, xs) || overlap(ws_span, os) || overlap(ws_span, xs) || overlap(ws_span, cs) ||
+      overlap(ws_span, s1))
+    return AGNES_ERR_INVALID_ARG;
+  const size_t need = agnes_gdn_prefill_workspace_size(num_seqs, total_tokens, num_k_heads, num_v_heads, head_dim,
+                                                       AGNES_BF16);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return AGNES_ERR_WORKSPACE;
+
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  agnes::PrefillArgs a{xb, xb + (int64_t)num_k_heads * head_dim, xb + (int64_t)2 * num_k_heads * head_dim,
+                       (int)AGNES_BF16, x_token_stride, x_token_stride, g, beta, cu_seqlens, num_seqs, total_tokens,
+                       num_k_heads, num_v_heads, scale, initial_state, final_state, o, (int)o_dtype, workspace,
+                       workspace_bytes, conv_weight, conv_bias, conv_state, l2norm_eps};
+  return hip_status(agnes::launch_prefill_mfma(a, static_cast<hipStream_t>(stream)));
+}
+
 AGNES_API int agnes_gdn_decode_step(const void* q, const void* k, const void* v, agnes_dtype in_dtype,
                                     int64_t qk_token_stride, int64_t v_token_stride, const float* g,
                                     const float* beta, int batch, int num_k_heads, int num_v_heads, int head_dim,

@@ -78,6 +78,20 @@ __device__ __forceinline__ void widen8(const Raw8<DT>& r, float out[8]) {
   }
 }
 
+// Element i (0..8n-1) of n consecutive raw 8-element loads, as fp32.
+template <int DT>
+__device__ __forceinline__ float raw_at(const Raw8<DT>* r, int i) {
+  if constexpr (DT == DT_BF16) {
+    const uint4 u = r[i >> 3].u[0];
+    const uint32_t wd = ((i & 7) >> 1) == 0 ? u.x : ((i & 7) >> 1) == 1 ? u.y : ((i & 7) >> 1) == 2 ? u.z : u.w;
+    return __uint_as_float((i & 1) ? (wd & 0xffff0000u) : (wd << 16));
+  } else {
+    const uint4 u = r[i >> 3].u[(i & 7) >> 2];
+    const uint32_t wd = (i & 3) == 0 ? u.x : (i & 3) == 1 ? u.y : (i & 3) == 2 ? u.z : u.w;
+    return __uint_as_float(wd);
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ void store8(void* base, int64_t idx, const float v[8]) {
   if constexpr (DT == DT_BF16) {
@@ -104,6 +118,29 @@ template <int DT>
 __device__ __forceinline__ void store1(void* base, int64_t idx, float v) {
   if constexpr (DT == DT_BF16) static_cast<uint16_t*>(base)[idx] = (uint16_t)f32_to_bf16(v);
   else static_cast<float*>(base)[idx] = v;
+}
+
+// ---------------------------------------------------------------- causal conv, kernel 4
+// bias + sum_j w[e][j] x_j[e] for 8 channels e of one output row: x_j are the row's four input
+// rows (bf16 as loaded, oldest first), w the channels' taps as stored ([channel][4] bf16: for
+// channel e, dword 2e holds taps 0, 1 and dword 2e+1 taps 2, 3).  Each channel takes two bf16
+// dot products (exact bf16 x bf16 products, fp32 sums); pairs of one channel's inputs from two
+// rows are gathered with byte permutes.
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, a), __builtin_bit_cast(bf16x2v, b), c, false);
+}
+__device__ __forceinline__ uint32_t dw(const uint4& u, int i) { return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w; }
+__device__ __forceinline__ void conv4_bf16x8(const uint4 (&x)[4], const uint4 (&w)[4], const float (&bias)[8],
+                                             float (&acc)[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // dword i of a row: channels 2i (low half), 2i+1 (high half)
+    const uint32_t a0 = dw(x[0], i), a1 = dw(x[1], i), a2 = dw(x[2], i), a3 = dw(x[3], i);
+    const uint32_t p01l = __builtin_amdgcn_perm(a1, a0, 0x05040100u), p01h = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+    const uint32_t p23l = __builtin_amdgcn_perm(a3, a2, 0x05040100u), p23h = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
+    acc[2 * i] = dot2_bf16(dw(w[i], 1), p23l, dot2_bf16(dw(w[i], 0), p01l, bias[2 * i]));
+    acc[2 * i + 1] = dot2_bf16(dw(w[i], 3), p23h, dot2_bf16(dw(w[i], 2), p01h, bias[2 * i + 1]));
+  }
 }
 
 // ---------------------------------------------------------------- reductions

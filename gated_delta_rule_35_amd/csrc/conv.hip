@@ -252,6 +252,16 @@ static hipError_t launch_conv_t(const ConvArgs& a, hipStream_t st) {
   return hipSuccess;
 }
 
+hipError_t launch_conv_history(const ConvArgs& a, hipStream_t st) {
+  if (!a.state || a.num_seqs == 0) return hipSuccess;
+  const unsigned cblocks = (unsigned)((a.channels / 8 + CONV_THREADS - 1) / CONV_THREADS);
+  if (a.dtype == DT_BF16)
+    hipLaunchKernelGGL((conv_state_kernel<DT_BF16>), dim3(cblocks, (unsigned)a.num_seqs), dim3(CONV_THREADS), 0, st, a);
+  else
+    hipLaunchKernelGGL((conv_state_kernel<DT_F32>), dim3(cblocks, (unsigned)a.num_seqs), dim3(CONV_THREADS), 0, st, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_conv(const ConvArgs& a, hipStream_t st) {
   return a.dtype == DT_BF16 ? launch_conv_t<DT_BF16>(a, st) : launch_conv_t<DT_F32>(a, st);
 }

@@ -26,20 +26,6 @@
 
 namespace agnes {
 
-// Element i (0..8n-1) of n consecutive raw 8-element loads, as fp32.
-template <int DT>
-__device__ __forceinline__ float raw_at(const Raw8<DT>* r, int i) {
-  if constexpr (DT == DT_BF16) {
-    const uint4 u = r[i >> 3].u[0];
-    const uint32_t wd = ((i & 7) >> 1) == 0 ? u.x : ((i & 7) >> 1) == 1 ? u.y : ((i & 7) >> 1) == 2 ? u.z : u.w;
-    return __uint_as_float((i & 1) ? (wd & 0xffff0000u) : (wd << 16));
-  } else {
-    const uint4 u = r[i >> 3].u[(i & 7) >> 2];
-    const uint32_t wd = (i & 3) == 0 ? u.x : (i & 3) == 1 ? u.y : (i & 3) == 2 ? u.z : u.w;
-    return __uint_as_float(wd);
-  }
-}
-
 // Conv + SiLU (+ L2 over the 16 lanes of a head) of channels c0..c0+7 of entry b, result to
 // dst (LDS); the history of those channels in slot `slot` advances by the current input.
 // Inputs stay as loaded (raw) and are widened where used, to keep registers free for the

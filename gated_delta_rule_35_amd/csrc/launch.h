@@ -46,6 +46,13 @@ struct PrefillArgs {
   int o_dtype;
   void* workspace;
   size_t workspace_bytes;
+  // Fused prologue (all null for the plain call): q, k, v above are the q | k | v channel
+  // ranges of the raw projection output x (row stride qk_stride == v_stride), and the
+  // prefill applies the causal conv + SiLU + L2 of q, k itself.
+  const void* conv_w;     // [(2 hk + hv) * 128, 4] bf16
+  const void* conv_b;     // [(2 hk + hv) * 128] bf16 or nullptr
+  void* conv_hist;        // [num_seqs, (2 hk + hv) * 128, 3] bf16 or nullptr (zeros); advanced after the call
+  float l2_eps;
 };
 
 struct DecodeArgs {
@@ -104,6 +111,7 @@ struct NormArgs {
 };
 
 hipError_t launch_conv(const ConvArgs& a, hipStream_t s);
+hipError_t launch_conv_history(const ConvArgs& a, hipStream_t s);  // final history only
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s);
 size_t prefill_mfma_workspace(int num_seqs, int64_t total, int hk, int hv);

@@ -38,6 +38,13 @@
 //     other half of a double buffer with the next chunk (q/k image, record, V slice) by direct
 //     global -> LDS loads.  Each chunk costs one workgroup barrier; each role runs its own
 //     loop with the same barrier count, so registers are allocated per role.
+// Fused prologue (same kernels, compiled a second time): q, k, v are the channel ranges of
+// the raw projection output x, and the causal conv (kernel 4) + SiLU + L2 of q and k run
+// inside the prefill instead of in a separate pass over x.  prep convolves the chunk's q and
+// k rows (a 3-token halo from x, or from the conv history before a sequence's first token)
+// straight into its fp16 staging; in the scan the copy waves bring the raw x rows of the V
+// slice one chunk early and convolve them while the next chunk's copies are in flight.  The
+// conv history is advanced by a fourth launch once every read of the old one is done.
 // Number formats: bf16 inputs widen exactly to fp16 (normal range); fp32 intermediates
 // (S, R', U, P, X) are rounded to fp16 once per use (2^-11 relative); every product
 // accumulates in fp32 and the state itself stays fp32.
@@ -57,6 +64,7 @@ constexpr int NWAVES = 2 + NCP;  // chain wave, output wave, copy waves
 constexpr int DVB = 16 * NVT;
 constexpr int NB = D / DVB;  // scan workgroups per value head
 constexpr int LDV = DVB + 8; // bf16 row stride of the staged V slice
+constexpr int VR_ROWS = 80;  // raw x rows of a V slice (fused): 3 halo + 64, to 5 x 1 KiB copies
 }  // namespace mp
 
 // Per (chunk, value head) record written by prep and copied verbatim into LDS by scan, so it
@@ -200,8 +208,10 @@ __host__ __device__ constexpr int tri(int i, int j) { return i * (i + 1) / 2 + j
 struct PrepSmem {
   union U {
     struct {
-      uint16_t Q[mp::C][mp::LDQ];   // bf16 q rows as stored (rows >= L: copies of row 0)
-      uint16_t K[mp::C][mp::LDQ];   // bf16 k rows as stored
+      uint16_t Q[mp::C][mp::LDQ];   // bf16 q rows as stored (rows >= L: copies of row 0); fused: fp16
+      uint16_t K[mp::C][mp::LDQ];   // bf16 k rows as stored; fused: fp16
+      uint16_t Xq[mp::C + 4][mp::D];  // fused: raw x rows c0 - 3 .. c0 + 64 of the q head (bf16)
+      uint16_t Xk[mp::C + 4][mp::D];  // fused: the same for the k head
     } qk;                           // until the Gram products are done
     struct Head {
       float A[10][16][17];          // lower blocks of A, fp32
@@ -253,6 +263,7 @@ __device__ __forceinline__ f4 blk_xz(const PrepSmem::U::Head& hd, int i, int ln,
 // One workgroup per (chunk, key group, round of up to PH value heads of the group): the q/k
 // rows, the Gram products and the fp16 q/k image are shared; each value head of the round
 // has four waves of its own for the decay-scaled A, P and X.
+template <bool FUSED>
 __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6))) void prep_kernel(PrefillArgs a, int64_t maxch) {
   using namespace mp;
   __shared__ PrepSmem sm;
@@ -281,9 +292,26 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
   unsigned char* rec = base + ws.rec + ((size_t)h * maxch + j) * REC_BYTES;
   PrepSmem::U::Head& hd = sm.u.hd[slot];
 
-  // ---- q, k rows of the chunk -> LDS (direct copies, 17 x 1 KiB per matrix, spread over
-  // the waves; the 17th 16-byte piece of a row is padding and re-reads the row's start)
-  {
+  if constexpr (FUSED) {
+    // ---- raw x rows c0 - 3 .. c0 + 64 of the q and k heads -> LDS (direct copies, 17 x 1 KiB
+    // per head); rows outside the sequence re-read row c0 (the halo before the sequence start is
+    // taken from the conv history in the conv pass below).
+    const uint16_t* xq = static_cast<const uint16_t*>(a.q) + (int64_t)kh * D;  // a.q: channel 0 of x
+    const uint16_t* xk = static_cast<const uint16_t*>(a.k) + (int64_t)kh * D;
+#pragma unroll
+    for (int t = 0; t < (34 + 4 * PH - 1) / (4 * PH); ++t) {
+      const int i = w + 4 * PH * t;
+      if (i >= 34) break;
+      const int ii = i < 17 ? i : i - 17;
+      const int jj = 64 * ii + lane, row = jj >> 4, pc = jj & 15;
+      const int64_t pos = c0 - 3 + row;
+      const int64_t o = (pos >= start && row < 3 + L ? pos : c0) * a.qk_stride + 8 * pc;
+      uint16_t* dst = (i < 17 ? &sm.u.qk.Xq[0][0] : &sm.u.qk.Xk[0][0]) + 512 * ii;
+      __builtin_amdgcn_global_load_lds((glb_void*)((i < 17 ? xq : xk) + o), (lds_void*)dst, 16, 0, 0);
+    }
+  } else {
+    // ---- q, k rows of the chunk -> LDS (direct copies, 17 x 1 KiB per matrix, spread over
+    // the waves; the 17th 16-byte piece of a row is padding and re-reads the row's start)
     constexpr int QPR = LDQ / 8;
     const uint16_t* qb = static_cast<const uint16_t*>(a.q) + c0 * a.qk_stride + (int64_t)kh * D;
     const uint16_t* kb = static_cast<const uint16_t*>(a.k) + c0 * a.qk_stride + (int64_t)kh * D;
@@ -315,6 +343,57 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
   }
   __builtin_amdgcn_s_waitcnt(0);
   lds_barrier();
+  if constexpr (FUSED) {
+    // ---- conv + SiLU + L2 of the staged rows, fp16 into Q / K (rows >= L zero).  Thread
+    // (row group rr, head hs, 8 channels col) takes rows rr, rr + 24, rr + 48; the 16 lanes of a
+    // (row, head) are consecutive, so the L2 norm is a 16-lane sum.
+    const int col = tid & 15, hs = (tid >> 4) & 1, rr = tid >> 5;
+    const int Ctot = (2 * a.hk + a.hv) * D;
+    const int ch = (hs ? a.hk + kh : kh) * D + 8 * col;
+    uint4 wr[4];  // conv taps of the 8 channels, packed bf16 as stored
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) wr[q4] = load_raw8<DT_BF16>(a.conv_w, (int64_t)ch * 4 + 8 * q4).u[0];
+    float bs[8];
+    if (a.conv_b) load8<DT_BF16>(a.conv_b, ch, bs);
+    else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bs[e] = 0.f;
+    }
+    const uint16_t (*X)[D] = hs ? sm.u.qk.Xk : sm.u.qk.Xq;
+    const uint16_t* hist = static_cast<const uint16_t*>(a.conv_hist);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int r = rr + 24 * k;
+      if (r >= C) break;
+      uint4 xr[4];
+#pragma unroll
+      for (int jt = 0; jt < 4; ++jt) {
+        const int i = r + jt;  // staged row i = x row c0 - 3 + i
+        if (c0 - 3 + i < start) {  // before the sequence start: history entry i (oldest first)
+          const uint16_t* hp = hist + ((int64_t)n * Ctot + ch) * 3 + i;
+          xr[jt] = hist ? make_uint4(hp[0] | (uint32_t)hp[3] << 16, hp[6] | (uint32_t)hp[9] << 16,
+                                          hp[12] | (uint32_t)hp[15] << 16, hp[18] | (uint32_t)hp[21] << 16)
+                             : make_uint4(0, 0, 0, 0);
+        } else {
+          xr[jt] = *reinterpret_cast<const uint4*>(&X[i][8 * col]);
+        }
+      }
+      float y[8], ss = 0.f;
+      conv4_bf16x8(xr, wr, bs, y);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        y[e] = silu(y[e]);
+        ss = fmaf(y[e], y[e], ss);
+      }
+      ss = sum16(ss);
+      const float rs = rsqrt_fast(ss + a.l2_eps);
+      h8 hv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hv[e] = r < L ? (_Float16)(y[e] * rs) : (_Float16)0.f;
+      *reinterpret_cast<h8*>(hs ? &sm.u.qk.K[r][8 * col] : &sm.u.qk.Q[r][8 * col]) = hv;
+    }
+    lds_barrier();
+  }
   if (v == 0 && act) {
     float* gr = reinterpret_cast<float*>(rec + offsetof(RecImage, gt));
     gr[lane] = bv;
@@ -331,9 +410,15 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int col = 32 * ks + 8 * lg;
-      const bf8 kbv = *reinterpret_cast<const bf8*>(&sm.u.qk.K[16 * bj + ln][col]);
-      gk = mfma_bf(*reinterpret_cast<const bf8*>(&sm.u.qk.K[16 * bi + ln][col]), kbv, gk);
-      gq = mfma_bf(*reinterpret_cast<const bf8*>(&sm.u.qk.Q[16 * bi + ln][col]), kbv, gq);
+      if constexpr (FUSED) {  // fp16 rows
+        const h8 kbv = *reinterpret_cast<const h8*>(&sm.u.qk.K[16 * bj + ln][col]);
+        gk = mfma_16x16x32(*reinterpret_cast<const h8*>(&sm.u.qk.K[16 * bi + ln][col]), kbv, gk);
+        gq = mfma_16x16x32(*reinterpret_cast<const h8*>(&sm.u.qk.Q[16 * bi + ln][col]), kbv, gq);
+      } else {
+        const bf8 kbv = *reinterpret_cast<const bf8*>(&sm.u.qk.K[16 * bj + ln][col]);
+        gk = mfma_bf(*reinterpret_cast<const bf8*>(&sm.u.qk.K[16 * bi + ln][col]), kbv, gk);
+        gq = mfma_bf(*reinterpret_cast<const bf8*>(&sm.u.qk.Q[16 * bi + ln][col]), kbv, gq);
+      }
     }
   }
   if (rd == 0) {
@@ -342,7 +427,8 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
       const bool isk = i >= C * (D / 8);
       const int r = (i >> 4) & (C - 1), col = 8 * (i & 15);
       const uint4 u = *reinterpret_cast<const uint4*>(isk ? &sm.u.qk.K[r][col] : &sm.u.qk.Q[r][col]);
-      *reinterpret_cast<h8*>(isk ? &img->K[r][col] : &img->Q[r][col]) = cvt8(r < L ? u : make_uint4(0, 0, 0, 0));
+      *reinterpret_cast<h8*>(isk ? &img->K[r][col] : &img->Q[r][col]) =
+          FUSED ? __builtin_bit_cast(h8, u) : cvt8(r < L ? u : make_uint4(0, 0, 0, 0));
     }
   }
   lds_barrier();  // q/k rows are dead from here
@@ -450,6 +536,7 @@ struct ScanSmem {
   ScanBuf B[2];                      // by chunk parity
   float Os[mp::C][mp::DVB + 4];      // output tile staging of the output wave
   ExBuf X[2];                        // by chunk parity
+  uint16_t Vr[2][mp::VR_ROWS][mp::DVB];  // fused prologue: raw x rows of the V slice, by chunk parity
 };
 static_assert(sizeof(ScanSmem) <= 160 * 1024, "scan LDS");
 
@@ -498,6 +585,7 @@ __device__ __forceinline__ void row_bcast16(float v, float (&o)[16]) {
 __device__ __forceinline__ uint2 lds_tr4_raw(const uint16_t* p) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4v*)(p)));
 }
+__device__ __forceinline__ f4 h4_to_f4(h4 v) { return f4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]}; }
 __device__ __forceinline__ f4 bf16x4_to_f4(uint2 u) {
   return f4{__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
             __uint_as_float(u.y & 0xffff0000u)};
@@ -510,6 +598,7 @@ __device__ __forceinline__ f4 bf16x4_to_f4(uint2 u) {
 // and the next chunk's S^T operands to exS for the output wave.  76 products of 16x16x32.
 // The wave issues in order, so the code is laid out by hand: operands are read a step ahead,
 // and the results of a product are first used several products later.
+template <bool VF16>
 __device__ __forceinline__ void chain_step(const ScanBuf& B, ExBuf& exU, ExBuf& exS, int lane, int ln, int lg,
                                            f4 (&sacc)[mp::NVT][8], h8 (&sb)[mp::NVT][4]) {
   using namespace mp;
@@ -576,7 +665,7 @@ __device__ __forceinline__ void chain_step(const ScanBuf& B, ExBuf& exU, ExBuf& 
     f4 rp[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const f4 vv = bf16x4_to_f4(vr[t][i]);
+      const f4 vv = VF16 ? h4_to_f4(__builtin_bit_cast(h4, vr[t][i])) : bf16x4_to_f4(vr[t][i]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) rp[i][e] = bb[4 * i + e] * (vv[e] - gg[4 * i + e] * kq[t][i][e]);
     }
@@ -725,47 +814,97 @@ __device__ __forceinline__ void o_step(const ExBuf& exU, float (*Os)[mp::DVB + 4
   }
 }
 
-// Copy waves: issue the direct global -> LDS loads of chunk c into buffer B (no registers).
-// A chunk is 58 copies of 1 KiB (q/k image 34, record 19, V slice 5) landing back to back in
-// the buffer; copy wave q of NCP issues the copies u = q, q + NCP, ...  The q/k image and the
-// record are contiguous; the V slice is gathered from the strided tensor into padded rows,
-// rows past the end of the chunk re-reading its first row (finite values that only ever meet
-// beta = 0).  Each wave issues at most about one direct copy per 100 cycles, hence several.
-__device__ __forceinline__ void issue_chunk(ScanBuf& B, const PrefillArgs& a, const Geo& G,
-                                            const unsigned char* ws, int c, int q) {
+// Copy waves: issue the direct global -> LDS loads (no registers) of chunk c into buffer
+// B[c & 1] (c < 0: none) and, for the fused prologue, of the raw x rows of chunk cv's V slice
+// into Vr[cv & 1] (cv < 0: none).  A chunk is 58 copies of 1 KiB (q/k image 34, record 19, V
+// slice 5) landing back to back in the buffer; copy wave q of NCP issues the copies u = q,
+// q + NCP, ...  The q/k image and the record are contiguous; the V slice is gathered from
+// the strided tensor into padded rows, rows past the end of the chunk re-reading its first
+// row (finite values that only ever meet beta = 0).  The raw rows of the fused path are the
+// chunk's 64 rows after a 3-row halo (x rows c0 - 3 .. c0 + 76); rows outside the sequence
+// re-read row c0 (the halo before the sequence start comes from the conv history instead).
+// Each wave issues at most about one direct copy per 100 cycles, hence several.
+template <bool FUSED>
+__device__ __forceinline__ void issue_chunk(ScanSmem& sm, const PrefillArgs& a, const Geo& G,
+                                            const unsigned char* ws, int c, int cv, int q) {
   using namespace mp;
   constexpr int NQK = QK_BYTES / 1024, NREC = REC_BYTES / 1024, NV = C * (LDV / 8) / 64;
   static_assert(sizeof(ScanBuf) == (NQK + NREC + NV) * 1024, "chunk buffer is a whole number of copies");
+  static_assert(VR_ROWS * DVB * 2 == NV * 1024, "raw V rows take as many copies as the V slice");
   const int lane = G.lane;
-  const unsigned char* qk = ws + G.qk0 + (size_t)c * QK_BYTES + 16 * lane;
-  const unsigned char* rec = ws + G.rec0 + (size_t)c * REC_BYTES + 16 * lane;
-  const int L = G.len(c);
-  const uint16_t* vb = static_cast<const uint16_t*>(a.v) + (G.start + (int64_t)c * C) * a.v_stride +
-                       (int64_t)G.h * D + G.dv0;
-  unsigned char* dst = reinterpret_cast<unsigned char*>(&B);
+  const int cq = c < 0 ? 0 : c;
+  const unsigned char* qk = ws + G.qk0 + (size_t)cq * QK_BYTES + 16 * lane;
+  const unsigned char* rec = ws + G.rec0 + (size_t)cq * REC_BYTES + 16 * lane;
+  const uint16_t* vb = static_cast<const uint16_t*>(a.v) + (int64_t)G.h * D + G.dv0;
+  unsigned char* dst = reinterpret_cast<unsigned char*>(&sm.B[cq & 1]);
 #pragma unroll
   for (int k = 0; k < (NQK + NREC + NV + NCP - 1) / NCP; ++k) {
     const int u = q + NCP * k;
     if (u >= NQK + NREC + NV) break;
-    const void* src;
-    if (u < NQK) {
-      src = qk + 1024 * u;
-    } else if (u < NQK + NREC) {
-      src = rec + 1024 * (u - NQK);
+    if (u < NQK + NREC) {
+      if (c < 0) continue;
+      const void* src = u < NQK ? (const void*)(qk + 1024 * u) : (const void*)(rec + 1024 * (u - NQK));
+      __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(dst + 1024 * u), 16, 0, 0);
+    } else if constexpr (FUSED) {
+      if (cv < 0) continue;
+      const int64_t c0 = G.start + (int64_t)cv * C;
+      const int jv = 64 * (u - NQK - NREC) + lane, i = jv >> 2, pc = jv & 3;
+      const int64_t pos = c0 - 3 + i;
+      const bool in = pos >= G.start && i < 3 + G.len(cv);
+      const uint16_t* src = vb + (in ? pos : c0) * a.v_stride + 8 * pc;
+      __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(&sm.Vr[cv & 1][0][0] + 8 * jv), 16, 0, 0);
     } else {
+      if (c < 0) continue;
       constexpr int VPR = LDV / 8;  // 16-byte pieces per padded V row (5)
+      const int L = G.len(c);
       const int j = 64 * (u - NQK - NREC) + lane, r = j / VPR, pc = j % VPR;
-      src = vb + ((r < L && pc < DVB / 8) ? (int64_t)r * a.v_stride + 8 * pc : 0);
+      const uint16_t* src = vb + (G.start + (int64_t)c * C) * a.v_stride +
+                            ((r < L && pc < DVB / 8) ? (int64_t)r * a.v_stride + 8 * pc : 0);
+      __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(dst + 1024 * u), 16, 0, 0);
     }
-    __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(dst + 1024 * u), 16, 0, 0);
   }
+}
+
+// Copy waves, fused prologue: the V slice of chunk cc = SiLU(causal conv) of its raw x rows in
+// Vr[cc & 1] (row r of the chunk reads raw rows r .. r + 3), fp16 into B[cc & 1].Vs.  For the
+// sequence's first chunk the halo rows are the conv history (zeros without one).  Item
+// q * 64 + lane < 256: chunk row item / 4, value columns 8 (item % 4) .. + 7; the lane's conv
+// taps (packed bf16, as stored) and biases of those 8 channels are loaded once per sequence.
+__device__ __forceinline__ void conv_vslice(ScanSmem& sm, const PrefillArgs& a, const Geo& G, int n, int cc, int q,
+                                            const uint4 (&wt)[4], const float (&bs)[8]) {
+  using namespace mp;
+  const int item = q * 64 + G.lane;
+  if (item >= C * DVB / 8) return;
+  const int r = item >> 2, cg = item & 3;
+  uint4 xr[4];
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    const int i = r + jt;
+    if (cc == 0 && i < 3) {
+      const uint16_t* hist = static_cast<const uint16_t*>(a.conv_hist);
+      const int64_t ch = (int64_t)(2 * a.hk + G.h) * D + G.dv0 + 8 * cg;
+      const int64_t Ctot = (int64_t)(2 * a.hk + a.hv) * D;
+      const uint16_t* hp = hist + ((int64_t)n * Ctot + ch) * 3 + i;
+      xr[jt] = hist ? make_uint4(hp[0] | (uint32_t)hp[3] << 16, hp[6] | (uint32_t)hp[9] << 16,
+                                 hp[12] | (uint32_t)hp[15] << 16, hp[18] | (uint32_t)hp[21] << 16)
+                    : make_uint4(0, 0, 0, 0);
+    } else {
+      xr[jt] = *reinterpret_cast<const uint4*>(&sm.Vr[cc & 1][i][8 * cg]);
+    }
+  }
+  float acc[8];
+  conv4_bf16x8(xr, wt, bs, acc);
+  h8 o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (_Float16)silu(acc[e]);
+  *reinterpret_cast<h8*>(&sm.B[cc & 1].Vs[r][8 * cg]) = o;
 }
 
 // Waves: 0 chain wave, 1 output wave (both for all NVT value tiles), then NCP copy waves.
 // Iteration c (one LDS barrier each, n + 1 in all): the chain wave on chunk c; the output wave
 // finishes and writes out chunk c-1 and starts chunk c; the copy waves fill the other buffer
 // with chunk c+1.
-template <int O_DT>
+template <int O_DT, bool FUSED>
 __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, int64_t maxch) {
   using namespace mp;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -820,9 +959,10 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
         sm.X[0].s[t][ks][lane] = sb[t][ks];
       }
     }
+    if constexpr (FUSED) lds_barrier();  // (the copy waves' extra prologue step)
     lds_barrier();
     for (int c = 0; c < nc + 1; ++c) {
-      if (c < nc) chain_step(sm.B[c & 1], sm.X[c & 1], sm.X[(c + 1) & 1], lane, ln, lg, sacc, sb);
+      if (c < nc) chain_step<FUSED>(sm.B[c & 1], sm.X[c & 1], sm.X[(c + 1) & 1], lane, ln, lg, sacc, sb);
       lds_barrier();
     }
     if (a.s1) {
@@ -839,6 +979,7 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
     f4 qs[NVT][4];
     h8 pa[6];
     float ge = 0.f;
+    if constexpr (FUSED) lds_barrier();
     lds_barrier();
     for (int c = 0; c < nc + 1; ++c) {
       if (c >= 1) o_step<O_DT>(sm.X[(c - 1) & 1], sm.Os, a, G, c - 1, qs, pa, ge);
@@ -847,17 +988,46 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
     }
   } else {  // copy wave
     const int q = G.w - 2;
-    if (nc > 0) {
-      issue_chunk(sm.B[0], a, G, ws, 0, q);
+    if constexpr (FUSED) {
+      // Step c: copies of chunk c+1 and raw rows of chunk c+2 in flight while the raw rows of
+      // chunk c+1 (landed during step c-1) are convolved into its V slice.
+      uint4 wt[4];  // conv taps of the lane's 8 value channels, packed bf16 as stored
+      float bs[8];
+      const int64_t ch = (int64_t)(2 * a.hk + G.h) * D + G.dv0 + 8 * (lane & 3);
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) wt[q4] = load_raw8<DT_BF16>(a.conv_w, ch * 4 + 8 * q4).u[0];
+      if (a.conv_b) load8<DT_BF16>(a.conv_b, ch, bs);
+      else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bs[e] = 0.f;
+      }
+      if (nc > 0) issue_chunk<true>(sm, a, G, ws, 0, 0, q);
+      if (nc > 1) issue_chunk<true>(sm, a, G, ws, -1, 1, q);
       __builtin_amdgcn_s_waitcnt(0);
-    }
-    lds_barrier();
-    for (int c = 0; c < nc + 1; ++c) {
-      if (c + 1 < nc) {
-        issue_chunk(sm.B[(c + 1) & 1], a, G, ws, c + 1, q);
+      lds_barrier();  // raw rows of chunk 0 visible to every copy wave
+      if (nc > 0) conv_vslice(sm, a, G, n, 0, q, wt, bs);
+      lds_barrier();
+      for (int c = 0; c < nc + 1; ++c) {
+        if (c + 1 < nc) {
+          issue_chunk<true>(sm, a, G, ws, c + 1, c + 2 < nc ? c + 2 : -1, q);
+          conv_vslice(sm, a, G, n, c + 1, q, wt, bs);
+          __builtin_amdgcn_s_waitcnt(0);
+        }
+        lds_barrier();
+      }
+    } else {
+      if (nc > 0) {
+        issue_chunk<false>(sm, a, G, ws, 0, -1, q);
         __builtin_amdgcn_s_waitcnt(0);
       }
       lds_barrier();
+      for (int c = 0; c < nc + 1; ++c) {
+        if (c + 1 < nc) {
+          issue_chunk<false>(sm, a, G, ws, c + 1, -1, q);
+          __builtin_amdgcn_s_waitcnt(0);
+        }
+        lds_barrier();
+      }
     }
   }
 }
@@ -868,7 +1038,7 @@ size_t prefill_mfma_workspace(int num_seqs, int64_t total, int hk, int hv) {
   return WsLayout(num_seqs, hv, hk, max_chunks(total, num_seqs)).bytes;
 }
 
-template <int O_DT>
+template <int O_DT, bool FUSED>
 static hipError_t launch_o(const PrefillArgs& a, hipStream_t st) {
   if (a.num_seqs == 0) return hipSuccess;
   const int64_t maxch = max_chunks(a.total, a.num_seqs);
@@ -878,22 +1048,29 @@ static hipError_t launch_o(const PrefillArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   if (a.total > 0) {
     const int64_t rounds = (a.hv / a.hk + mp::PH - 1) / mp::PH;
-    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)(maxch * a.hk * rounds)), dim3(256 * mp::PH), 0, st, a, maxch);
+    hipLaunchKernelGGL((prep_kernel<FUSED>), dim3((unsigned)(maxch * a.hk * rounds)), dim3(256 * mp::PH), 0, st, a,
+                       maxch);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const size_t smem = sizeof(ScanSmem);
-  auto k = scan_kernel<O_DT>;
+  auto k = scan_kernel<O_DT, FUSED>;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(k, dim3((unsigned)((int64_t)a.num_seqs * a.hv * mp::NB)), dim3(64 * mp::NWAVES), smem, st, a,
                      maxch);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess || !FUSED || !a.conv_hist) return e;
+  // advance the conv history once every read of the old one (prep, scan) is done
+  const ConvArgs h{a.q, a.qk_stride, nullptr, 0, DT_BF16, a.conv_w, a.conv_b, a.cu, a.num_seqs, a.total,
+                   (2 * a.hk + a.hv) * mp::D, a.conv_hist, 0, 0.f};
+  return launch_conv_history(h, st);
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st) {
-  return a.o_dtype == DT_BF16 ? launch_o<DT_BF16>(a, st) : launch_o<DT_F32>(a, st);
+  if (a.conv_w) return a.o_dtype == DT_BF16 ? launch_o<DT_BF16, true>(a, st) : launch_o<DT_F32, true>(a, st);
+  return a.o_dtype == DT_BF16 ? launch_o<DT_BF16, false>(a, st) : launch_o<DT_F32, false>(a, st);
 }
 
 }  // namespace agnes

@@ -141,6 +141,37 @@ int agnes_gdn_prefill_chunked(const void* q, const void* k, const void* v, agnes
                               void* stream);
 
 /*
+ * agnes_gdn_prefill_fused — agnes_gdn_conv (prefill mode, L2 on the q and k
+ * heads) followed by agnes_gdn_prefill_chunked, as one call that never stores
+ * the conv output (model card 架构 table, delta-rule row: the kernel-4 causal
+ * conv in front of the recurrence; discosf article, section 二.1: chunked
+ * prefill, chunk 64).  The conv runs inside the prefill kernels; q, k and v
+ * go to the matrix cores as fp16 straight from the fp32 conv result (the
+ * separate calls round them to bf16 in between).
+ *
+ *   x            [total_tokens, C] bf16, C = (2 Hk + Hv) * head_dim channels q (Hk
+ *                heads) | k (Hk heads) | v (Hv heads); row stride x_token_stride
+ *   conv_weight  [C, 4] bf16 contiguous;  conv_bias [C] bf16 or NULL
+ *   conv_state   [num_seqs, C, 3] bf16 contiguous, oldest first, or NULL (zero
+ *                history, final history not written).  In: each sequence's
+ *                history.  Out: the last 3 inputs of each sequence (history
+ *                included for sequences shorter than 3), written after every read
+ *                of the old contents.
+ *   l2norm_eps   the q/k L2 norm divides by sqrt(sum of squares + l2norm_eps)
+ *   the rest     as agnes_gdn_prefill_chunked (same workspace size query with
+ *                in_dtype AGNES_BF16).
+ * Supported: bf16 x (AGNES_ERR_UNSUPPORTED otherwise), head_dim 128, Hv a multiple of Hk.
+ */
+int agnes_gdn_prefill_fused(const void* x, int64_t x_token_stride, agnes_dtype dtype,
+                            const void* conv_weight, const void* conv_bias, void* conv_state,
+                            const float* g, const float* beta, const int32_t* cu_seqlens,
+                            int num_seqs, int64_t total_tokens, int num_k_heads, int num_v_heads,
+                            int head_dim, float scale, float l2norm_eps,
+                            const float* initial_state, float* final_state, void* o,
+                            agnes_dtype o_dtype, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/*
  * agnes_gdn_decode_step — one stepwise decode token for each of `batch`
  * independent sequences (discosf article, section 二.1: stepwise decode path),
  * updating each fp32 state in place with one read and one write:

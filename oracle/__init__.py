@@ -28,11 +28,12 @@ nothing on the pages can settle that.
 from .gdn import recurrence, recurrence_matrix_form, decode_step, key_head_of
 from .conv import causal_conv, l2norm_heads, silu
 from .norm import gated_rmsnorm
-from .layer import prefill_layer, decode_layer_step
+from .layer import prefill_layer, decode_layer_step, prefill_conv_recurrence
 from .inputs import as_f64
 
 __all__ = [
     "recurrence", "recurrence_matrix_form", "decode_step", "key_head_of",
     "causal_conv", "l2norm_heads", "silu", "gated_rmsnorm", "prefill_layer", "decode_layer_step",
+    "prefill_conv_recurrence",
     "as_f64",
 ]

@@ -33,6 +33,20 @@ def _split(u, hk, hv):
     return q, k, v
 
 
+def prefill_conv_recurrence(x, conv_w, cu_seqlens, conv_state, g, beta, initial_state, hk, hv,
+                            conv_bias=None, scale=1.0, l2_eps=1e-6):
+    """conv + SiLU + L2(q, k) -> recurrence over a packed batch, nothing rounded in between.
+
+    x [T, C]; cu_seqlens [N+1]; conv_state [N, C, 3] or None (zeros); initial_state
+    [N, Hv, D, D] or None.  Returns (o [T, Hv, D], final conv state [N, C, 3], final state).
+    """
+    u, cs1 = causal_conv(x, conv_w, cu_seqlens, conv_state, conv_bias, l2_heads=2 * hk, head_dim=D,
+                         eps=l2_eps)
+    q, k, v = _split(u, hk, hv)
+    o, s1 = recurrence(q, k, v, g, beta, cu_seqlens, initial_state, scale)
+    return o, cs1, s1
+
+
 def prefill_layer(x, conv_w, conv_state, g, beta, z, norm_w, state, hk, hv, conv_bias=None,
                   scale=1.0, l2_eps=1e-6, norm_eps=1e-6):
     """One sequence of T tokens: x [T, C]; conv_state [C, 3] or None; state [Hv, D, D] or None.

@@ -181,3 +181,30 @@ def test_decode_fused_checks(lib):
     assert fused(lib, cs=P[0] + 1024) == INV            # conv history overlaps x
     assert fused(lib, y=P[5] + 64) == INV               # y overlaps z
     assert lib.agnes_gdn_last_hip_error() == 0
+
+
+def pfused(lib, **kw):
+    a = dict(x=P[0], xs=10 * 128, dt=BF16, w=P[1], b=None, cs=None, g=P[3], be=P[4], cu=P[5], n=1, T=64, hk=2, hv=6,
+             hd=128, sc=1.0, eps=1e-6, s0=None, s1=P[7], o=P[8], odt=F32, ws=None, wsb=0)
+    a.update(kw)
+    return lib.agnes_gdn_prefill_fused(a["x"], a["xs"], a["dt"], a["w"], a["b"], a["cs"], a["g"], a["be"], a["cu"],
+                                       a["n"], a["T"], a["hk"], a["hv"], a["hd"], a["sc"], a["eps"], a["s0"], a["s1"],
+                                       a["o"], a["odt"], a["ws"], a["wsb"], None)
+
+
+def test_prefill_fused_checks(lib):
+    assert pfused(lib, dt=F32) == UNS                   # the fused path takes bf16 x only
+    assert pfused(lib, hd=64) == UNS
+    assert pfused(lib, hv=5, xs=9 * 128) == UNS         # Hv % Hk
+    assert pfused(lib, w=None) == INV
+    assert pfused(lib, x=None) == INV
+    assert pfused(lib, xs=10 * 128 - 8) == INV          # stride below the channel count
+    assert pfused(lib, x=P[0] + 8) == INV
+    assert pfused(lib, eps=-1.0) == INV
+    assert pfused(lib, o=P[0] + 64) == INV              # o overlaps x
+    assert pfused(lib, cs=P[0] + 128) == INV            # conv history overlaps x
+    assert pfused(lib, n=0) == INV                      # tokens without sequences
+    need = lib.agnes_gdn_prefill_workspace_size(1, 64, 2, 6, 128, BF16)
+    assert pfused(lib) == WS
+    assert pfused(lib, ws=P[9], wsb=need - 1) == WS
+    assert lib.agnes_gdn_last_hip_error() == 0

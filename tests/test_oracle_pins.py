@@ -439,3 +439,29 @@ def test_pin_layer_slots_permute_and_padding_is_inert():
     untouched = [1, 2, 3, 5]
     np.testing.assert_array_equal(cs1[untouched], cs[untouched])
     np.testing.assert_array_equal(st1[untouched], st[untouched])
+
+
+def test_pin_packed_layer_prefill_equals_per_sequence():
+    """The packed conv + recurrence over several sequences (with histories and initial states)
+    equals the single-sequence layer run on each: no history, state or conv tap crosses a
+    sequence boundary, and each sequence's final history and state land in its own slot."""
+    rng = np.random.default_rng(43)
+    Hk, Hv = 1, 2
+    lens = [5, 0, 2, 9]
+    T = sum(lens)
+    x, w, g, beta, z, nw = _layer_inputs(rng, T, Hk, Hv)
+    C = x.shape[1]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    cs = rng.standard_normal((len(lens), C, 3))
+    s0 = rng.standard_normal((len(lens), Hv, 128, 128)) * 0.01
+    o, cs1, s1 = oracle.prefill_conv_recurrence(x, w, cu, cs, g, beta, s0, Hk, Hv)
+    for n in range(len(lens)):
+        a, b = cu[n], cu[n + 1]
+        if b == a:
+            np.testing.assert_array_equal(cs1[n], cs[n])
+            np.testing.assert_array_equal(s1[n], s0[n])
+            continue
+        _, on, csn, sn = oracle.prefill_layer(x[a:b], w, cs[n], g[a:b], beta[a:b], z[a:b], nw, s0[n], Hk, Hv)
+        np.testing.assert_allclose(o[a:b], on, rtol=1e-12, atol=1e-14)
+        np.testing.assert_array_equal(cs1[n], csn)
+        np.testing.assert_allclose(s1[n], sn, rtol=1e-12, atol=1e-14)
