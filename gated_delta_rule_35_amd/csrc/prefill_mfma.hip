@@ -537,6 +537,7 @@ struct ScanSmem {
   float Os[mp::C][mp::DVB + 4];      // output tile staging of the output wave
   ExBuf X[2];                        // by chunk parity
   uint16_t Vr[2][mp::VR_ROWS][mp::DVB];  // fused prologue: raw x rows of the V slice, by chunk parity
+  int ks_done;                       // c + 1 once the chain wave's K S^T of chunk c is done
 };
 static_assert(sizeof(ScanSmem) <= 160 * 1024, "scan LDS");
 
@@ -565,20 +566,24 @@ __device__ __forceinline__ h8 kt_operand(const ScanBuf& B, int kt, int ks, int t
   return cat(lds_tr4(&B.QK.K[32 * ks + trow][16 * kt + tcol]), lds_tr4(&B.QK.K[32 * ks + 16 + trow][16 * kt + tcol]));
 }
 
-// Per-row gates in result layout.  Lane (n, g) of a 16x16 result fragment of tile i holds
-// rows 16i + 4g + e; a lane reads the single gate of row 16(n/4) + 4g + n%4 and the row
-// broadcast of the DPP unit (lane k of each 16-lane row to the whole row) hands lane
-// (n, g) the gate of row 16i + 4g + e from lane 4i + e.
-__device__ __forceinline__ int gate_row(int ln, int lg) { return 16 * (ln >> 2) + 4 * lg + (ln & 3); }
-template <int K>
-__device__ __forceinline__ float rowb(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x150 + K, 0xf, 0xf, false));
+// Bounded wait for an LDS flag that another wave of the workgroup raises.  The flag only
+// orders work in time (every data hand-over goes through a barrier), so it is relaxed, and
+// the bound (never reached when the flag works) keeps a broken one from hanging the GPU.
+__device__ __forceinline__ void wait_flag(const int* f, int target) {
+  for (int i = 0; i < (1 << 20); ++i) {
+    if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return;
+    __builtin_amdgcn_s_sleep(1);
+  }
 }
-__device__ __forceinline__ void row_bcast16(float v, float (&o)[16]) {
-  o[0] = rowb<0>(v); o[1] = rowb<1>(v); o[2] = rowb<2>(v); o[3] = rowb<3>(v);
-  o[4] = rowb<4>(v); o[5] = rowb<5>(v); o[6] = rowb<6>(v); o[7] = rowb<7>(v);
-  o[8] = rowb<8>(v); o[9] = rowb<9>(v); o[10] = rowb<10>(v); o[11] = rowb<11>(v);
-  o[12] = rowb<12>(v); o[13] = rowb<13>(v); o[14] = rowb<14>(v); o[15] = rowb<15>(v);
+
+// Gates of the rows a lane holds in result layout (rows 16i + 4g + e of tile i, e = 0..3):
+// four 16-byte LDS reads of a [64] gate row.
+__device__ __forceinline__ void gate_rows16(const float* gt, int lg, float (&o)[16]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f4 v = *reinterpret_cast<const f4*>(gt + 16 * i + 4 * lg);
+    o[4 * i] = v[0]; o[4 * i + 1] = v[1]; o[4 * i + 2] = v[2]; o[4 * i + 3] = v[3];
+  }
 }
 
 // Raw transposing read of 4 bf16 values (see lds_tr4); widened later by bf16x4_to_f4.
@@ -600,17 +605,15 @@ __device__ __forceinline__ f4 bf16x4_to_f4(uint2 u) {
 // and the results of a product are first used several products later.
 template <bool VF16>
 __device__ __forceinline__ void chain_step(const ScanBuf& B, ExBuf& exU, ExBuf& exS, int lane, int ln, int lg,
-                                           f4 (&sacc)[mp::NVT][8], h8 (&sb)[mp::NVT][4]) {
+                                           f4 (&sacc)[mp::NVT][8], h8 (&sb)[mp::NVT][4], int* ks_done, int c) {
   using namespace mp;
   const RecImage& R = B.R;
   const f4 zero = {0.f, 0.f, 0.f, 0.f};
-  const int gi = gate_row(ln, lg);
   const int trow = 4 * lg + (ln >> 2), tcol = 4 * (ln & 3);
   h8 ka[2][4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) ka[0][rt] = a_perm(&B.QK.K[16 * rt + ln][0], 0, lg);
   const float dec = R.gt[1][C - 1];
-  const float gb = R.gt[0][gi], ge = R.gt[1][gi], gl = R.gt[2][gi];
   f4 kq[NVT][4];
 #pragma unroll
   for (int t = 0; t < NVT; ++t)
@@ -652,13 +655,15 @@ __device__ __forceinline__ void chain_step(const ScanBuf& B, ExBuf& exU, ExBuf& 
       }
     __builtin_amdgcn_sched_barrier(0);
   }
+  // the LDS-heavy start of the chunk is over: let the output wave begin (a timing hint only)
+  if (lane == 0) __hip_atomic_store(ks_done, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   // K^T operands of the first two key tiles, then R' and U for both tiles
   h8 kta[2][2];
   kta[0][0] = kt_operand(B, 0, 0, trow, tcol);
   kta[0][1] = kt_operand(B, 0, 1, trow, tcol);
   float bb[16], gg[16];
-  row_bcast16(gb, bb);
-  row_bcast16(ge, gg);
+  gate_rows16(R.gt[0], lg, bb);
+  gate_rows16(R.gt[1], lg, gg);
   h8 rb[NVT][2];
 #pragma unroll
   for (int t = 0; t < NVT; ++t) {
@@ -685,7 +690,7 @@ __device__ __forceinline__ void chain_step(const ScanBuf& B, ExBuf& exU, ExBuf& 
   kta[1][0] = kt_operand(B, 1, 0, trow, tcol);
   kta[1][1] = kt_operand(B, 1, 1, trow, tcol);
   float ll[16];
-  row_bcast16(gl, ll);
+  gate_rows16(R.gt[2], lg, ll);
   __builtin_amdgcn_sched_barrier(0);
   h8 db[NVT][2];
 #pragma unroll
@@ -738,7 +743,7 @@ __device__ __forceinline__ void chain_step(const ScanBuf& B, ExBuf& exU, ExBuf& 
 // Output wave, part 1 (chunk c in buffer B, both value tiles): Q S^T with the S^T operands the
 // chain wave handed over, and the operands of P and the gates exp(gamma) kept for part 2.
 __device__ __forceinline__ void qs_step(const ScanBuf& B, const ExBuf& exS, int lane, int ln, int lg,
-                                        f4 (&qs)[mp::NVT][4], h8 (&pa)[6], float& ge) {
+                                        f4 (&qs)[mp::NVT][4], h8 (&pa)[6], float (&ge)[16]) {
   using namespace mp;
   const f4 zero = {0.f, 0.f, 0.f, 0.f};
   h8 sb[NVT][4];
@@ -764,7 +769,7 @@ __device__ __forceinline__ void qs_step(const ScanBuf& B, const ExBuf& exS, int 
       for (int i = 0; i < 4; ++i) pa[i] = a_perm(&B.R.P[16 * i + ln][0], 0, lg);
       pa[4] = a_perm(&B.R.P[32 + ln][0], 32, lg);
       pa[5] = a_perm(&B.R.P[48 + ln][0], 32, lg);
-      ge = B.R.gt[1][gate_row(ln, lg)];
+      gate_rows16(B.R.gt[1], lg, ge);
     }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
@@ -780,35 +785,53 @@ __device__ __forceinline__ void qs_step(const ScanBuf& B, const ExBuf& exS, int 
 template <int O_DT>
 __device__ __forceinline__ void o_step(const ExBuf& exU, float (*Os)[mp::DVB + 4], const PrefillArgs& a,
                                        const Geo& G, int c, const f4 (&qs)[mp::NVT][4], const h8 (&pa)[6],
-                                       float ge) {
+                                       const float (&gg)[16]) {
   using namespace mp;
   const int lane = G.lane, ln = G.ln, lg = G.lg;
-  float gg[16];
-  row_bcast16(ge, gg);
+  // All products first, then all stores: each result is used only after every product has
+  // been issued, and the staging reads are unconditional, so nothing waits on one latency at
+  // a time.
+  h8 ub[NVT][2];
 #pragma unroll
   for (int t = 0; t < NVT; ++t) {
-    const h8 ub0 = exU.u[t][0][lane], ub1 = exU.u[t][1][lane];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = qs[t][i][e] * gg[4 * i + e];
-      o = mfma_16x16x32(pa[i], ub0, o);
-      if (i >= 2) o = mfma_16x16x32(pa[i + 2], ub1, o);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Os[16 * i + 4 * lg + e][16 * t + ln] = a.scale * o[e];
-    }
+    ub[t][0] = exU.u[t][0][lane];
+    ub[t][1] = exU.u[t][1][lane];
   }
+  f4 o[NVT][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < NVT; ++t) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[t][i][e] = qs[t][i][e] * gg[4 * i + e];
+      o[t][i] = mfma_16x16x32(pa[i], ub[t][0], o[t][i]);
+    }
+#pragma unroll
+  for (int i = 2; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < NVT; ++t) o[t][i] = mfma_16x16x32(pa[i + 2], ub[t][1], o[t][i]);
+#pragma unroll
+  for (int t = 0; t < NVT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Os[16 * i + 4 * lg + e][16 * t + ln] = a.scale * o[t][i][e];
   // Os is written and read back by this wave only: LDS keeps a wave's accesses in order.
   const int L = G.len(c);
   const int part = lane & 3;
+  f4 x[C / 16][2];
+#pragma unroll
+  for (int rg = 0; rg < C / 16; ++rg) {
+    const int r = 16 * rg + (lane >> 2);
+    x[rg][0] = *reinterpret_cast<const f4*>(&Os[r][8 * part]);
+    x[rg][1] = *reinterpret_cast<const f4*>(&Os[r][8 * part + 4]);
+  }
 #pragma unroll
   for (int rg = 0; rg < C / 16; ++rg) {
     const int r = 16 * rg + (lane >> 2);
     if (r < L) {
-      const f4 x0 = *reinterpret_cast<const f4*>(&Os[r][8 * part]);
-      const f4 x1 = *reinterpret_cast<const f4*>(&Os[r][8 * part + 4]);
-      const float v[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+      const float v[8] = {x[rg][0][0], x[rg][0][1], x[rg][0][2], x[rg][0][3],
+                          x[rg][1][0], x[rg][1][1], x[rg][1][2], x[rg][1][3]};
       store8<O_DT>(a.o, ((G.start + (int64_t)c * C + r) * a.hv + G.h) * (int64_t)D + G.dv0 + 8 * part, v);
     }
   }
@@ -937,6 +960,7 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
   G.qk0 = wl.qk + ((size_t)G.kh * (size_t)maxch + (size_t)off[n]) * QK_BYTES;
   const int ln = G.ln, lg = G.lg, lane = G.lane;
   const int nc = G.nchunks;
+  if (threadIdx.x == 0) sm.ks_done = 0;  // ordered before every use by the prologue barrier
 
   if (G.w == 0) {  // chain wave
     f4 sacc[NVT][8];
@@ -962,7 +986,7 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
     if constexpr (FUSED) lds_barrier();  // (the copy waves' extra prologue step)
     lds_barrier();
     for (int c = 0; c < nc + 1; ++c) {
-      if (c < nc) chain_step<FUSED>(sm.B[c & 1], sm.X[c & 1], sm.X[(c + 1) & 1], lane, ln, lg, sacc, sb);
+      if (c < nc) chain_step<FUSED>(sm.B[c & 1], sm.X[c & 1], sm.X[(c + 1) & 1], lane, ln, lg, sacc, sb, &sm.ks_done, c);
       lds_barrier();
     }
     if (a.s1) {
@@ -978,10 +1002,13 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
   } else if (G.w == 1) {  // output wave
     f4 qs[NVT][4];
     h8 pa[6];
-    float ge = 0.f;
+    float ge[16] = {};
     if constexpr (FUSED) lds_barrier();
     lds_barrier();
     for (int c = 0; c < nc + 1; ++c) {
+      // Start once the chain wave is past K S^T: run beside it, the output wave's LDS reads
+      // slow the chain's operand reads (the serial path) by about a third.
+      if (c < nc) wait_flag(&sm.ks_done, c + 1);
       if (c >= 1) o_step<O_DT>(sm.X[(c - 1) & 1], sm.Os, a, G, c - 1, qs, pa, ge);
       if (c < nc) qs_step(sm.B[c & 1], sm.X[c & 1], lane, ln, lg, qs, pa, ge);
       lds_barrier();
