@@ -291,6 +291,21 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
   const int h = kh * grp + (act ? z : 0);
   unsigned char* rec = base + ws.rec + ((size_t)h * maxch + j) * REC_BYTES;
   PrepSmem::U::Head& hd = sm.u.hd[slot];
+  // The gates of the chunk (one value head per four waves), requested before the row copies.
+  float gv = 0.f, bv = 0.f;
+  if (v == 0 && act) {
+    gv = lane < L ? a.g[(c0 + lane) * a.hv + h] : 0.f;
+    bv = lane < L ? a.beta[(c0 + lane) * a.hv + h] : 0.f;
+  }
+  // Fused prologue: the conv taps and bias of this thread's 8 channels of the conv pass below,
+  // requested first so that their latency overlaps the row copies.
+  uint4 cw[4] = {}, cb = make_uint4(0, 0, 0, 0);
+  if constexpr (FUSED) {
+    const int ch = (((tid >> 4) & 1) ? a.hk + kh : kh) * D + 8 * (tid & 15);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) cw[q4] = load_raw8<DT_BF16>(a.conv_w, (int64_t)ch * 4 + 8 * q4).u[0];
+    if (a.conv_b) cb = load_raw8<DT_BF16>(a.conv_b, ch).u[0];
+  }
 
   if constexpr (FUSED) {
     // ---- raw x rows c0 - 3 .. c0 + 64 of the q and k heads -> LDS (direct copies, 17 x 1 KiB
@@ -327,12 +342,9 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
       __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)dst, 16, 0, 0);
     }
   }
-  // gates: inclusive prefix sum of log-decays; rows >= L get g = beta = 0.  The record's copy
-  // is stored after the barrier so that the wait below covers loads only.
-  float gv = 0.f, bv = 0.f;
+  // gates: inclusive prefix sum of log-decays (loaded at the top); rows >= L get g = beta = 0.
+  // The record's copy is stored after the barrier so that the wait below covers loads only.
   if (v == 0 && act) {
-    gv = lane < L ? a.g[(c0 + lane) * a.hv + h] : 0.f;
-    bv = lane < L ? a.beta[(c0 + lane) * a.hv + h] : 0.f;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const float t = __shfl_up(gv, o, 64);
@@ -350,14 +362,11 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
     const int col = tid & 15, hs = (tid >> 4) & 1, rr = tid >> 5;
     const int Ctot = (2 * a.hk + a.hv) * D;
     const int ch = (hs ? a.hk + kh : kh) * D + 8 * col;
-    uint4 wr[4];  // conv taps of the 8 channels, packed bf16 as stored
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) wr[q4] = load_raw8<DT_BF16>(a.conv_w, (int64_t)ch * 4 + 8 * q4).u[0];
     float bs[8];
-    if (a.conv_b) load8<DT_BF16>(a.conv_b, ch, bs);
-    else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) bs[e] = 0.f;
+    {
+      Raw8<DT_BF16> br;
+      br.u[0] = cb;
+      widen8<DT_BF16>(br, bs);
     }
     const uint16_t (*X)[D] = hs ? sm.u.qk.Xk : sm.u.qk.Xq;
     const uint16_t* hist = static_cast<const uint16_t*>(a.conv_hist);
@@ -379,7 +388,7 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
         }
       }
       float y[8], ss = 0.f;
-      conv4_bf16x8(xr, wr, bs, y);
+      conv4_bf16x8(xr, cw, bs, y);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         y[e] = silu(y[e]);
