@@ -59,8 +59,14 @@ constexpr int D = 128;       // head dim (key and value)
 constexpr int LDQ = D + 8;   // fp16 row stride of staged Q/K rows
 constexpr int LDT = C + 8;   // fp16 row stride of [*, chunk] tiles
 constexpr int NVT = 2;       // 16-wide value tiles per scan workgroup
+// Value tiles per chain wave and per output wave.  One tile per wave (two chain and two output
+// waves) shortens each wave's serial work, but every wave then streams the whole K, Q, X and P
+// tiles from LDS for half the columns; at two tiles per wave the chunk period is the same or
+// shorter.
+constexpr int TPW = 2;
+constexpr int NPAIR = NVT / TPW;  // chain waves (and as many output waves) per scan workgroup
 constexpr int NCP = 6;       // copy waves
-constexpr int NWAVES = 2 + NCP;  // chain wave, output wave, copy waves
+constexpr int NWAVES = 2 * NPAIR + NCP;  // chain waves, output waves, copy waves
 constexpr int DVB = 16 * NVT;
 constexpr int NB = D / DVB;  // scan workgroups per value head
 constexpr int LDV = DVB + 8; // bf16 row stride of the staged V slice
@@ -546,7 +552,7 @@ struct ScanSmem {
   float Os[mp::C][mp::DVB + 4];      // output tile staging of the output wave
   ExBuf X[2];                        // by chunk parity
   uint16_t Vr[2][mp::VR_ROWS][mp::DVB];  // fused prologue: raw x rows of the V slice, by chunk parity
-  int ks_done;                       // c + 1 once the chain wave's K S^T of chunk c is done
+  int ks_done[mp::NPAIR];            // c + 1 once chain wave p's K S^T of chunk c is done
 };
 static_assert(sizeof(ScanSmem) <= 160 * 1024, "scan LDS");
 
@@ -605,16 +611,17 @@ __device__ __forceinline__ f4 bf16x4_to_f4(uint2 u) {
             __uint_as_float(u.y & 0xffff0000u)};
 }
 
-// Chain wave on the chunk in buffer B, for both value tiles at once (every LDS operand feeds
-// one product per tile): K S^T, R' = beta (V - exp(gamma) K S^T), U = X R', and the state
-// update S^T <- exp(gamma_63) S^T + K^T diag(exp(gamma_63 - gamma)) U.  sb holds the fp16
-// B operands of S^T entering the chunk and leaves with those of the next chunk; U goes to exU
-// and the next chunk's S^T operands to exS for the output wave.  76 products of 16x16x32.
+// Chain wave on the chunk in buffer B, for its TPW value tiles t0 .. t0 + TPW - 1 (every LDS
+// operand feeds one product per tile): K S^T, R' = beta (V - exp(gamma) K S^T), U = X R', and
+// the state update S^T <- exp(gamma_63) S^T + K^T diag(exp(gamma_63 - gamma)) U.  sb holds the
+// fp16 B operands of S^T entering the chunk and leaves with those of the next chunk; U goes to
+// exU and the next chunk's S^T operands to exS for the output wave.  38 products of 16x16x32
+// per tile.
 // The wave issues in order, so the code is laid out by hand: operands are read a step ahead,
 // and the results of a product are first used several products later.
 template <bool VF16>
-__device__ __forceinline__ void chain_step(const ScanBuf& B, ExBuf& exU, ExBuf& exS, int lane, int ln, int lg,
-                                           f4 (&sacc)[mp::NVT][8], h8 (&sb)[mp::NVT][4], int* ks_done, int c) {
+__device__ __forceinline__ void chain_step(const ScanBuf& B, ExBuf& exU, ExBuf& exS, int t0, int lane, int ln, int lg,
+                                           f4 (&sacc)[mp::TPW][8], h8 (&sb)[mp::TPW][4], int* ks_done, int c) {
   using namespace mp;
   const RecImage& R = B.R;
   const f4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -623,16 +630,16 @@ __device__ __forceinline__ void chain_step(const ScanBuf& B, ExBuf& exU, ExBuf& 
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) ka[0][rt] = a_perm(&B.QK.K[16 * rt + ln][0], 0, lg);
   const float dec = R.gt[1][C - 1];
-  f4 kq[NVT][4];
+  f4 kq[TPW][4];
 #pragma unroll
-  for (int t = 0; t < NVT; ++t)
+  for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) kq[t][rt] = zero;
   __builtin_amdgcn_sched_barrier(0);
   // K S^T; alongside, the V slices, X operands and the decay of the state (sacc is not an
   // operand until the update: the products use the fp16 copy sb)
   h8 xa[6];
-  uint2 vr[NVT][4];
+  uint2 vr[TPW][4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     if (ks < 3) {
@@ -641,9 +648,9 @@ __device__ __forceinline__ void chain_step(const ScanBuf& B, ExBuf& exU, ExBuf& 
     }
     if (ks == 1) {
 #pragma unroll
-      for (int t = 0; t < NVT; ++t)
+      for (int t = 0; t < TPW; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) vr[t][i] = lds_tr4_raw(&B.Vs[16 * i + 4 * lg + (ln >> 2)][16 * t + 4 * (ln & 3)]);
+        for (int i = 0; i < 4; ++i) vr[t][i] = lds_tr4_raw(&B.Vs[16 * i + 4 * lg + (ln >> 2)][16 * (t0 + t) + 4 * (ln & 3)]);
     }
     if (ks == 2) {
 #pragma unroll
@@ -654,9 +661,9 @@ __device__ __forceinline__ void chain_step(const ScanBuf& B, ExBuf& exU, ExBuf& 
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int t = 0; t < NVT; ++t) kq[t][rt] = mfma_16x16x32(ka[ks & 1][rt], sb[t][ks], kq[t][rt]);
+      for (int t = 0; t < TPW; ++t) kq[t][rt] = mfma_16x16x32(ka[ks & 1][rt], sb[t][ks], kq[t][rt]);
 #pragma unroll
-    for (int t = 0; t < NVT; ++t)
+    for (int t = 0; t < TPW; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         sacc[t][2 * ks][e] *= dec;
@@ -673,9 +680,9 @@ __device__ __forceinline__ void chain_step(const ScanBuf& B, ExBuf& exU, ExBuf& 
   float bb[16], gg[16];
   gate_rows16(R.gt[0], lg, bb);
   gate_rows16(R.gt[1], lg, gg);
-  h8 rb[NVT][2];
+  h8 rb[TPW][2];
 #pragma unroll
-  for (int t = 0; t < NVT; ++t) {
+  for (int t = 0; t < TPW; ++t) {
     f4 rp[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -686,13 +693,13 @@ __device__ __forceinline__ void chain_step(const ScanBuf& B, ExBuf& exU, ExBuf& 
     rb[t][0] = b_pair(rp[0], rp[1]);
     rb[t][1] = b_pair(rp[2], rp[3]);
   }
-  f4 u[NVT][4];
+  f4 u[TPW][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int t = 0; t < NVT; ++t) u[t][i] = mfma_16x16x32(xa[i], rb[t][0], zero);
+    for (int t = 0; t < TPW; ++t) u[t][i] = mfma_16x16x32(xa[i], rb[t][0], zero);
 #pragma unroll
-  for (int t = 0; t < NVT; ++t) {
+  for (int t = 0; t < TPW; ++t) {
     u[t][2] = mfma_16x16x32(xa[4], rb[t][1], u[t][2]);
     u[t][3] = mfma_16x16x32(xa[5], rb[t][1], u[t][3]);
   }
@@ -701,9 +708,9 @@ __device__ __forceinline__ void chain_step(const ScanBuf& B, ExBuf& exU, ExBuf& 
   float ll[16];
   gate_rows16(R.gt[2], lg, ll);
   __builtin_amdgcn_sched_barrier(0);
-  h8 db[NVT][2];
+  h8 db[TPW][2];
 #pragma unroll
-  for (int t = 0; t < NVT; ++t) {
+  for (int t = 0; t < TPW; ++t) {
     f4 ud[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -722,15 +729,15 @@ __device__ __forceinline__ void chain_step(const ScanBuf& B, ExBuf& exU, ExBuf& 
       n1 = kt_operand(B, kt + 2, 1, trow, tcol);
     }
 #pragma unroll
-    for (int t = 0; t < NVT; ++t) {
+    for (int t = 0; t < TPW; ++t) {
       sacc[t][kt] = mfma_16x16x32(kta[kt & 1][0], db[t][0], sacc[t][kt]);
       sacc[t][kt] = mfma_16x16x32(kta[kt & 1][1], db[t][1], sacc[t][kt]);
     }
     if (kt == 1) {
 #pragma unroll
-      for (int t = 0; t < NVT; ++t) {
-        exU.u[t][0][lane] = b_pair(u[t][0], u[t][1]);
-        exU.u[t][1][lane] = b_pair(u[t][2], u[t][3]);
+      for (int t = 0; t < TPW; ++t) {
+        exU.u[t0 + t][0][lane] = b_pair(u[t][0], u[t][1]);
+        exU.u[t0 + t][1][lane] = b_pair(u[t][2], u[t][3]);
       }
     }
     if (kt < 6) {
@@ -743,28 +750,29 @@ __device__ __forceinline__ void chain_step(const ScanBuf& B, ExBuf& exU, ExBuf& 
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int t = 0; t < NVT; ++t) {
+    for (int t = 0; t < TPW; ++t) {
       sb[t][ks] = b_pair(sacc[t][2 * ks], sacc[t][2 * ks + 1]);
-      exS.s[t][ks][lane] = sb[t][ks];
+      exS.s[t0 + t][ks][lane] = sb[t][ks];
     }
 }
 
-// Output wave, part 1 (chunk c in buffer B, both value tiles): Q S^T with the S^T operands the
-// chain wave handed over, and the operands of P and the gates exp(gamma) kept for part 2.
-__device__ __forceinline__ void qs_step(const ScanBuf& B, const ExBuf& exS, int lane, int ln, int lg,
-                                        f4 (&qs)[mp::NVT][4], h8 (&pa)[6], float (&ge)[16]) {
+// Output wave, part 1 (chunk c in buffer B, value tiles t0 .. t0 + TPW - 1): Q S^T with the S^T
+// operands the chain wave handed over, and the operands of P and the gates exp(gamma) kept for
+// part 2.
+__device__ __forceinline__ void qs_step(const ScanBuf& B, const ExBuf& exS, int t0, int lane, int ln, int lg,
+                                        f4 (&qs)[mp::TPW][4], h8 (&pa)[6], float (&ge)[16]) {
   using namespace mp;
   const f4 zero = {0.f, 0.f, 0.f, 0.f};
-  h8 sb[NVT][4];
+  h8 sb[TPW][4];
 #pragma unroll
-  for (int t = 0; t < NVT; ++t)
+  for (int t = 0; t < TPW; ++t)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) sb[t][ks] = exS.s[t][ks][lane];
+    for (int ks = 0; ks < 4; ++ks) sb[t][ks] = exS.s[t0 + t][ks][lane];
   h8 qa[2][4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) qa[0][rt] = a_perm(&B.QK.Q[16 * rt + ln][0], 0, lg);
 #pragma unroll
-  for (int t = 0; t < NVT; ++t)
+  for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt) qs[t][rt] = zero;
   __builtin_amdgcn_sched_barrier(0);
@@ -783,34 +791,34 @@ __device__ __forceinline__ void qs_step(const ScanBuf& B, const ExBuf& exS, int 
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int t = 0; t < NVT; ++t) qs[t][rt] = mfma_16x16x32(qa[ks & 1][rt], sb[t][ks], qs[t][rt]);
+      for (int t = 0; t < TPW; ++t) qs[t][rt] = mfma_16x16x32(qa[ks & 1][rt], sb[t][ks], qs[t][rt]);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // Output wave, part 2 (the chunk c of part 1, one iteration later): O = diag(exp gamma) Q S^T
-// + P U for both tiles, staged in Os by this wave and written out from there (rows < L, four
-// lanes per row, eight values each).
+// + P U for its tiles, staged in their columns of Os by this wave and written out from there
+// (rows < L, 2 TPW lanes per row, eight values each).
 template <int O_DT>
 __device__ __forceinline__ void o_step(const ExBuf& exU, float (*Os)[mp::DVB + 4], const PrefillArgs& a,
-                                       const Geo& G, int c, const f4 (&qs)[mp::NVT][4], const h8 (&pa)[6],
+                                       const Geo& G, int c, int t0, const f4 (&qs)[mp::TPW][4], const h8 (&pa)[6],
                                        const float (&gg)[16]) {
   using namespace mp;
   const int lane = G.lane, ln = G.ln, lg = G.lg;
   // All products first, then all stores: each result is used only after every product has
   // been issued, and the staging reads are unconditional, so nothing waits on one latency at
   // a time.
-  h8 ub[NVT][2];
+  h8 ub[TPW][2];
 #pragma unroll
-  for (int t = 0; t < NVT; ++t) {
-    ub[t][0] = exU.u[t][0][lane];
-    ub[t][1] = exU.u[t][1][lane];
+  for (int t = 0; t < TPW; ++t) {
+    ub[t][0] = exU.u[t0 + t][0][lane];
+    ub[t][1] = exU.u[t0 + t][1][lane];
   }
-  f4 o[NVT][4];
+  f4 o[TPW][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int t = 0; t < NVT; ++t) {
+    for (int t = 0; t < TPW; ++t) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[t][i][e] = qs[t][i][e] * gg[4 * i + e];
       o[t][i] = mfma_16x16x32(pa[i], ub[t][0], o[t][i]);
@@ -818,30 +826,31 @@ __device__ __forceinline__ void o_step(const ExBuf& exU, float (*Os)[mp::DVB + 4
 #pragma unroll
   for (int i = 2; i < 4; ++i)
 #pragma unroll
-    for (int t = 0; t < NVT; ++t) o[t][i] = mfma_16x16x32(pa[i + 2], ub[t][1], o[t][i]);
+    for (int t = 0; t < TPW; ++t) o[t][i] = mfma_16x16x32(pa[i + 2], ub[t][1], o[t][i]);
 #pragma unroll
-  for (int t = 0; t < NVT; ++t)
+  for (int t = 0; t < TPW; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Os[16 * i + 4 * lg + e][16 * t + ln] = a.scale * o[t][i][e];
+      for (int e = 0; e < 4; ++e) Os[16 * i + 4 * lg + e][16 * (t0 + t) + ln] = a.scale * o[t][i][e];
   // Os is written and read back by this wave only: LDS keeps a wave's accesses in order.
+  constexpr int LPR = 2 * TPW, RPP = 64 / LPR;  // lanes per row, rows per pass
   const int L = G.len(c);
-  const int part = lane & 3;
-  f4 x[C / 16][2];
+  const int part = lane % LPR, col = 16 * t0 + 8 * part;
+  f4 x[C / RPP][2];
 #pragma unroll
-  for (int rg = 0; rg < C / 16; ++rg) {
-    const int r = 16 * rg + (lane >> 2);
-    x[rg][0] = *reinterpret_cast<const f4*>(&Os[r][8 * part]);
-    x[rg][1] = *reinterpret_cast<const f4*>(&Os[r][8 * part + 4]);
+  for (int rg = 0; rg < C / RPP; ++rg) {
+    const int r = RPP * rg + lane / LPR;
+    x[rg][0] = *reinterpret_cast<const f4*>(&Os[r][col]);
+    x[rg][1] = *reinterpret_cast<const f4*>(&Os[r][col + 4]);
   }
 #pragma unroll
-  for (int rg = 0; rg < C / 16; ++rg) {
-    const int r = 16 * rg + (lane >> 2);
+  for (int rg = 0; rg < C / RPP; ++rg) {
+    const int r = RPP * rg + lane / LPR;
     if (r < L) {
       const float v[8] = {x[rg][0][0], x[rg][0][1], x[rg][0][2], x[rg][0][3],
                           x[rg][1][0], x[rg][1][1], x[rg][1][2], x[rg][1][3]};
-      store8<O_DT>(a.o, ((G.start + (int64_t)c * C + r) * a.hv + G.h) * (int64_t)D + G.dv0 + 8 * part, v);
+      store8<O_DT>(a.o, ((G.start + (int64_t)c * C + r) * a.hv + G.h) * (int64_t)D + G.dv0 + col, v);
     }
   }
 }
@@ -856,6 +865,12 @@ __device__ __forceinline__ void o_step(const ExBuf& exU, float (*Os)[mp::DVB + 4
 // chunk's 64 rows after a 3-row halo (x rows c0 - 3 .. c0 + 76); rows outside the sequence
 // re-read row c0 (the halo before the sequence start comes from the conv history instead).
 // Each wave issues at most about one direct copy per 100 cycles, hence several.
+// First copy index u >= base with u = q (mod NCP).
+__device__ __forceinline__ int first_copy(int base, int q) {
+  const int r = (q - base) % mp::NCP;
+  return base + (r < 0 ? r + mp::NCP : r);
+}
+
 template <bool FUSED>
 __device__ __forceinline__ void issue_chunk(ScanSmem& sm, const PrefillArgs& a, const Geo& G,
                                             const unsigned char* ws, int c, int cv, int q) {
@@ -863,36 +878,40 @@ __device__ __forceinline__ void issue_chunk(ScanSmem& sm, const PrefillArgs& a, 
   constexpr int NQK = QK_BYTES / 1024, NREC = REC_BYTES / 1024, NV = C * (LDV / 8) / 64;
   static_assert(sizeof(ScanBuf) == (NQK + NREC + NV) * 1024, "chunk buffer is a whole number of copies");
   static_assert(VR_ROWS * DVB * 2 == NV * 1024, "raw V rows take as many copies as the V slice");
+  // q is wave-uniform (a scalar): every loop below runs on scalar counters, and a copy costs
+  // an address add, an m0 add and the load.
   const int lane = G.lane;
-  const int cq = c < 0 ? 0 : c;
-  const unsigned char* qk = ws + G.qk0 + (size_t)cq * QK_BYTES + 16 * lane;
-  const unsigned char* rec = ws + G.rec0 + (size_t)cq * REC_BYTES + 16 * lane;
   const uint16_t* vb = static_cast<const uint16_t*>(a.v) + (int64_t)G.h * D + G.dv0;
-  unsigned char* dst = reinterpret_cast<unsigned char*>(&sm.B[cq & 1]);
-#pragma unroll
-  for (int k = 0; k < (NQK + NREC + NV + NCP - 1) / NCP; ++k) {
-    const int u = q + NCP * k;
-    if (u >= NQK + NREC + NV) break;
-    if (u < NQK + NREC) {
-      if (c < 0) continue;
-      const void* src = u < NQK ? (const void*)(qk + 1024 * u) : (const void*)(rec + 1024 * (u - NQK));
-      __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(dst + 1024 * u), 16, 0, 0);
-    } else if constexpr (FUSED) {
-      if (cv < 0) continue;
-      const int64_t c0 = G.start + (int64_t)cv * C;
-      const int jv = 64 * (u - NQK - NREC) + lane, i = jv >> 2, pc = jv & 3;
-      const int64_t pos = c0 - 3 + i;
-      const bool in = pos >= G.start && i < 3 + G.len(cv);
-      const uint16_t* src = vb + (in ? pos : c0) * a.v_stride + 8 * pc;
-      __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(&sm.Vr[cv & 1][0][0] + 8 * jv), 16, 0, 0);
-    } else {
-      if (c < 0) continue;
+  if (c >= 0) {
+    unsigned char* dst = reinterpret_cast<unsigned char*>(&sm.B[c & 1]);
+    const unsigned char* qk = ws + G.qk0 + (size_t)c * QK_BYTES + 16 * lane;
+    for (int u = q; u < NQK; u += NCP)
+      __builtin_amdgcn_global_load_lds((glb_void*)(qk + 1024 * u), (lds_void*)(dst + 1024 * u), 16, 0, 0);
+    const unsigned char* rec = ws + G.rec0 + (size_t)c * REC_BYTES + 16 * lane - 1024 * NQK;
+    for (int u = first_copy(NQK, q); u < NQK + NREC; u += NCP)
+      __builtin_amdgcn_global_load_lds((glb_void*)(rec + 1024 * u), (lds_void*)(dst + 1024 * u), 16, 0, 0);
+    if constexpr (!FUSED) {
       constexpr int VPR = LDV / 8;  // 16-byte pieces per padded V row (5)
       const int L = G.len(c);
-      const int j = 64 * (u - NQK - NREC) + lane, r = j / VPR, pc = j % VPR;
-      const uint16_t* src = vb + (G.start + (int64_t)c * C) * a.v_stride +
-                            ((r < L && pc < DVB / 8) ? (int64_t)r * a.v_stride + 8 * pc : 0);
-      __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(dst + 1024 * u), 16, 0, 0);
+      for (int u = first_copy(NQK + NREC, q); u < NQK + NREC + NV; u += NCP) {
+        const int j = 64 * (u - NQK - NREC) + lane, r = j / VPR, pc = j % VPR;
+        const uint16_t* src = vb + (G.start + (int64_t)c * C) * a.v_stride +
+                              ((r < L && pc < DVB / 8) ? (int64_t)r * a.v_stride + 8 * pc : 0);
+        __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(dst + 1024 * u), 16, 0, 0);
+      }
+    }
+  }
+  if constexpr (FUSED) {
+    if (cv >= 0) {
+      const int64_t c0 = G.start + (int64_t)cv * C;
+      for (int u = first_copy(NQK + NREC, q); u < NQK + NREC + NV; u += NCP) {
+        const int jv = 64 * (u - NQK - NREC) + lane, i = jv >> 2, pc = jv & 3;
+        const int64_t pos = c0 - 3 + i;
+        const bool in = pos >= G.start && i < 3 + G.len(cv);
+        const uint16_t* src = vb + (in ? pos : c0) * a.v_stride + 8 * pc;
+        __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(&sm.Vr[cv & 1][0][0] + 512 * (u - NQK - NREC)), 16,
+                                         0, 0);
+      }
     }
   }
 }
@@ -932,10 +951,10 @@ __device__ __forceinline__ void conv_vslice(ScanSmem& sm, const PrefillArgs& a, 
   *reinterpret_cast<h8*>(&sm.B[cc & 1].Vs[r][8 * cg]) = o;
 }
 
-// Waves: 0 chain wave, 1 output wave (both for all NVT value tiles), then NCP copy waves.
-// Iteration c (one LDS barrier each, n + 1 in all): the chain wave on chunk c; the output wave
-// finishes and writes out chunk c-1 and starts chunk c; the copy waves fill the other buffer
-// with chunk c+1.
+// Waves: NPAIR chain waves, NPAIR output waves (pair p for value tiles TPW p .. TPW p + TPW - 1),
+// then NCP copy waves.  Iteration c (one LDS barrier each, n + 1 in all): the chain waves on
+// chunk c; the output waves finish and write out chunk c-1 and start chunk c; the copy waves
+// fill the other buffer with chunk c+1.
 template <int O_DT, bool FUSED>
 __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, int64_t maxch) {
   using namespace mp;
@@ -969,19 +988,20 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
   G.qk0 = wl.qk + ((size_t)G.kh * (size_t)maxch + (size_t)off[n]) * QK_BYTES;
   const int ln = G.ln, lg = G.lg, lane = G.lane;
   const int nc = G.nchunks;
-  if (threadIdx.x == 0) sm.ks_done = 0;  // ordered before every use by the prologue barrier
+  if (threadIdx.x < NPAIR) sm.ks_done[threadIdx.x] = 0;  // ordered before every use by the prologue barrier
 
-  if (G.w == 0) {  // chain wave
-    f4 sacc[NVT][8];
-    h8 sb[NVT][4];
+  if (G.w < NPAIR) {  // chain wave
+    const int pr = NPAIR == 1 ? 0 : G.w, t0 = TPW * pr;
+    f4 sacc[TPW][8];
+    h8 sb[TPW][4];
 #pragma unroll
-    for (int t = 0; t < NVT; ++t) {
+    for (int t = 0; t < TPW; ++t) {
 #pragma unroll
       for (int kt = 0; kt < 8; ++kt) {
         f4 v = {0.f, 0.f, 0.f, 0.f};
         if (a.s0) {
           const float4 x =
-              *reinterpret_cast<const float4*>(a.s0 + G.sbase + (int64_t)(G.dv0 + 16 * t + ln) * D + 16 * kt + 4 * lg);
+              *reinterpret_cast<const float4*>(a.s0 + G.sbase + (int64_t)(G.dv0 + 16 * (t0 + t) + ln) * D + 16 * kt + 4 * lg);
           v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
         }
         sacc[t][kt] = v;
@@ -989,27 +1009,29 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         sb[t][ks] = b_pair(sacc[t][2 * ks], sacc[t][2 * ks + 1]);
-        sm.X[0].s[t][ks][lane] = sb[t][ks];
+        sm.X[0].s[t0 + t][ks][lane] = sb[t][ks];
       }
     }
     if constexpr (FUSED) lds_barrier();  // (the copy waves' extra prologue step)
     lds_barrier();
     for (int c = 0; c < nc + 1; ++c) {
-      if (c < nc) chain_step<FUSED>(sm.B[c & 1], sm.X[c & 1], sm.X[(c + 1) & 1], lane, ln, lg, sacc, sb, &sm.ks_done, c);
+      if (c < nc)
+        chain_step<FUSED>(sm.B[c & 1], sm.X[c & 1], sm.X[(c + 1) & 1], t0, lane, ln, lg, sacc, sb, &sm.ks_done[pr], c);
       lds_barrier();
     }
     if (a.s1) {
 #pragma unroll
-      for (int t = 0; t < NVT; ++t)
+      for (int t = 0; t < TPW; ++t)
 #pragma unroll
         for (int kt = 0; kt < 8; ++kt) {
           const f4 v = sacc[t][kt];
-          *reinterpret_cast<float4*>(a.s1 + G.sbase + (int64_t)(G.dv0 + 16 * t + ln) * D + 16 * kt + 4 * lg) =
+          *reinterpret_cast<float4*>(a.s1 + G.sbase + (int64_t)(G.dv0 + 16 * (t0 + t) + ln) * D + 16 * kt + 4 * lg) =
               make_float4(v[0], v[1], v[2], v[3]);
         }
     }
-  } else if (G.w == 1) {  // output wave
-    f4 qs[NVT][4];
+  } else if (G.w < 2 * NPAIR) {  // output wave
+    const int pr = NPAIR == 1 ? 0 : G.w - NPAIR, t0 = TPW * pr;
+    f4 qs[TPW][4];
     h8 pa[6];
     float ge[16] = {};
     if constexpr (FUSED) lds_barrier();
@@ -1017,13 +1039,13 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
     for (int c = 0; c < nc + 1; ++c) {
       // Start once the chain wave is past K S^T: run beside it, the output wave's LDS reads
       // slow the chain's operand reads (the serial path) by about a third.
-      if (c < nc) wait_flag(&sm.ks_done, c + 1);
-      if (c >= 1) o_step<O_DT>(sm.X[(c - 1) & 1], sm.Os, a, G, c - 1, qs, pa, ge);
-      if (c < nc) qs_step(sm.B[c & 1], sm.X[c & 1], lane, ln, lg, qs, pa, ge);
+      if (c < nc) wait_flag(&sm.ks_done[pr], c + 1);
+      if (c >= 1) o_step<O_DT>(sm.X[(c - 1) & 1], sm.Os, a, G, c - 1, t0, qs, pa, ge);
+      if (c < nc) qs_step(sm.B[c & 1], sm.X[c & 1], t0, lane, ln, lg, qs, pa, ge);
       lds_barrier();
     }
   } else {  // copy wave
-    const int q = G.w - 2;
+    const int q = __builtin_amdgcn_readfirstlane(G.w - 2 * NPAIR);  // wave-uniform: scalar copy loop
     if constexpr (FUSED) {
       // Step c: copies of chunk c+1 and raw rows of chunk c+2 in flight while the raw rows of
       // chunk c+1 (landed during step c-1) are convolved into its V slice.
