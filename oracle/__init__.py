@@ -18,6 +18,10 @@ delta rule of Yang, Kautz & Hatamizadeh, "Gated Delta Networks: Improving
 Mamba2 with Delta Rule" (ICLR 2025), equation of the gated delta rule:
     S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,  o_t = S_t q_t.
 
+The global attention layer of the same model (24 query / 4 KV heads of dimension 256, RMS-norm
+on q and k, partial three-axis rotary, sigmoid output gate; same model card, rows 全局注意力 and
+位置编码) is in attention.py.
+
 Every routine works in fp64 on exactly upcast inputs.  Pins that tie each
 function to something other than itself live in tests/test_oracle_pins.py;
 the readings of points the pages leave open are listed at the top of each
@@ -30,10 +34,16 @@ from .conv import causal_conv, l2norm_heads, silu
 from .norm import gated_rmsnorm
 from .layer import prefill_layer, decode_layer_step, prefill_conv_recurrence
 from .inputs import as_f64
+from .attention import (
+    rms_norm_heads, rope_inv_freq, rope_angles, apply_rotary, text_positions, qk_prep,
+    causal_attention, attention_prefill, attention_decode,
+)
 
 __all__ = [
     "recurrence", "recurrence_matrix_form", "decode_step", "key_head_of",
     "causal_conv", "l2norm_heads", "silu", "gated_rmsnorm", "prefill_layer", "decode_layer_step",
     "prefill_conv_recurrence",
     "as_f64",
+    "rms_norm_heads", "rope_inv_freq", "rope_angles", "apply_rotary", "text_positions", "qk_prep",
+    "causal_attention", "attention_prefill", "attention_decode",
 ]

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the gated delta-rule layer.
+"""Seeded synthetic inputs for the gated delta-rule layer and the global attention layer.
 
 This module is shared by the HIP path's tests/benchmark and by the fp64 oracle:
 both receive exactly the bytes generated here.  It holds no arithmetic of the
@@ -12,8 +12,10 @@ from .configs import (
     LAYER, make_config, decode_step_inputs, varlen_lengths, unit_vectors,
     gate_draws,
 )
+from .attention import ATTN, attn_prefill_inputs, attn_decode_inputs
 
 __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "LAYER", "make_config",
     "decode_step_inputs", "varlen_lengths", "unit_vectors", "gate_draws",
+    "ATTN", "attn_prefill_inputs", "attn_decode_inputs",
 ]
