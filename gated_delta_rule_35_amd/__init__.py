@@ -13,13 +13,15 @@ discosf article "Agnes 3.0 Flash 刚上线就刷屏…", section 二.1):
   decode_step     stepwise gated delta rule, state updated in place
   gated_rmsnorm   y = rmsnorm(o) * w * silu(z)
   decode_fused    one decode token through conv, recurrence and norm in one launch
+The global attention layer of the same model (model card, rows 全局注意力 and 位置编码):
+  attn_prefill    q/k RMS-norm + partial three-axis rotary, causal GQA softmax attention, sigmoid gate
 """
 import torch
 
 from . import _lib
 
 __all__ = ["conv", "prefill_chunked", "prefill_fused", "decode_step", "gated_rmsnorm", "decode_fused",
-           "prefill_workspace_size",
+           "prefill_workspace_size", "attn_prefill", "attn_prefill_workspace_size",
            "AgnesError", "version", "LIB_PATH"]
 
 LIB_PATH = _lib.LIB_PATH
@@ -65,15 +67,15 @@ def _rows(t, name, width):
     return t.stride(0) if t.numel() > 0 else width
 
 
-def _heads(t, name, heads):
-    """Token stride of a [T, heads, 128] view with contiguous heads."""
-    if t.dim() != 3 or t.shape[1] != heads or t.shape[2] != HEAD_DIM:
-        raise ValueError(f"{name}: expected [T, {heads}, {HEAD_DIM}], got {tuple(t.shape)}")
+def _heads(t, name, heads, dim=HEAD_DIM):
+    """Token stride of a [T, heads, dim] view with contiguous heads."""
+    if t.dim() != 3 or t.shape[1] != heads or t.shape[2] != dim:
+        raise ValueError(f"{name}: expected [T, {heads}, {dim}], got {tuple(t.shape)}")
     if t.numel() == 0:
-        return heads * HEAD_DIM
-    if t.stride(2) != 1 or (heads > 1 and t.stride(1) != HEAD_DIM):
+        return heads * dim
+    if t.stride(2) != 1 or (heads > 1 and t.stride(1) != dim):
         raise ValueError(f"{name}: heads must be contiguous (strides {t.stride()})")
-    return t.stride(0) if t.shape[0] > 0 else heads * HEAD_DIM
+    return t.stride(0) if t.shape[0] > 0 else heads * dim
 
 
 def version():
@@ -300,3 +302,61 @@ def decode_fused(x, conv_weight, conv_state, g, beta, z, norm_weight, state, *, 
         norm_eps, _ptr(y), _ptr(o), _dt(y), _stream(x.device))
     _check("agnes_gdn_decode_fused", st)
     return y
+
+
+ATTN_HEAD_DIM = 256
+ATTN_ROT_DIM = 64
+
+
+def attn_prefill_workspace_size(num_seqs, total_tokens):
+    return int(_lib.load().agnes_attn_prefill_workspace_size(num_seqs, total_tokens))
+
+
+def attn_prefill(q, k, v, gate, q_norm_weight, k_norm_weight, cu_seqlens, *, positions=None, k_out=None,
+                 v_out=None, rope_base=1e7, norm_eps=1e-6, scale=0.0, o=None, o_dtype=None, workspace=None):
+    """Global attention layer over a packed batch (prefill).
+
+    q, gate: bf16 [T, Hq, 256]; k, v: bf16 [T, Hkv, 256] (token strides free, heads contiguous);
+    norm weights: bf16 [256]; cu_seqlens: int32 [N+1] (device); positions: int32 [3, T] or None
+    (text positions).  k_out: bf16 [T, Hkv, 256] view receiving the normalised, rotated k (the KV
+    cache rows; allocated when None); v_out: optional copy of v.  scale <= 0 selects 1/16.
+    Returns (o [T, Hq, 256], k_out).
+    """
+    T, Hq, _ = q.shape
+    Hkv = k.shape[1]
+    strides = {}
+    for t, name, h in ((q, "q", Hq), (gate, "gate", Hq), (k, "k", Hkv), (v, "v", Hkv)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+        strides[name] = _heads(t, name, h, ATTN_HEAD_DIM)
+    for t, name in ((q_norm_weight, "q_norm_weight"), (k_norm_weight, "k_norm_weight")):
+        if t.dtype != torch.bfloat16 or t.numel() != ATTN_HEAD_DIM or not t.is_contiguous():
+            raise ValueError(f"{name}: expected contiguous bf16 [256]")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    n = cu_seqlens.numel() - 1
+    ps = 0
+    if positions is not None:
+        if positions.dtype != torch.int32 or positions.dim() != 2 or positions.shape[0] != 3 \
+                or positions.shape[1] != T or positions.stride(1) != 1:
+            raise ValueError("positions: expected int32 [3, T] with unit inner stride")
+        ps = positions.stride(0)
+    if k_out is None:
+        k_out = torch.empty((T, Hkv, ATTN_HEAD_DIM), dtype=torch.bfloat16, device=q.device)
+    kos = _heads(k_out, "k_out", Hkv, ATTN_HEAD_DIM)
+    vos = 0 if v_out is None else _heads(v_out, "v_out", Hkv, ATTN_HEAD_DIM)
+    if o is None:
+        o = torch.empty((T, Hq, ATTN_HEAD_DIM), dtype=o_dtype or torch.bfloat16, device=q.device)
+    elif not o.is_contiguous():
+        raise ValueError("o must be contiguous")
+    need = attn_prefill_workspace_size(n, T)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = _lib.load().agnes_attn_prefill(
+        _ptr(q), strides["q"], _ptr(k), strides["k"], _ptr(v), strides["v"], _ptr(gate), strides["gate"],
+        _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(positions), ps, _ptr(cu_seqlens), n, T, Hq, Hkv,
+        ATTN_HEAD_DIM, ATTN_ROT_DIM, rope_base, norm_eps, scale, _ptr(k_out), kos, _ptr(v_out), vos,
+        _ptr(o), _dt(o), _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(q.device))
+    _check("agnes_attn_prefill", st)
+    return o, k_out

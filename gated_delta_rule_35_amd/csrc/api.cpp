@@ -43,7 +43,7 @@ AGNES_API const char* agnes_gdn_status_string(int status) {
   switch (status) {
     case AGNES_OK: return "AGNES_OK";
     case AGNES_ERR_INVALID_ARG: return "AGNES_ERR_INVALID_ARG: invalid argument (pointer, size, stride or overlap)";
-    case AGNES_ERR_UNSUPPORTED: return "AGNES_ERR_UNSUPPORTED: outside the supported set (head_dim 128, kernel 4, Hv % Hk == 0)";
+    case AGNES_ERR_UNSUPPORTED: return "AGNES_ERR_UNSUPPORTED: outside the supported set of the call (head dims, kernel size, head ratio)";
     case AGNES_ERR_WORKSPACE: return "AGNES_ERR_WORKSPACE: workspace missing or too small";
     case AGNES_ERR_HIP: return "AGNES_ERR_HIP: a HIP launch failed";
     default: return "unknown agnes_status";
@@ -280,4 +280,67 @@ AGNES_API int agnes_gdn_decode_fused(const void* x, int64_t x_token_stride, agne
                            norm_weight, state, slots, num_slots, batch, num_k_heads, num_v_heads, scale,
                            l2norm_eps, norm_eps, y, o, (int)o_dtype};
   return hip_status(agnes::launch_decode_fused(a, static_cast<hipStream_t>(stream)));
+}
+
+AGNES_API size_t agnes_attn_prefill_workspace_size(int num_seqs, int64_t total_tokens) {
+  if (num_seqs < 0 || total_tokens < 0) return 0;
+  return agnes::attn_prefill_workspace(num_seqs, total_tokens);
+}
+
+AGNES_API int agnes_attn_prefill(const void* q, int64_t q_token_stride, const void* k, int64_t k_token_stride,
+                                 const void* v, int64_t v_token_stride, const void* gate, int64_t gate_token_stride,
+                                 const void* q_norm_weight, const void* k_norm_weight, const int32_t* positions,
+                                 int64_t positions_stride, const int32_t* cu_seqlens, int num_seqs,
+                                 int64_t total_tokens, int num_q_heads, int num_kv_heads, int head_dim, int rot_dim,
+                                 float rope_base, float norm_eps, float scale, void* k_out,
+                                 int64_t k_out_token_stride, void* v_out, int64_t v_out_token_stride, void* o,
+                                 agnes_dtype o_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  constexpr int kAttnDim = 256;
+  if (!valid_dtype(o_dtype)) return AGNES_ERR_INVALID_ARG;
+  if (num_seqs < 0 || total_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0) return AGNES_ERR_INVALID_ARG;
+  if (head_dim != kAttnDim || rot_dim != 64 || num_q_heads % num_kv_heads) return AGNES_ERR_UNSUPPORTED;
+  if (num_seqs == 0 && total_tokens != 0) return AGNES_ERR_INVALID_ARG;
+  if (num_seqs > 0 && !cu_seqlens) return AGNES_ERR_INVALID_ARG;
+  if (total_tokens > 0 && (!q || !k || !v || !gate || !q_norm_weight || !k_norm_weight || !k_out || !o))
+    return AGNES_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(gate, 16) || !aligned(k_out, 16) ||
+      !aligned(v_out, 16) || !aligned(o, 16) || !aligned(q_norm_weight, 8) || !aligned(k_norm_weight, 8) ||
+      !aligned(positions, 4) || !aligned(cu_seqlens, 4))
+    return AGNES_ERR_INVALID_ARG;
+  const int64_t qw = (int64_t)num_q_heads * head_dim, kw = (int64_t)num_kv_heads * head_dim;
+  if (q_token_stride < qw || gate_token_stride < qw || k_token_stride < kw || v_token_stride < kw ||
+      k_out_token_stride < kw || (v_out && v_out_token_stride < kw) || q_token_stride % 8 || gate_token_stride % 8 ||
+      k_token_stride % 8 || v_token_stride % 8 || k_out_token_stride % 8 || (v_out && v_out_token_stride % 8))
+    return AGNES_ERR_INVALID_ARG;
+  if (positions && positions_stride < total_tokens) return AGNES_ERR_INVALID_ARG;
+  if (!std::isfinite(rope_base) || rope_base <= 0.f || !std::isfinite(norm_eps) || norm_eps < 0.f ||
+      !std::isfinite(scale))
+    return AGNES_ERR_INVALID_ARG;
+  if (((total_tokens + 127) / 128 + num_seqs) * (int64_t)num_q_heads >= INT32_MAX) return AGNES_ERR_UNSUPPORTED;
+  const Span os = span(o, total_tokens, qw, qw, esize(o_dtype));
+  const Span ks = span(k_out, total_tokens, k_out_token_stride, kw, 2);
+  const Span vs = span(v_out, total_tokens, v_out_token_stride, kw, 2);
+  const Span ins[4] = {span(q, total_tokens, q_token_stride, qw, 2), span(k, total_tokens, k_token_stride, kw, 2),
+                       span(v, total_tokens, v_token_stride, kw, 2),
+                       span(gate, total_tokens, gate_token_stride, qw, 2)};
+  for (const Span& in : ins)
+    if (overlap(os, in) || overlap(ks, in) || overlap(vs, in)) return AGNES_ERR_INVALID_ARG;
+  if (overlap(os, ks) || overlap(os, vs) || overlap(ks, vs)) return AGNES_ERR_INVALID_ARG;
+  const size_t need = agnes::attn_prefill_workspace(num_seqs, total_tokens);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return AGNES_ERR_WORKSPACE;
+
+  agnes::AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.gate = gate;
+  a.q_stride = q_token_stride; a.k_stride = k_token_stride; a.v_stride = v_token_stride;
+  a.gate_stride = gate_token_stride;
+  a.q_norm_w = q_norm_weight; a.k_norm_w = k_norm_weight;
+  a.pos3 = positions; a.pos3_stride = positions_stride;
+  a.cu = cu_seqlens; a.num_seqs = num_seqs; a.total = total_tokens;
+  a.hq = num_q_heads; a.hkv = num_kv_heads;
+  a.rope_base = rope_base; a.eps = norm_eps; a.scale = scale;
+  a.k_out = k_out; a.k_out_stride = k_out_token_stride;
+  a.v_out = v_out; a.v_out_stride = v_out_token_stride;
+  a.o = o; a.o_dtype = (int)o_dtype;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  return hip_status(agnes::launch_attn_prefill(a, static_cast<hipStream_t>(stream)));
 }

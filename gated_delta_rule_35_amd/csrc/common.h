@@ -108,6 +108,17 @@ __device__ __forceinline__ void store8(void* base, int64_t idx, const float v[8]
   }
 }
 
+// 4 consecutive values (8-byte aligned for bf16, 16 for f32).
+template <int DT>
+__device__ __forceinline__ void store4(void* base, int64_t idx, f4 v) {
+  if constexpr (DT == DT_BF16) {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) =
+        make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+  } else {
+    *reinterpret_cast<float4*>(static_cast<float*>(base) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ float load1(const void* base, int64_t idx) {
   if constexpr (DT == DT_BF16) return bf16_to_f32(static_cast<const uint16_t*>(base)[idx]);

@@ -110,6 +110,45 @@ struct NormArgs {
   int y_dtype;
 };
 
+// Global attention layer (query heads hq, KV heads hkv, head dim 256, rotary on dims 0..63).
+// Prefill: q, gate [T, hq, 256] and k, v [T, hkv, 256] bf16 rows with the given token strides;
+// k_out receives the normalised, rotated k (bf16, token stride k_out_stride) and is what the
+// attention reads; v_out (optional) a copy of v.  Decode: one token per batch entry, caches
+// [batch, max_len, hkv, 256] bf16, cache_lens[b] tokens already cached.
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* gate;
+  int64_t q_stride, k_stride, v_stride, gate_stride;
+  const void* q_norm_w;   // [256] bf16
+  const void* k_norm_w;   // [256] bf16
+  const int32_t* pos3;    // [3][pos3_stride] positions (text, height, width) or nullptr: text
+  int64_t pos3_stride;
+  const int32_t* cu;      // prefill: cu_seqlens [num_seqs + 1]
+  int num_seqs;
+  int64_t total;          // prefill: tokens; decode: batch
+  int hq, hkv;
+  float rope_base, eps, scale;  // scale <= 0: 1/sqrt(256)
+  void* k_out;
+  int64_t k_out_stride;
+  void* v_out;
+  int64_t v_out_stride;
+  void* o;                // [T or batch, hq, 256]
+  int o_dtype;
+  void* workspace;
+  size_t workspace_bytes;
+  size_t off_off, tab_off;  // set by the launcher
+  // decode
+  void* k_cache;
+  void* v_cache;
+  int64_t max_len;
+  const int32_t* cache_lens;
+};
+
+hipError_t launch_attn_prefill(AttnArgs a, hipStream_t s);
+size_t attn_prefill_workspace(int num_seqs, int64_t total);
+
 hipError_t launch_conv(const ConvArgs& a, hipStream_t s);
 hipError_t launch_conv_history(const ConvArgs& a, hipStream_t s);  // final history only
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);

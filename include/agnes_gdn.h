@@ -253,6 +253,56 @@ int agnes_gdn_decode_fused(const void* x, int64_t x_token_stride, agnes_dtype dt
                            void* y, void* o, agnes_dtype o_dtype, void* stream);
 
 /* Human-readable name of an agnes_status value (static string). */
+/*
+ * agnes_attn_prefill_workspace_size — bytes of device workspace agnes_attn_prefill
+ * needs (0 for an empty batch).
+ */
+size_t agnes_attn_prefill_workspace_size(int num_seqs, int64_t total_tokens);
+
+/*
+ * agnes_attn_prefill — the global attention layer over a packed batch (model card
+ * "Agnes-3.0-Flash Preview", 架构 table, rows 全局注意力 and 位置编码; discosf
+ * article, section 二.1): RMS-norm of every q and k head, three-axis rotary on
+ * their first rot_dim dims, causal softmax attention inside each sequence
+ * (query head h reads KV head h / (num_q_heads / num_kv_heads)), and the output
+ * times sigmoid(gate).
+ *
+ *   q, gate        bf16 [total_tokens, num_q_heads, head_dim], row strides
+ *                  q_token_stride, gate_token_stride (elements, multiples of 8)
+ *   k, v           bf16 [total_tokens, num_kv_heads, head_dim], row strides
+ *                  k_token_stride, v_token_stride
+ *   q_norm_weight, k_norm_weight   bf16 [head_dim]: x / sqrt(mean(x^2) + norm_eps) * w
+ *   positions      device int32 [3][positions_stride] (text, height, width) per
+ *                  token, or NULL for text (the index in the sequence on all
+ *                  three axes).  Frequency j < rot_dim/2 turns dims j and
+ *                  j + rot_dim/2 by position(axis j mod 3) * rope_base^(-2j/rot_dim);
+ *                  the angles are formed in fp64.
+ *   cu_seqlens     device int32 [num_seqs + 1], cu[0] = 0, nondecreasing
+ *   scale          softmax scale; <= 0 selects 1/sqrt(head_dim)
+ *   k_out          bf16 [total_tokens, num_kv_heads, head_dim], row stride
+ *                  k_out_token_stride: receives the normalised, rotated k (the KV
+ *                  cache rows); the attention reads it, so it is required
+ *   v_out          optional bf16 copy of v (row stride v_out_token_stride), or NULL
+ *   o              [total_tokens, num_q_heads, head_dim] contiguous, o_dtype
+ *   workspace      >= agnes_attn_prefill_workspace_size() bytes, 256-byte aligned
+ *
+ * Supported: head_dim 256, rot_dim 64, num_q_heads % num_kv_heads == 0.  The
+ * products run on bf16 matrix cores with fp32 accumulation: q after norm and
+ * rotary, k as stored in k_out, v, and the softmax weights are bf16 operands;
+ * the softmax statistics are fp32.  k_out, v_out and o must not overlap any
+ * input or each other.
+ */
+int agnes_attn_prefill(const void* q, int64_t q_token_stride, const void* k, int64_t k_token_stride,
+                       const void* v, int64_t v_token_stride, const void* gate,
+                       int64_t gate_token_stride, const void* q_norm_weight,
+                       const void* k_norm_weight, const int32_t* positions,
+                       int64_t positions_stride, const int32_t* cu_seqlens, int num_seqs,
+                       int64_t total_tokens, int num_q_heads, int num_kv_heads, int head_dim,
+                       int rot_dim, float rope_base, float norm_eps, float scale, void* k_out,
+                       int64_t k_out_token_stride, void* v_out, int64_t v_out_token_stride,
+                       void* o, agnes_dtype o_dtype, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 const char* agnes_gdn_status_string(int status);
 
 /* hipError_t of the last AGNES_ERR_HIP returned on the calling thread (0 if none). */

@@ -36,7 +36,7 @@ from .layer import prefill_layer, decode_layer_step, prefill_conv_recurrence
 from .inputs import as_f64
 from .attention import (
     rms_norm_heads, rope_inv_freq, rope_angles, apply_rotary, text_positions, qk_prep,
-    causal_attention, attention_prefill, attention_decode,
+    causal_attention, causal_attention_rows, attention_prefill, attention_decode,
 )
 
 __all__ = [
@@ -45,5 +45,5 @@ __all__ = [
     "prefill_conv_recurrence",
     "as_f64",
     "rms_norm_heads", "rope_inv_freq", "rope_angles", "apply_rotary", "text_positions", "qk_prep",
-    "causal_attention", "attention_prefill", "attention_decode",
+    "causal_attention", "causal_attention_rows", "attention_prefill", "attention_decode",
 ]

@@ -7,7 +7,7 @@ interleaved, base 1e7, applied to the first 25 % of the head dim, 64 dims); disc
 "Agnes 3.0 Flash 刚上线就刷屏…", section 二.1 (the same specification; only these 18 layers
 keep a KV cache).
 
-The pages give no formula.  Readings (each pinned in tests/test_oracle_pins.py):
+The pages give no formula.  Readings (each pinned in tests/test_oracle_attention_pins.py):
   * inputs are the projections q, gate [T, Hq, 256] and k, v [T, Hkv, 256]; query head h reads
     KV head h // (Hq / Hkv) (contiguous groups);
   * RMS-norm per head over its 256 values, x / sqrt(mean(x^2) + eps) * w, one weight [256] for
@@ -107,6 +107,24 @@ def causal_attention(qr, kr, v, cu_seqlens, scale=None):
             p = np.exp(s)
             p /= p.sum(axis=1, keepdims=True)
             out[a:b, h] = p @ v[a:b, h // grp]
+    return out
+
+
+def causal_attention_rows(qr, kr, v, cu_seqlens, rows, heads, scale=None):
+    """Rows of causal_attention for the listed tokens and query heads only: [len(rows),
+    len(heads), D].  For checks at sizes where the whole output is too costly."""
+    qr, kr, v = as_f64(qr), as_f64(kr), as_f64(v)
+    d = qr.shape[2]
+    grp = qr.shape[1] // kr.shape[1]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    out = np.zeros((len(rows), len(heads), d))
+    for i, t in enumerate(rows):
+        a = int(cu[np.searchsorted(cu, t, side="right") - 1])
+        for j, h in enumerate(heads):
+            s = kr[a:t + 1, h // grp] @ qr[t, h] * scale
+            p = np.exp(s - s.max())
+            out[i, j] = (p / p.sum()) @ v[a:t + 1, h // grp]
     return out
 
 

@@ -30,13 +30,13 @@ def lib():
 
 def header_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(agnes_gdn_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(agnes_\w+)\s*\(", text, re.M)))
 
 
-def test_header_declares_the_four_layer_calls():
+def test_header_declares_the_layer_calls():
     names = header_functions()
     for n in ("agnes_gdn_conv", "agnes_gdn_prefill_chunked", "agnes_gdn_decode_step",
-              "agnes_gdn_gated_rmsnorm"):
+              "agnes_gdn_gated_rmsnorm", "agnes_attn_prefill"):
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
 
@@ -45,7 +45,7 @@ def test_library_exports_exactly_the_header(lib):
     for name in header_functions():
         assert hasattr(lib, name), name
     out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
-    exported = sorted(set(re.findall(r"\b(agnes_gdn_\w+)\b", out)))
+    exported = sorted(set(re.findall(r"\b(agnes_\w+)\b", out)))
     assert exported == header_functions()
 
 
@@ -207,4 +207,44 @@ def test_prefill_fused_checks(lib):
     need = lib.agnes_gdn_prefill_workspace_size(1, 64, 2, 6, 128, BF16)
     assert pfused(lib) == WS
     assert pfused(lib, ws=P[9], wsb=need - 1) == WS
+    assert lib.agnes_gdn_last_hip_error() == 0
+
+
+def attn(lib, **kw):
+    T, hq, hkv = 100, 24, 4
+    a = dict(q=P[0], qs=hq * 256, k=P[1], ks=hkv * 256, v=P[2], vs=hkv * 256, g=P[3], gs=hq * 256, qw=P[4], kw=P[4] + 512,
+             pos=None, ps=0, cu=P[5], n=1, T=T, hq=hq, hkv=hkv, hd=256, rd=64, base=1e7, eps=1e-6, sc=0.0, ko=P[6],
+             kos=hkv * 256, vo=None, vos=0, o=P[7], odt=BF16, ws=None, wsb=0)
+    a.update(kw)
+    return lib.agnes_attn_prefill(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["g"], a["gs"], a["qw"], a["kw"],
+                                  a["pos"], a["ps"], a["cu"], a["n"], a["T"], a["hq"], a["hkv"], a["hd"], a["rd"],
+                                  a["base"], a["eps"], a["sc"], a["ko"], a["kos"], a["vo"], a["vos"], a["o"], a["odt"],
+                                  a["ws"], a["wsb"], None)
+
+
+def test_attn_prefill_checks(lib):
+    assert attn(lib, n=0, T=0, q=None, k=None, v=None, g=None, ko=None, o=None) == 0  # empty batch
+    assert attn(lib, hd=128) == UNS
+    assert attn(lib, rd=32) == UNS
+    assert attn(lib, hq=10) == UNS                      # Hq % Hkv
+    assert attn(lib, ko=None) == INV                    # k_out is what the attention reads
+    assert attn(lib, g=None) == INV
+    assert attn(lib, qw=None) == INV
+    assert attn(lib, qs=24 * 256 - 8) == INV            # stride below the heads
+    assert attn(lib, ks=4 * 256 + 4) == INV             # stride % 8
+    assert attn(lib, q=P[0] + 8) == INV                 # misaligned
+    assert attn(lib, qw=P[4] + 2) == INV
+    assert attn(lib, pos=P[8], ps=99) == INV            # positions stride below T
+    assert attn(lib, base=0.0) == INV
+    assert attn(lib, eps=float("nan")) == INV
+    assert attn(lib, odt=5) == INV
+    assert attn(lib, n=0) == INV                        # tokens without sequences
+    assert attn(lib, o=P[0] + 512) == INV               # o overlaps q
+    assert attn(lib, ko=P[1]) == INV                    # k_out overlaps k
+    assert attn(lib, vo=P[7] + 1024, vos=1024) == INV   # v_out overlaps o
+    need = lib.agnes_attn_prefill_workspace_size(1, 100)
+    assert need > 0
+    assert attn(lib) == WS
+    assert attn(lib, ws=P[9], wsb=need - 1) == WS
+    assert attn(lib, ws=P[9] + 16, wsb=need) == WS      # not 256-byte aligned
     assert lib.agnes_gdn_last_hip_error() == 0

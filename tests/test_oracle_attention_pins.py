@@ -166,3 +166,15 @@ def test_pin_packed_sequences_are_independent():
             on, kn = oracle.attention_prefill(q[a:b], k[a:b], v[a:b], gate[a:b], [0, b - a], w, w)
             np.testing.assert_allclose(o[a:b], on, rtol=1e-13, atol=1e-14)
             np.testing.assert_allclose(kr[a:b], kn, rtol=1e-13, atol=1e-14)
+
+
+def test_pin_row_subset_equals_full_attention():
+    """The per-row routine used for large checks gives the full routine's rows (sequence start
+    found from cu_seqlens, head map, causal prefix)."""
+    rng = np.random.default_rng(15)
+    cu = np.array([0, 5, 5, 12])
+    q, k, v = _rand(rng, 12, 6, D), _rand(rng, 12, 2, D), _rand(rng, 12, 2, D)
+    full = oracle.causal_attention(q, k, v, cu)
+    rows, heads = [0, 4, 5, 6, 11], [0, 2, 3, 5]
+    sub = oracle.causal_attention_rows(q, k, v, cu, rows, heads)
+    np.testing.assert_allclose(sub, full[rows][:, heads], rtol=1e-13, atol=1e-14)
