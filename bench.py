@@ -8,7 +8,8 @@ prefill call (agnes_gdn_prefill_fused), then the norm.  The same chain as three 
 (conv, prefill, norm) is timed beside it.  The same run also times the batched decode step
 (256 sequences, one token each, fp32 states updated in place) and reports its state HBM GB/s,
 and the fused decode step (conv-history update + conv + L2 + recurrence + gated norm in one
-launch) beside the three unfused calls it replaces.
+launch) beside the three unfused calls it replaces, and the prefill of the model's global
+attention layer (24 query / 4 KV heads of 256, T = 8192) with its matrix-core roofline.
 
 Inputs are synthetic (seeded), generated on the host and resident in HBM before timing.
 
@@ -49,6 +50,10 @@ DECODE_BYTES = DECODE_B * HV * D * D * 4 * 2 + DECODE_B * (2 * HK * D * 2 + HV *
 FUSED_DECODE_BYTES = (DECODE_B * HV * D * D * 4 * 2 + DECODE_B * 10240 * 2 + DECODE_B * 10240 * 3 * 2 * 2
                       + 10240 * 4 * 2 + DECODE_B * HV * D * 2 * 2 + DECODE_B * HV * 4 * 2 + D * 2)
 CAL_BYTES = 256 << 20          # device-to-device copy of known size, for the HBM counter scale
+# global attention layer (24 query / 4 KV heads of 256): QK^T and PV over the causal pairs,
+# 2 x 256 multiply-adds each per query head
+ATTN_HQ, ATTN_HKV, ATTN_D = 24, 4, 256
+ATTN_FLOP = ATTN_HQ * 4 * ATTN_D * T * (T + 1) // 2
 
 # HBM traffic per call from the committed counter summary (FETCH_SIZE and WRITE_SIZE runs, each
 # scaled by the same counter on the calibration copy).  A figure is used only while the source
@@ -251,6 +256,31 @@ def main():
     ms_fused = np.mean([e[0].elapsed_time(e[1]) for e in fevs])
     fused_gbs = FUSED_DECODE_BYTES / (ms_fused * 1e-3) / 1e9
 
+    # ---- global attention prefill, T = 8192, one sequence
+    from synth import attn_prefill_inputs
+    ad = attn_prefill_inputs(np.random.default_rng(2001), [T], ATTN_HQ, ATTN_HKV, ATTN_D)
+    aq, ak, av, ag = (to_dev(ad[n], torch) for n in ("q", "k", "v", "gate"))
+    aqw, akw = to_dev(ad["qw"], torch), to_dev(ad["kw"], torch)
+    acu = torch.tensor([0, T], dtype=torch.int32, device="cuda")
+    ako = torch.empty((T, ATTN_HKV, ATTN_D), dtype=torch.bfloat16, device="cuda")
+    ao = torch.empty((T, ATTN_HQ, ATTN_D), dtype=torch.bfloat16, device="cuda")
+    aws = torch.empty(gdn.attn_prefill_workspace_size(1, T), dtype=torch.uint8, device="cuda")
+
+    def astep():
+        gdn.attn_prefill(aq, ak, av, ag, aqw, akw, acu, k_out=ako, o=ao, workspace=aws)
+
+    for _ in range(max(args.warmup, 1)):
+        astep()
+    torch.cuda.synchronize()
+    aevs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        aevs[i][0].record()
+        astep()
+        aevs[i][1].record()
+    torch.cuda.synchronize()
+    ms_attn = np.mean([e[0].elapsed_time(e[1]) for e in aevs])
+    attn_tflops = ATTN_FLOP / (ms_attn * 1e-3) / 1e12
+
     pre_tflops = FLOP_PER_TOKEN * T / (ms_fpre * 1e-3) / 1e12
     res = {
         "metric": METRIC,
@@ -302,6 +332,13 @@ def main():
                                       "frac": round(fused_gbs / HBM_PEAK_GBS, 4),
                                       "traffic": measured_traffic("decode_fused"),
                                       "bytes_per_launch": FUSED_DECODE_BYTES}},
+        "attention_prefill": {"T": T, "num_q_heads": ATTN_HQ, "num_kv_heads": ATTN_HKV, "head_dim": ATTN_D,
+                              "ms": round(ms_attn, 4), "tokens_per_s": round(T / (ms_attn * 1e-3), 1),
+                              "roofline": {"bound": "mfma",
+                                           "kernel": "agnes_attn_prefill call (offsets + k prep + attention launches)",
+                                           "achieved": round(attn_tflops, 2), "peak": MFMA_PEAK_TFLOPS,
+                                           "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_PEAK_TFLOPS, 4),
+                                           "flops_per_launch": ATTN_FLOP, "operands": "bf16"}},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -313,6 +313,10 @@ AGNES_API int agnes_attn_prefill(const void* q, int64_t q_token_stride, const vo
       k_token_stride % 8 || v_token_stride % 8 || k_out_token_stride % 8 || (v_out && v_out_token_stride % 8))
     return AGNES_ERR_INVALID_ARG;
   if (positions && positions_stride < total_tokens) return AGNES_ERR_INVALID_ARG;
+  // 64-row blocks are addressed with 32-bit element offsets
+  if (q_token_stride > (1 << 24) || k_token_stride > (1 << 24) || v_token_stride > (1 << 24) ||
+      k_out_token_stride > (1 << 24))
+    return AGNES_ERR_UNSUPPORTED;
   if (!std::isfinite(rope_base) || rope_base <= 0.f || !std::isfinite(norm_eps) || norm_eps < 0.f ||
       !std::isfinite(scale))
     return AGNES_ERR_INVALID_ARG;

@@ -13,10 +13,14 @@
 //      32 queries.  The q rows arrive by direct global -> LDS copies and are normalised and
 //      rotated in place, scaled by log2(e)/16 and kept as bf16 matrix-core operands.  K and V
 //      blocks of 64 keys are double-buffered in LDS (direct copies, 16-byte chunks of a row
-//      XOR-swizzled by the row's low four bits, so the fragment reads are free of bank
-//      conflicts).  Per block: S^T = K Q^T (each lane then holds scores of one query), an
-//      online softmax in base 2, and O^T += V^T P^T with the V^T fragments from the transposing
-//      LDS read.  The output is divided by the softmax sum, multiplied by sigmoid(gate) and
+//      XOR-swizzled by a permutation of the row's low four bits, so both the 16-byte fragment
+//      reads and the transposing reads are free of bank conflicts).  Per block: S^T = K Q^T
+//      (each lane then holds scores of one query), an online softmax in base 2, and
+//      O^T += V^T P^T with the V^T fragments from the transposing LDS read; every LDS operand
+//      is read one step ahead of its products (one wave per SIMD: nothing else hides the
+//      latency).  The running maximum moves only when a score exceeds it by more than 2^8
+//      (the weights stay <= 256, the result is unchanged, and the accumulators are rescaled
+//      rarely).  The output is divided by the softmax sum, multiplied by sigmoid(gate) and
 //      stored straight from the result layout.
 #include "common.h"
 #include "launch.h"
@@ -43,10 +47,15 @@ struct AttnSmem {
 };
 static_assert(sizeof(AttnSmem) == 128 * 1024, "attention LDS");
 
+// Chunk permutation of a row: ((r & 7) << 1) | bit 3 of r.  For 16 consecutive rows it is a
+// bijection on 0..15 (the 16-byte fragment reads of 16 rows hit 16 different bank groups), and
+// rows 4a..4a+3 differ in bits 1..2 (the transposing reads of 4 rows x 2 adjacent chunks hit 8).
+__device__ __forceinline__ int rsw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+
 // Swizzled element offset of (row, col) in a [rows][256] bf16 tile: chunk col/8 of the row sits
-// at chunk position (col/8) ^ (row & 15).
+// at chunk position (col/8) ^ rsw(row).
 __device__ __forceinline__ int swz(int row, int col) {
-  return row * at::D + ((((col >> 3) ^ (row & 15)) << 3) | (col & 7));
+  return row * at::D + ((((col >> 3) ^ rsw(row)) << 3) | (col & 7));
 }
 
 __device__ __forceinline__ f4 amfma(abf8 a, abf8 b, f4 c) {
@@ -165,17 +174,37 @@ __global__ __launch_bounds__(256) void attn_kprep_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- 3. attention
 // Direct copies of 64 rows (two per 1 KiB copy) of a [rows][256] bf16 source into a swizzled
-// LDS tile: lane i of copy u brings row 2u + i/32, chunk (i % 32) ^ (row & 15), so the LDS slot
-// of chunk c of a row is c ^ (row & 15).  Rows at or past `valid` re-read row valid - 1 (their
-// results are masked or dropped).  Copies u = q, q + NW, ... < 32 are this wave's.
+// LDS tile: lane i of copy u brings row 2u + i/32, chunk (i % 32) ^ rsw(row), so the LDS slot
+// of chunk c of a row is c ^ rsw(row).  Rows at or past `valid` re-read row valid - 1 (their
+// results are masked or dropped).  Copies u = q + NW j (j < 8) are this wave's: row
+// r = 2q + rr + 8j, whose swizzle rsw(r) = ((2q + rr) << 1) | (j & 1) depends on j only through
+// its parity, so the lane's element offset is o[j & 1] + 8 j stride.
+struct CopyOffs {
+  int32_t o[2];
+};
+__device__ __forceinline__ CopyOffs copy_offs(int64_t stride, int q, int lane) {
+  CopyOffs c;
+  const int rr = lane >> 5, ch = lane & 31, r0 = 2 * q + rr;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) c.o[b] = (int32_t)(r0 * stride + 8 * (ch ^ ((r0 << 1) | b)));
+  return c;
+}
 __device__ __forceinline__ void copy_rows(uint16_t* tile, const uint16_t* src, int64_t stride, int row0, int valid,
-                                          int q, int lane) {
+                                          int q, int lane, const CopyOffs& off) {
+  if (row0 + 64 <= valid) {
+    const uint16_t* base = src + (int64_t)row0 * stride;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_global_load_lds((aglb_void*)(base + 8 * j * stride + off.o[j & 1]),
+                                       (alds_void*)(tile + 2 * (q + at::NW * j) * at::D), 16, 0, 0);
+    return;
+  }
   const int rr = lane >> 5, ch = lane & 31;
   for (int u = q; u < 32; u += at::NW) {
     int r = 2 * u + rr;
     const int lr = r;
     if (row0 + r >= valid) r = valid - 1 - row0;
-    const uint16_t* s = src + (int64_t)(row0 + r) * stride + 8 * (ch ^ (lr & 15));
+    const uint16_t* s = src + (int64_t)(row0 + r) * stride + 8 * (ch ^ rsw(lr));
     __builtin_amdgcn_global_load_lds((aglb_void*)s, (alds_void*)(tile + 2 * u * at::D), 16, 0, 0);
   }
 }
@@ -220,10 +249,12 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a, int nblk_tota
   const uint16_t* vsrc = static_cast<const uint16_t*>(a.v) + start * a.v_stride + (int64_t)g * D;
 
   // q rows into tiles 2 and 3 (rows 0..63, 64..127 of the block), K/V block 0 into tiles 0, 1
-  copy_rows(&sm.t[2][0][0], qsrc, a.q_stride, q0, len, w, lane);
-  copy_rows(&sm.t[3][0][0], qsrc, a.q_stride, q0 + BK, len, w, lane);
-  copy_rows(&sm.t[0][0][0], ksrc, a.k_out_stride, 0, len, w, lane);
-  copy_rows(&sm.t[1][0][0], vsrc, a.v_stride, 0, len, w, lane);
+  const CopyOffs qoff = copy_offs(a.q_stride, w, lane), koff = copy_offs(a.k_out_stride, w, lane),
+                 voff = copy_offs(a.v_stride, w, lane);
+  copy_rows(&sm.t[2][0][0], qsrc, a.q_stride, q0, len, w, lane, qoff);
+  copy_rows(&sm.t[3][0][0], qsrc, a.q_stride, q0 + BK, len, w, lane, qoff);
+  copy_rows(&sm.t[0][0][0], ksrc, a.k_out_stride, 0, len, w, lane, koff);
+  copy_rows(&sm.t[1][0][0], vsrc, a.v_stride, 0, len, w, lane, voff);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -289,29 +320,57 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a, int nblk_tota
   for (int kb = 0; kb < nkb; ++kb) {
     if (kb > 0) __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // block kb has landed; every wave is done with the other buffer
-    if (kb + 1 < nkb) {
-      const int nbuf = ((kb + 1) & 1) * 2;
-      copy_rows(&sm.t[nbuf][0][0], ksrc, a.k_out_stride, (kb + 1) * BK, len, w, lane);
-      copy_rows(&sm.t[nbuf + 1][0][0], vsrc, a.v_stride, (kb + 1) * BK, len, w, lane);
+    // copies of block kb + 1: spread over the K S^T steps below (a copy holds the wave at issue
+    // for ~4 products' time) when the block lies inside the sequence, all at once otherwise
+    const int nrow = (kb + 1) * BK;
+    const bool next = kb + 1 < nkb, spread = next && nrow + BK <= len;
+    uint16_t* nK = &sm.t[((kb + 1) & 1) * 2][0][0];
+    uint16_t* nV = nK + BK * D;
+    const uint16_t* kcp = ksrc + (int64_t)nrow * a.k_out_stride;
+    const uint16_t* vcp = vsrc + (int64_t)nrow * a.v_stride;
+    if (next && !spread) {
+      copy_rows(nK, ksrc, a.k_out_stride, nrow, len, w, lane, koff);
+      copy_rows(nV, vsrc, a.v_stride, nrow, len, w, lane, voff);
     }
     const uint16_t* Kt = &sm.t[(kb & 1) * 2][0][0];
     const uint16_t* Vt = &sm.t[(kb & 1) * 2 + 1][0][0];
-    // S^T = K Q^T: D[key 4lg+i of tile kt][query ln]
+    // S^T = K Q^T: D[key 4lg+i of tile kt][query ln]; K fragments one 32-dim step ahead
     f4 st[QT][4];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) st[qt][kt] = zero;
+    abf8 kf[2][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) kf[0][kt] = *reinterpret_cast<const abf8*>(Kt + swz(16 * kt + ln, 8 * lg));
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      abf8 kf[4];
+      if (spread) {
+        __builtin_amdgcn_global_load_lds((aglb_void*)(kcp + 8 * ks * a.k_out_stride + koff.o[ks & 1]),
+                                         (alds_void*)(nK + 2 * (w + NW * ks) * D), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((aglb_void*)(vcp + 8 * ks * a.v_stride + voff.o[ks & 1]),
+                                         (alds_void*)(nV + 2 * (w + NW * ks) * D), 16, 0, 0);
+      }
+      if (ks < 7) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) kf[kt] = *reinterpret_cast<const abf8*>(Kt + swz(16 * kt + ln, 32 * ks + 8 * lg));
+        for (int kt = 0; kt < 4; ++kt)
+          kf[(ks + 1) & 1][kt] = *reinterpret_cast<const abf8*>(Kt + swz(16 * kt + ln, 32 * (ks + 1) + 8 * lg));
+      }
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) st[qt][kt] = amfma(kf[kt], qf[qt][ks], st[qt][kt]);
+        for (int qt = 0; qt < QT; ++qt) st[qt][kt] = amfma(kf[ks & 1][kt], qf[qt][ks], st[qt][kt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // V^T fragments of dim tiles 0 and 1, then the softmax while they load
+    uint2 vq[3][4];
+#pragma unroll
+    for (int d = 0; d < 2; ++d)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        vq[d][2 * j] = atr4(Vt + swz(32 * j + trow, 16 * d + tcol));
+        vq[d][2 * j + 1] = atr4(Vt + swz(32 * j + 16 + trow, 16 * d + tcol));
+      }
     // causal and end-of-sequence mask, online softmax (base 2), P^T operands
     const int kbase = kb * BK;
     abf8 pf[QT][2];
@@ -334,43 +393,55 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a, int nblk_tota
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[qt][kt][i]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrun[qt], mx);
-      const float alpha = __builtin_amdgcn_exp2f(mrun[qt] - mnew);
-      mrun[qt] = mnew;
+      // move the running maximum only past a margin of 8 (factor 256)
+      const bool up = mx > mrun[qt] + 8.0f;
+      if (__builtin_amdgcn_ballot_w64(up) != 0) {
+        const float mnew = up ? mx : mrun[qt];
+        const float alpha = __builtin_amdgcn_exp2f(mrun[qt] - mnew);
+        mrun[qt] = mnew;
+        lsum[qt] *= alpha;
+#pragma unroll
+        for (int d = 0; d < 16; ++d) acc[qt][d] *= alpha;
+      }
       float ps = 0.f;
       float p[4][4];
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[kt][i] = __builtin_amdgcn_exp2f(st[qt][kt][i] - mnew);
+          p[kt][i] = __builtin_amdgcn_exp2f(st[qt][kt][i] - mrun[qt]);
           ps += p[kt][i];
         }
-      lsum[qt] = lsum[qt] * alpha + ps;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+      lsum[qt] += ps;
+      // keys 32 j + 4 lg + i (tile 2 j) then 32 j + 16 + 4 lg + i (tile 2 j + 1)
 #pragma unroll
-        for (int d = 0; d < 16; ++d) acc[qt][d] *= alpha;
-      }
-      // keys 32 ks + 4 lg + i (tile 2 ks) then 32 ks + 16 + 4 lg + i (tile 2 ks + 1)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const uint4 u = make_uint4(pack_bf16x2(p[2 * ks][0], p[2 * ks][1]), pack_bf16x2(p[2 * ks][2], p[2 * ks][3]),
-                                   pack_bf16x2(p[2 * ks + 1][0], p[2 * ks + 1][1]),
-                                   pack_bf16x2(p[2 * ks + 1][2], p[2 * ks + 1][3]));
-        pf[qt][ks] = __builtin_bit_cast(abf8, u);
+      for (int j = 0; j < 2; ++j) {
+        const uint4 u = make_uint4(pack_bf16x2(p[2 * j][0], p[2 * j][1]), pack_bf16x2(p[2 * j][2], p[2 * j][3]),
+                                   pack_bf16x2(p[2 * j + 1][0], p[2 * j + 1][1]),
+                                   pack_bf16x2(p[2 * j + 1][2], p[2 * j + 1][3]));
+        pf[qt][j] = __builtin_bit_cast(abf8, u);
       }
     }
-    // O^T += V^T P^T: A[m = dim 16 d + ln][k] from the transposing read of the V rows
+    __builtin_amdgcn_sched_barrier(0);
+    // O^T += V^T P^T: A[m = dim 16 d + ln][k] from the transposing read of the V rows, two dim
+    // tiles ahead
 #pragma unroll
     for (int d = 0; d < 16; ++d) {
+      if (d < 14) {
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const uint2 lo = atr4(Vt + swz(32 * ks + trow, 16 * d + tcol));
-        const uint2 hi = atr4(Vt + swz(32 * ks + 16 + trow, 16 * d + tcol));
+        for (int j = 0; j < 2; ++j) {
+          vq[(d + 2) % 3][2 * j] = atr4(Vt + swz(32 * j + trow, 16 * (d + 2) + tcol));
+          vq[(d + 2) % 3][2 * j + 1] = atr4(Vt + swz(32 * j + 16 + trow, 16 * (d + 2) + tcol));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint2 lo = vq[d % 3][2 * j], hi = vq[d % 3][2 * j + 1];
         const abf8 vf = __builtin_bit_cast(abf8, make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
-        for (int qt = 0; qt < QT; ++qt) acc[qt][d] = amfma(vf, pf[qt][ks], acc[qt][d]);
+        for (int qt = 0; qt < QT; ++qt) acc[qt][d] = amfma(vf, pf[qt][j], acc[qt][d]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 

@@ -286,7 +286,8 @@ size_t agnes_attn_prefill_workspace_size(int num_seqs, int64_t total_tokens);
  *   o              [total_tokens, num_q_heads, head_dim] contiguous, o_dtype
  *   workspace      >= agnes_attn_prefill_workspace_size() bytes, 256-byte aligned
  *
- * Supported: head_dim 256, rot_dim 64, num_q_heads % num_kv_heads == 0.  The
+ * Supported: head_dim 256, rot_dim 64, num_q_heads % num_kv_heads == 0, token
+ * strides of q, k, v and k_out up to 2^24 elements.  The
  * products run on bf16 matrix cores with fp32 accumulation: q after norm and
  * rotary, k as stored in k_out, v, and the softmax weights are bf16 operands;
  * the softmax statistics are fp32.  k_out, v_out and o must not overlap any
