@@ -15,6 +15,7 @@ discosf article "Agnes 3.0 Flash 刚上线就刷屏…", section 二.1):
   decode_fused    one decode token through conv, recurrence and norm in one launch
 The global attention layer of the same model (model card, rows 全局注意力 and 位置编码):
   attn_prefill    q/k RMS-norm + partial three-axis rotary, causal GQA softmax attention, sigmoid gate
+  attn_decode     one token per entry against a bf16 KV cache (the new k, v written at index len)
 """
 import torch
 
@@ -22,6 +23,7 @@ from . import _lib
 
 __all__ = ["conv", "prefill_chunked", "prefill_fused", "decode_step", "gated_rmsnorm", "decode_fused",
            "prefill_workspace_size", "attn_prefill", "attn_prefill_workspace_size",
+           "attn_decode", "attn_decode_workspace_size",
            "AgnesError", "version", "LIB_PATH"]
 
 LIB_PATH = _lib.LIB_PATH
@@ -360,3 +362,57 @@ def attn_prefill(q, k, v, gate, q_norm_weight, k_norm_weight, cu_seqlens, *, pos
         _stream(q.device))
     _check("agnes_attn_prefill", st)
     return o, k_out
+
+
+def attn_decode_workspace_size(batch, num_q_heads, num_kv_heads, max_len):
+    return int(_lib.load().agnes_attn_decode_workspace_size(batch, num_q_heads, num_kv_heads, max_len))
+
+
+def attn_decode(q, k, v, gate, q_norm_weight, k_norm_weight, k_cache, v_cache, cache_lens, *, positions=None,
+                rope_base=1e7, norm_eps=1e-6, scale=0.0, o=None, o_dtype=None, workspace=None):
+    """One decode step of the global attention layer.
+
+    q, gate: bf16 [B, Hq, 256]; k, v: bf16 [B, Hkv, 256]; caches: contiguous bf16
+    [B, max_len, Hkv, 256] (row cache_lens[b] of entry b is written); cache_lens: int32 [B]
+    (device; entries outside [0, max_len) are padding); positions: int32 [3, B] or None.
+    Returns o [B, Hq, 256].  The caller advances cache_lens.
+    """
+    B, Hq, _ = q.shape
+    Hkv = k.shape[1]
+    strides = {}
+    for t, name, h in ((q, "q", Hq), (gate, "gate", Hq), (k, "k", Hkv), (v, "v", Hkv)):
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+        strides[name] = _heads(t, name, h, ATTN_HEAD_DIM)
+    for c, name in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        if c.dtype != torch.bfloat16 or c.dim() != 4 or tuple(c.shape[::2]) != (B, Hkv) \
+                or c.shape[3] != ATTN_HEAD_DIM or not c.is_contiguous():
+            raise ValueError(f"{name}: expected contiguous bf16 [{B}, max_len, {Hkv}, 256]")
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    max_len = k_cache.shape[1]
+    if cache_lens.dtype != torch.int32 or cache_lens.numel() != B:
+        raise ValueError(f"cache_lens: expected int32 [{B}]")
+    for t, name in ((q_norm_weight, "q_norm_weight"), (k_norm_weight, "k_norm_weight")):
+        if t.dtype != torch.bfloat16 or t.numel() != ATTN_HEAD_DIM or not t.is_contiguous():
+            raise ValueError(f"{name}: expected contiguous bf16 [256]")
+    ps = 0
+    if positions is not None:
+        if positions.dtype != torch.int32 or positions.dim() != 2 or positions.shape[0] != 3 \
+                or positions.shape[1] != B or positions.stride(1) != 1:
+            raise ValueError("positions: expected int32 [3, B] with unit inner stride")
+        ps = positions.stride(0)
+    if o is None:
+        o = torch.empty((B, Hq, ATTN_HEAD_DIM), dtype=o_dtype or torch.bfloat16, device=q.device)
+    elif not o.is_contiguous():
+        raise ValueError("o must be contiguous")
+    need = attn_decode_workspace_size(B, Hq, Hkv, max_len)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    st = _lib.load().agnes_attn_decode(
+        _ptr(q), strides["q"], _ptr(k), strides["k"], _ptr(v), strides["v"], _ptr(gate), strides["gate"],
+        _ptr(q_norm_weight), _ptr(k_norm_weight), _ptr(positions), ps, _ptr(k_cache), _ptr(v_cache), max_len,
+        _ptr(cache_lens), B, Hq, Hkv, ATTN_HEAD_DIM, ATTN_ROT_DIM, rope_base, norm_eps, scale, _ptr(o), _dt(o),
+        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check("agnes_attn_decode", st)
+    return o

@@ -35,6 +35,11 @@ SIGNATURES = {
                                    c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_int, c_int64, c_int,
                                    c_int, c_int, c_int, c_float, c_float, c_float, c_void_p, c_int64,
                                    c_void_p, c_int64, c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
+    "agnes_attn_decode_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int64]),
+    "agnes_attn_decode": (c_int, [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
+                                  c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_int64, c_void_p,
+                                  c_int, c_int, c_int, c_int, c_int, c_float, c_float, c_float, c_void_p, c_int,
+                                  c_void_p, c_size_t, c_void_p]),
     "agnes_gdn_status_string": (ctypes.c_char_p, [c_int]),
     "agnes_gdn_last_hip_error": (c_int, []),
     "agnes_gdn_version": (ctypes.c_char_p, []),

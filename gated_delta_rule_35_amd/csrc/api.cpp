@@ -348,3 +348,59 @@ AGNES_API int agnes_attn_prefill(const void* q, int64_t q_token_stride, const vo
   a.workspace = workspace; a.workspace_bytes = workspace_bytes;
   return hip_status(agnes::launch_attn_prefill(a, static_cast<hipStream_t>(stream)));
 }
+
+AGNES_API size_t agnes_attn_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int64_t max_len) {
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_len <= 0) return 0;
+  return agnes::attn_decode_workspace(batch, num_q_heads, num_kv_heads, max_len);
+}
+
+AGNES_API int agnes_attn_decode(const void* q, int64_t q_stride, const void* k, int64_t k_stride, const void* v,
+                                int64_t v_stride, const void* gate, int64_t gate_stride, const void* q_norm_weight,
+                                const void* k_norm_weight, const int32_t* positions, int64_t positions_stride,
+                                void* k_cache, void* v_cache, int64_t max_len, const int32_t* cache_lens, int batch,
+                                int num_q_heads, int num_kv_heads, int head_dim, int rot_dim, float rope_base,
+                                float norm_eps, float scale, void* o, agnes_dtype o_dtype, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  constexpr int kAttnDim = 256;
+  if (!valid_dtype(o_dtype)) return AGNES_ERR_INVALID_ARG;
+  if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_len <= 0) return AGNES_ERR_INVALID_ARG;
+  if (head_dim != kAttnDim || rot_dim != 64 || num_q_heads % num_kv_heads) return AGNES_ERR_UNSUPPORTED;
+  if (max_len > (int64_t)1 << 30) return AGNES_ERR_UNSUPPORTED;
+  if (batch == 0) return AGNES_OK;
+  if (!q || !k || !v || !gate || !q_norm_weight || !k_norm_weight || !k_cache || !v_cache || !cache_lens || !o)
+    return AGNES_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(gate, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(o, 16) || !aligned(q_norm_weight, 8) || !aligned(k_norm_weight, 8) ||
+      !aligned(positions, 4) || !aligned(cache_lens, 4))
+    return AGNES_ERR_INVALID_ARG;
+  const int64_t qw = (int64_t)num_q_heads * head_dim, kw = (int64_t)num_kv_heads * head_dim;
+  if (q_stride < qw || gate_stride < qw || k_stride < kw || v_stride < kw || q_stride % 8 || gate_stride % 8 ||
+      k_stride % 8 || v_stride % 8)
+    return AGNES_ERR_INVALID_ARG;
+  if (positions && positions_stride < batch) return AGNES_ERR_INVALID_ARG;
+  if (!std::isfinite(rope_base) || rope_base <= 0.f || !std::isfinite(norm_eps) || norm_eps < 0.f ||
+      !std::isfinite(scale))
+    return AGNES_ERR_INVALID_ARG;
+  const int64_t cache_elems = (int64_t)batch * max_len * kw;
+  const Span os = span(o, batch, qw, qw, esize(o_dtype));
+  const Span kc = span(k_cache, 1, 0, cache_elems, 2), vc = span(v_cache, 1, 0, cache_elems, 2);
+  const Span ins[5] = {span(q, batch, q_stride, qw, 2), span(k, batch, k_stride, kw, 2), span(v, batch, v_stride, kw, 2),
+                       span(gate, batch, gate_stride, qw, 2), span(cache_lens, 1, 0, batch, 4)};
+  for (const Span& in : ins)
+    if (overlap(os, in) || overlap(kc, in) || overlap(vc, in)) return AGNES_ERR_INVALID_ARG;
+  if (overlap(os, kc) || overlap(os, vc) || overlap(kc, vc)) return AGNES_ERR_INVALID_ARG;
+  const size_t need = agnes::attn_decode_workspace(batch, num_q_heads, num_kv_heads, max_len);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return AGNES_ERR_WORKSPACE;
+
+  agnes::AttnArgs a{};
+  a.q = q; a.k = k; a.v = v; a.gate = gate;
+  a.q_stride = q_stride; a.k_stride = k_stride; a.v_stride = v_stride; a.gate_stride = gate_stride;
+  a.q_norm_w = q_norm_weight; a.k_norm_w = k_norm_weight;
+  a.pos3 = positions; a.pos3_stride = positions_stride;
+  a.total = batch; a.hq = num_q_heads; a.hkv = num_kv_heads;
+  a.rope_base = rope_base; a.eps = norm_eps; a.scale = scale;
+  a.o = o; a.o_dtype = (int)o_dtype;
+  a.workspace = workspace; a.workspace_bytes = workspace_bytes;
+  a.k_cache = k_cache; a.v_cache = v_cache; a.max_len = max_len; a.cache_lens = cache_lens;
+  return hip_status(agnes::launch_attn_decode(a, static_cast<hipStream_t>(stream)));
+}

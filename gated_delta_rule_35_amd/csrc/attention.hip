@@ -4,7 +4,7 @@
 // paired with dim j + 32), causal softmax attention with scale 1/16 inside each sequence, and a
 // sigmoid gate on the output.
 //
-// Prefill: three launches.
+// Prefill: three launches (decode: three more, at the end of this file).
 //   1. attn_offsets_kernel: first 128-query block of every sequence (device prefix sum).
 //   2. attn_kprep_kernel: per (token, KV head) the normalised, rotated k in bf16 (the KV cache
 //      rows, written where the caller says), an optional copy of v, and per token the 32 (cos,
@@ -468,6 +468,296 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a, int nblk_tota
       }
     }
   }
+}
+
+// ---------------------------------------------------------------- decode
+// One new token per batch entry b; the caches [batch][max_len][hkv][256] hold cache_lens[b]
+// earlier tokens and the new one goes to index L = cache_lens[b].  An entry with L outside
+// [0, max_len) is padding: no cache write, zero output.
+typedef short ds4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int entry_len(const AttnArgs& a, int b) {
+  const int L = a.cache_lens[b];
+  return (L >= 0 && (int64_t)L < a.max_len) ? L : -1;
+}
+
+__device__ __forceinline__ f4 amfma16(ds4v a, ds4v b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// 1. One wave per (entry, row): rows 0..hq-1 are the query heads (normalised, rotated, scaled by
+// log2(e) times the softmax scale, bf16 into the workspace), rows hq.. the KV heads (k normalised
+// and rotated into the k cache, v copied into the v cache, both at index L).
+__global__ __launch_bounds__(256) void attn_decode_prep_kernel(AttnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int rows = a.hq + a.hkv;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= a.total * rows) return;
+  const int b = (int)(wid / rows), r = (int)(wid % rows);
+  const int L = entry_len(a, b);
+  if (L < 0) return;
+  const bool isq = r < a.hq;
+  const int hd = isq ? r : r - a.hq;
+  const uint16_t* src = isq ? static_cast<const uint16_t*>(a.q) + b * a.q_stride + (int64_t)hd * at::D
+                            : static_cast<const uint16_t*>(a.k) + b * a.k_stride + (int64_t)hd * at::D;
+  const uint2 raw = *reinterpret_cast<const uint2*>(src + 4 * lane);
+  float x[4] = {bf16_to_f32(raw.x & 0xffffu), bf16_to_f32(raw.x >> 16), bf16_to_f32(raw.y & 0xffffu),
+                bf16_to_f32(raw.y >> 16)};
+  const float ss = wave_sum(x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3]);
+  const float rr = rsqrt_fast(ss * (1.0f / at::D) + a.eps);
+  const uint2 wr = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(isq ? a.q_norm_w : a.k_norm_w) +
+                                                   4 * lane);
+  x[0] *= rr * bf16_to_f32(wr.x & 0xffffu);
+  x[1] *= rr * bf16_to_f32(wr.x >> 16);
+  x[2] *= rr * bf16_to_f32(wr.y & 0xffffu);
+  x[3] *= rr * bf16_to_f32(wr.y >> 16);
+  float y[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = __shfl_xor(x[e], 8);
+  if (lane < 16) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float2 cs = rope_cs(a, b, L, 4 * (lane & 7) + e);
+      x[e] = lane < 8 ? x[e] * cs.x - y[e] * cs.y : x[e] * cs.x + y[e] * cs.y;
+    }
+  }
+  if (isq) {
+    const float qs = (a.scale > 0.f ? a.scale : 0.0625f) * 1.4426950408889634f;
+    uint16_t* qb = reinterpret_cast<uint16_t*>(static_cast<unsigned char*>(a.workspace) + a.off_off) +
+                   ((int64_t)b * a.hq + hd) * at::D + 4 * lane;
+    *reinterpret_cast<uint2*>(qb) = make_uint2(pack_bf16x2(x[0] * qs, x[1] * qs), pack_bf16x2(x[2] * qs, x[3] * qs));
+  } else {
+    const int64_t row = (((int64_t)b * a.max_len + L) * a.hkv + hd) * at::D + 4 * lane;
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.k_cache) + row) =
+        make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.v_cache) + row) =
+        *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.v) + b * a.v_stride + (int64_t)hd * at::D +
+                                        4 * lane);
+  }
+}
+
+// 2. Split-K attention: one workgroup per (entry, KV head, key range of sk keys).  The query
+// heads of the KV head's group are the rows of one 16-row tile (the rest zero).  64-key blocks
+// are double-buffered in LDS as in the prefill; wave w takes keys 16w..16w+15 of each block:
+// S^T = K Q^T (16 keys x 16 rows), an online softmax per row, and O^T += V^T P^T on 16x16x16
+// products whose B operand is the score fragment as it stands.  The waves' partial results are
+// merged through LDS into one (max, sum, O) per query head of the range, in the workspace.
+__global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int ns, int sk) {
+  using namespace at;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  AttnSmem& sm = *reinterpret_cast<AttnSmem*>(smem_raw);
+  const int G = a.hq / a.hkv;
+  const int s = blockIdx.x % ns, g = (blockIdx.x / ns) % a.hkv, b = blockIdx.x / (ns * a.hkv);
+  const int L = entry_len(a, b);
+  if (L < 0) return;
+  float* part = reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) + a.tab_off) +
+                (((int64_t)b * a.hkv + g) * ns + s) * G * (2 + D);
+  const int k0 = s * sk, k1 = (k0 + sk < L + 1 ? k0 + sk : L + 1);
+  const int lane = threadIdx.x & 63, ln = lane & 15, lg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (k0 >= k1) {  // empty range: a partial that weighs nothing
+    if (threadIdx.x < G) {
+      part[threadIdx.x * (2 + D)] = -INFINITY;
+      part[threadIdx.x * (2 + D) + 1] = 0.f;
+    }
+    return;
+  }
+  const int nblk = (k1 - k0 + BK - 1) / BK, valid = k1 - k0;
+  const int64_t ts = (int64_t)a.hkv * D;  // cache token stride
+  const uint16_t* ksrc = static_cast<const uint16_t*>(a.k_cache) + (((int64_t)b * a.max_len + k0) * a.hkv + g) * D;
+  const uint16_t* vsrc = static_cast<const uint16_t*>(a.v_cache) + (((int64_t)b * a.max_len + k0) * a.hkv + g) * D;
+  const CopyOffs off = copy_offs(ts, w, lane);
+  copy_rows(&sm.t[0][0][0], ksrc, ts, 0, valid, w, lane, off);
+  copy_rows(&sm.t[1][0][0], vsrc, ts, 0, valid, w, lane, off);
+  // Q^T operands: rows ln < G are the query heads g G + ln
+  abf8 qf[8];
+  {
+    const uint16_t* qb = reinterpret_cast<const uint16_t*>(static_cast<const unsigned char*>(a.workspace) + a.off_off) +
+                         ((int64_t)b * a.hq + g * G + (ln < G ? ln : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint4 u = *reinterpret_cast<const uint4*>(qb + 32 * ks + 8 * lg);
+      qf[ks] = __builtin_bit_cast(abf8, ln < G ? u : make_uint4(0, 0, 0, 0));
+    }
+  }
+  const f4 zero = {0.f, 0.f, 0.f, 0.f};
+  f4 acc[16];
+#pragma unroll
+  for (int d = 0; d < 16; ++d) acc[d] = zero;
+  float mrun = -INFINITY, lsum = 0.f;
+  const int trow = 4 * lg + (ln >> 2), tcol = 4 * (ln & 3);
+  for (int kb = 0; kb < nblk; ++kb) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // block kb has landed; every wave is done with the other buffer
+    if (kb + 1 < nblk) {
+      const int nb = ((kb + 1) & 1) * 2;
+      copy_rows(&sm.t[nb][0][0], ksrc, ts, (kb + 1) * BK, valid, w, lane, off);
+      copy_rows(&sm.t[nb + 1][0][0], vsrc, ts, (kb + 1) * BK, valid, w, lane, off);
+    }
+    const uint16_t* Kt = &sm.t[(kb & 1) * 2][0][0];
+    const uint16_t* Vt = &sm.t[(kb & 1) * 2 + 1][0][0];
+    f4 st = zero;
+    abf8 kf[2];
+    kf[0] = *reinterpret_cast<const abf8*>(Kt + swz(16 * w + ln, 8 * lg));
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks < 7) kf[(ks + 1) & 1] = *reinterpret_cast<const abf8*>(Kt + swz(16 * w + ln, 32 * (ks + 1) + 8 * lg));
+      st = amfma(kf[ks & 1], qf[ks], st);
+    }
+    // keys k0 + 64 kb + 16 w + 4 lg + i at or past k1 do not exist
+    const int kidx = kb * BK + 16 * w + 4 * lg;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (kidx + i >= valid) st[i] = -INFINITY;
+    float m = fmaxf(fmaxf(st[0], st[1]), fmaxf(st[2], st[3]));
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));
+    const bool up = m > mrun + 8.0f;  // move the running maximum only past a margin of 8
+    if (__builtin_amdgcn_ballot_w64(up) != 0) {
+      const float mnew = up ? m : mrun;
+      const float alpha = __builtin_amdgcn_exp2f(mrun - mnew);
+      mrun = mnew;
+      lsum *= alpha;
+#pragma unroll
+      for (int d = 0; d < 16; ++d) acc[d] *= alpha;
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {  // a missing key weighs 0 (also while no key of this row exists)
+      p[i] = st[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st[i] - mrun);
+      lsum += p[i];
+    }
+    const ds4v pb = __builtin_bit_cast(ds4v, make_uint2(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])));
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+      const ds4v va = __builtin_bit_cast(ds4v, atr4(Vt + swz(16 * w + trow, 16 * d + tcol)));
+      acc[d] = amfma16(va, pb, acc[d]);
+    }
+  }
+  // merge the four waves: row q = ln, dims 16 d + 4 lg + i
+  lsum += __shfl_xor(lsum, 16);
+  lsum += __shfl_xor(lsum, 32);
+  __syncthreads();  // every wave is done with the tiles
+  float* red = reinterpret_cast<float*>(smem_raw);  // [wave][16 rows][2 + 256]
+  float* mine = red + (w * 16 + ln) * (2 + D);
+  if (lg == 0) {
+    mine[0] = mrun;
+    mine[1] = lsum;
+  }
+#pragma unroll
+  for (int d = 0; d < 16; ++d)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mine[2 + 16 * d + 4 * lg + i] = acc[d][i];
+  __syncthreads();
+  const int dim = threadIdx.x;  // 256 threads, one dim each
+  for (int q = 0; q < G; ++q) {
+    float mw[NW], M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      mw[v] = red[(v * 16 + q) * (2 + D)];
+      M = fmaxf(M, mw[v]);
+    }
+    float l = 0.f, o = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const float wv = mw[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[v] - M);
+      l += wv * red[(v * 16 + q) * (2 + D) + 1];
+      o += wv * red[(v * 16 + q) * (2 + D) + 2 + dim];
+    }
+    float* pq = part + q * (2 + D);
+    if (dim == 0) {
+      pq[0] = M;
+      pq[1] = l;
+    }
+    pq[2 + dim] = o;
+  }
+}
+
+// 3. One wave per (entry, query head): merge the key ranges, divide by the softmax sum, apply
+// sigmoid(gate) and store; padding entries get zeros.
+template <int O_DT>
+__global__ __launch_bounds__(256) void attn_decode_combine_kernel(AttnArgs a, int ns) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= a.total * a.hq) return;
+  const int b = (int)(wid / a.hq), h = (int)(wid % a.hq);
+  const int G = a.hq / a.hkv, g = h / G, q = h % G;
+  const int64_t oi = ((int64_t)b * a.hq + h) * at::D + 4 * lane;
+  const int L = entry_len(a, b);
+  f4 o = {0.f, 0.f, 0.f, 0.f};
+  if (L >= 0) {
+    const float* part = reinterpret_cast<const float*>(static_cast<const unsigned char*>(a.workspace) + a.tab_off) +
+                        (((int64_t)b * a.hkv + g) * ns) * G * (2 + at::D) + q * (2 + at::D);
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, part[(int64_t)s * G * (2 + at::D)]);
+    float l = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float* ps = part + (int64_t)s * G * (2 + at::D);
+      const float ms = ps[0];
+      if (ms == -INFINITY) continue;  // an empty key range (its values are not written)
+      const float wv = __builtin_amdgcn_exp2f(ms - M);
+      l += wv * ps[1];
+      const float4 v = *reinterpret_cast<const float4*>(ps + 2 + 4 * lane);
+      o[0] += wv * v.x;
+      o[1] += wv * v.y;
+      o[2] += wv * v.z;
+      o[3] += wv * v.w;
+    }
+    const uint2 gr = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.gate) + b * a.gate_stride +
+                                                     (int64_t)h * at::D + 4 * lane);
+    const float gv[4] = {bf16_to_f32(gr.x & 0xffffu), bf16_to_f32(gr.x >> 16), bf16_to_f32(gr.y & 0xffffu),
+                         bf16_to_f32(gr.y >> 16)};
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] *= inv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv[e]));
+  }
+  store4<O_DT>(a.o, oi, o);
+}
+
+// Decode split: about 1024 workgroups over the batch and KV heads, ranges of at least 64 keys.
+static void decode_split(int64_t batch, int hkv, int64_t max_len, int& ns, int& sk) {
+  const int64_t pairs = batch * hkv > 0 ? batch * hkv : 1;
+  int64_t n = (1024 + pairs - 1) / pairs;
+  const int64_t nmax = (max_len + at::BK - 1) / at::BK;
+  if (n > nmax) n = nmax;
+  if (n < 1) n = 1;
+  int64_t k = (max_len + n - 1) / n;
+  k = (k + at::BK - 1) / at::BK * at::BK;
+  sk = (int)k;
+  ns = (int)((max_len + k - 1) / k);
+}
+
+size_t attn_decode_workspace(int64_t batch, int hq, int hkv, int64_t max_len) {
+  if (batch <= 0 || hkv <= 0) return 0;
+  int ns, sk;
+  decode_split(batch, hkv, max_len, ns, sk);
+  const size_t qb = ((size_t)batch * hq * at::D * 2 + 255) & ~size_t(255);
+  return qb + (size_t)batch * hq * ns * (2 + at::D) * 4;
+}
+
+hipError_t launch_attn_decode(AttnArgs a, hipStream_t st) {
+  if (a.total == 0) return hipSuccess;
+  int ns, sk;
+  decode_split(a.total, a.hkv, a.max_len, ns, sk);
+  a.off_off = 0;  // bf16 [batch][hq][256] prepared queries
+  a.tab_off = ((size_t)a.total * a.hq * at::D * 2 + 255) & ~size_t(255);  // partial results
+  const int64_t waves = a.total * (a.hq + a.hkv);
+  hipLaunchKernelGGL(attn_decode_prep_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t smem = sizeof(AttnSmem);
+  static const hipError_t a0 = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_decode_kernel),
+                                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (a0 != hipSuccess) return a0;
+  hipLaunchKernelGGL(attn_decode_kernel, dim3((unsigned)(a.total * a.hkv * ns)), dim3(256), smem, st, a, ns, sk);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t cw = a.total * a.hq;
+  if (a.o_dtype == DT_BF16)
+    hipLaunchKernelGGL(attn_decode_combine_kernel<DT_BF16>, dim3((unsigned)((cw + 3) / 4)), dim3(256), 0, st, a, ns);
+  else
+    hipLaunchKernelGGL(attn_decode_combine_kernel<DT_F32>, dim3((unsigned)((cw + 3) / 4)), dim3(256), 0, st, a, ns);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- host side

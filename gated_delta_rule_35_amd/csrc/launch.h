@@ -148,6 +148,8 @@ struct AttnArgs {
 
 hipError_t launch_attn_prefill(AttnArgs a, hipStream_t s);
 size_t attn_prefill_workspace(int num_seqs, int64_t total);
+hipError_t launch_attn_decode(AttnArgs a, hipStream_t s);
+size_t attn_decode_workspace(int64_t batch, int hq, int hkv, int64_t max_len);
 
 hipError_t launch_conv(const ConvArgs& a, hipStream_t s);
 hipError_t launch_conv_history(const ConvArgs& a, hipStream_t s);  // final history only

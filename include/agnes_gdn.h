@@ -304,6 +304,46 @@ int agnes_attn_prefill(const void* q, int64_t q_token_stride, const void* k, int
                        void* o, agnes_dtype o_dtype, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/*
+ * agnes_attn_decode_workspace_size — bytes of device workspace agnes_attn_decode
+ * needs for this batch, head count and cache length (0 for an empty batch).
+ */
+size_t agnes_attn_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
+                                        int64_t max_len);
+
+/*
+ * agnes_attn_decode — one decode step of the global attention layer (model card
+ * "Agnes-3.0-Flash Preview", 架构 table, rows 全局注意力 and 位置编码; discosf
+ * article, section 二.1: only these layers keep a KV cache).  For each batch
+ * entry b with L = cache_lens[b] tokens cached: the new token's q and k are
+ * RMS-normed and rotated at position L (or positions[.][b]), its k and v are
+ * written into the caches at index L, and its output is the softmax attention
+ * over the L + 1 cached keys, times sigmoid(gate).
+ *
+ *   q, gate        bf16 [batch, num_q_heads, head_dim], row strides in elements
+ *   k, v           bf16 [batch, num_kv_heads, head_dim], row strides in elements
+ *   q_norm_weight, k_norm_weight, rope_base, norm_eps, scale   as agnes_attn_prefill
+ *   positions      device int32 [3][positions_stride] per entry, or NULL (L on
+ *                  all three axes)
+ *   k_cache, v_cache  bf16 [batch, max_len, num_kv_heads, head_dim] contiguous;
+ *                  row L of entry b is written (k normalised and rotated, v as given)
+ *   cache_lens     device int32 [batch]; an entry with a length outside
+ *                  [0, max_len) is padding: its o is zero and no cache row changes
+ *   o              [batch, num_q_heads, head_dim] contiguous, o_dtype
+ *   workspace      >= agnes_attn_decode_workspace_size() bytes, 256-byte aligned
+ *
+ * The caller advances cache_lens after the call.  Same supported set and number
+ * formats as agnes_attn_prefill.  o, the caches and the inputs must not overlap.
+ */
+int agnes_attn_decode(const void* q, int64_t q_stride, const void* k, int64_t k_stride,
+                      const void* v, int64_t v_stride, const void* gate, int64_t gate_stride,
+                      const void* q_norm_weight, const void* k_norm_weight,
+                      const int32_t* positions, int64_t positions_stride, void* k_cache,
+                      void* v_cache, int64_t max_len, const int32_t* cache_lens, int batch,
+                      int num_q_heads, int num_kv_heads, int head_dim, int rot_dim,
+                      float rope_base, float norm_eps, float scale, void* o, agnes_dtype o_dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 const char* agnes_gdn_status_string(int status);
 
 /* hipError_t of the last AGNES_ERR_HIP returned on the calling thread (0 if none). */

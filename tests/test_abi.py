@@ -36,7 +36,7 @@ def header_functions():
 def test_header_declares_the_layer_calls():
     names = header_functions()
     for n in ("agnes_gdn_conv", "agnes_gdn_prefill_chunked", "agnes_gdn_decode_step",
-              "agnes_gdn_gated_rmsnorm", "agnes_attn_prefill"):
+              "agnes_gdn_gated_rmsnorm", "agnes_attn_prefill", "agnes_attn_decode"):
         assert n in names
     assert set(names) == set(_lib.SIGNATURES)
 
@@ -247,4 +247,37 @@ def test_attn_prefill_checks(lib):
     assert attn(lib) == WS
     assert attn(lib, ws=P[9], wsb=need - 1) == WS
     assert attn(lib, ws=P[9] + 16, wsb=need) == WS      # not 256-byte aligned
+    assert lib.agnes_gdn_last_hip_error() == 0
+
+
+def adec(lib, **kw):
+    B, hq, hkv, L = 8, 24, 4, 1000
+    a = dict(q=P[0], qs=hq * 256, k=P[1], ks=hkv * 256, v=P[2], vs=hkv * 256, g=P[3], gs=hq * 256, qw=P[4],
+             kw=P[4] + 512, pos=None, ps=0, kc=P[5], vc=P[6], L=L, lens=P[7], B=B, hq=hq, hkv=hkv, hd=256, rd=64,
+             base=1e7, eps=1e-6, sc=0.0, o=P[8], odt=BF16, ws=None, wsb=0)
+    a.update(kw)
+    return lib.agnes_attn_decode(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["g"], a["gs"], a["qw"], a["kw"],
+                                 a["pos"], a["ps"], a["kc"], a["vc"], a["L"], a["lens"], a["B"], a["hq"], a["hkv"],
+                                 a["hd"], a["rd"], a["base"], a["eps"], a["sc"], a["o"], a["odt"], a["ws"], a["wsb"],
+                                 None)
+
+
+def test_attn_decode_checks(lib):
+    assert adec(lib, B=0, q=None, kc=None) == 0         # empty batch
+    assert adec(lib, hd=128) == UNS
+    assert adec(lib, hq=22) == UNS                      # Hq % Hkv
+    assert adec(lib, L=0) == INV                        # no cache rows
+    assert adec(lib, kc=None) == INV
+    assert adec(lib, lens=None) == INV
+    assert adec(lib, qs=24 * 256 - 8) == INV
+    assert adec(lib, vs=4 * 256 + 4) == INV
+    assert adec(lib, kc=P[5] + 8) == INV                # misaligned
+    assert adec(lib, pos=P[9], ps=7) == INV             # positions stride below the batch
+    assert adec(lib, sc=float("nan")) == INV
+    assert adec(lib, vc=P[5] + 4096) == INV             # caches overlap
+    assert adec(lib, o=P[0] + 1024) == INV              # o overlaps q
+    need = lib.agnes_attn_decode_workspace_size(8, 24, 4, 1000)
+    assert need > 0
+    assert adec(lib) == WS
+    assert adec(lib, ws=P[10], wsb=need - 1) == WS
     assert lib.agnes_gdn_last_hip_error() == 0

@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synth import attn_prefill_inputs, f32_to_bf16_bits
+from synth import attn_prefill_inputs, attn_decode_inputs, f32_to_bf16_bits
 from tests.helpers import dev, host, rel_l2, as_f64, check_bf16_out
 
 torch = pytest.importorskip("torch")
@@ -102,3 +102,91 @@ def test_attn_prefill_t8192_sampled_rows():
     print(f"attention prefill T=8192 sampled rows: o rel-L2 {e:.3e}")
     assert e <= TOL
     check_bf16_out(ko, kr, exact_frac=0.99)
+
+
+# ---------------------------------------------------------------- decode
+
+def _decode(d, o_dtype=torch.float32, lens=None):
+    kc, vc = dev(d["k_cache"]), dev(d["v_cache"])
+    lens = d["lens"] if lens is None else lens
+    o = gdn.attn_decode(dev(d["q"]), dev(d["k"]), dev(d["v"]), dev(d["gate"]), dev(d["qw"]), dev(d["kw"]), kc, vc,
+                        dev(np.asarray(lens, np.int32)), o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    return host(o), host(kc), host(vc)
+
+
+def _decode_check(d, lens, lmax):
+    o, kc, vc = _decode(d, lens=lens)
+    live = [b for b in range(len(lens)) if 0 <= lens[b] < lmax]
+    ro, rkc, rvc = oracle.attention_decode(d["q"][live], d["k"][live], d["v"][live], d["gate"][live],
+                                           d["k_cache"][live], d["v_cache"][live], np.asarray(lens)[live],
+                                           d["qw"], d["kw"])
+    e = rel_l2(o[live], ro)
+    for b in range(len(lens)):
+        if b not in live:  # padding: zero output, cache untouched
+            assert not o[b].any()
+            np.testing.assert_array_equal(kc[b], d["k_cache"][b])
+            np.testing.assert_array_equal(vc[b], d["v_cache"][b])
+    for i, b in enumerate(live):
+        L = lens[b]
+        others = np.ones(lmax, bool)
+        others[L] = False
+        np.testing.assert_array_equal(kc[b][others], d["k_cache"][b][others])
+        np.testing.assert_array_equal(vc[b][others], d["v_cache"][b][others])
+        np.testing.assert_array_equal(vc[b][L], d["v"][b])
+        check_bf16_out(kc[b][L], rkc[i][L], exact_frac=0.99)
+    return e
+
+
+def test_attn_decode_mixed_lengths_and_padding():
+    """Empty cache, one token, a 64-key block edge, a long entry, and a padding entry (length
+    outside the cache)."""
+    rng = np.random.default_rng(540)
+    lmax = 800
+    lens = [0, 1, 63, 64, 700, 800]
+    d = attn_decode_inputs(rng, [min(x, lmax) for x in lens], lmax)
+    e = _decode_check(d, lens, lmax)
+    print(f"attention decode mixed lengths: o rel-L2 {e:.3e}")
+    assert e <= TOL
+
+
+def test_attn_decode_long_context_splits():
+    """Caches of 8191 and 5000 tokens: the keys are split over several workgroups and merged."""
+    rng = np.random.default_rng(550)
+    lmax = 8192
+    lens = [8191, 5000]
+    d = attn_decode_inputs(rng, lens, lmax)
+    e = _decode_check(d, lens, lmax)
+    print(f"attention decode long context: o rel-L2 {e:.3e}")
+    assert e <= TOL
+
+
+def test_attn_decode_bf16_output_is_rne_of_fp32_output():
+    rng = np.random.default_rng(560)
+    d = attn_decode_inputs(rng, [10, 300], 512)
+    o32, _, _ = _decode(d)
+    o16, _, _ = _decode(d, torch.bfloat16)
+    np.testing.assert_array_equal(o16, f32_to_bf16_bits(o32))
+
+
+def test_attn_decode_continues_prefill():
+    """A GPU prefill of 100 tokens fills the cache (its k_out and v_out are the cache rows), then
+    three decode steps follow: their outputs are the oracle prefill's rows 100..102."""
+    rng = np.random.default_rng(570)
+    T, lmax, hq, hkv = 103, 128, 24, 4
+    d = attn_prefill_inputs(rng, [T], hq, hkv)
+    kc = torch.zeros((1, lmax, hkv, D), dtype=torch.bfloat16, device="cuda")
+    vc = torch.zeros((1, lmax, hkv, D), dtype=torch.bfloat16, device="cuda")
+    cu = np.array([0, 100], np.int32)
+    gdn.attn_prefill(dev(d["q"][:100]), dev(d["k"][:100]), dev(d["v"][:100]), dev(d["gate"][:100]), dev(d["qw"]),
+                     dev(d["kw"]), dev(cu), k_out=kc[0, :100], v_out=vc[0, :100])
+    outs = []
+    for t in range(100, T):
+        o = gdn.attn_decode(dev(d["q"][t:t + 1]), dev(d["k"][t:t + 1]), dev(d["v"][t:t + 1]), dev(d["gate"][t:t + 1]),
+                            dev(d["qw"]), dev(d["kw"]), kc, vc, dev(np.array([t], np.int32)), o_dtype=torch.float32)
+        outs.append(host(o)[0])
+    torch.cuda.synchronize()
+    ro, _ = oracle.attention_prefill(d["q"], d["k"], d["v"], d["gate"], [0, T], d["qw"], d["kw"])
+    e = rel_l2(np.stack(outs), ro[100:])
+    print(f"attention decode after prefill: o rel-L2 {e:.3e}")
+    assert e <= TOL
