@@ -9,7 +9,8 @@ prefill call (agnes_gdn_prefill_fused), then the norm.  The same chain as three 
 (256 sequences, one token each, fp32 states updated in place) and reports its state HBM GB/s,
 and the fused decode step (conv-history update + conv + L2 + recurrence + gated norm in one
 launch) beside the three unfused calls it replaces, and the prefill of the model's global
-attention layer (24 query / 4 KV heads of 256, T = 8192) with its matrix-core roofline.
+attention layer (24 query / 4 KV heads of 256, T = 8192) with its matrix-core roofline, and
+that layer's decode step over a 64 x 8191-token bf16 KV cache with its HBM roofline.
 
 Inputs are synthetic (seeded), generated on the host and resident in HBM before timing.
 
@@ -54,6 +55,11 @@ CAL_BYTES = 256 << 20          # device-to-device copy of known size, for the HB
 # 2 x 256 multiply-adds each per query head
 ATTN_HQ, ATTN_HKV, ATTN_D = 24, 4, 256
 ATTN_FLOP = ATTN_HQ * 4 * ATTN_D * T * (T + 1) // 2
+# attention decode: 64 entries with 8191 cached tokens each; per step the K and V caches of the
+# 8192 keys are read once, plus q, gate, o rows and the new k, v rows
+ATTN_DEC_B, ATTN_DEC_LEN = 64, 8192
+ATTN_DEC_BYTES = (ATTN_DEC_B * ATTN_DEC_LEN * ATTN_HKV * ATTN_D * 2 * 2
+                  + ATTN_DEC_B * ATTN_D * 2 * (3 * ATTN_HQ + 4 * ATTN_HKV))
 
 # HBM traffic per call from the committed counter summary (FETCH_SIZE and WRITE_SIZE runs, each
 # scaled by the same counter on the calibration copy).  A figure is used only while the source
@@ -280,6 +286,34 @@ def main():
     torch.cuda.synchronize()
     ms_attn = np.mean([e[0].elapsed_time(e[1]) for e in aevs])
     attn_tflops = ATTN_FLOP / (ms_attn * 1e-3) / 1e12
+    del aq, ak, av, ag, ako, ao, aws
+
+    # ---- global attention decode: 64 entries, 8191 cached tokens each
+    from synth import attn_decode_inputs
+    dd = attn_decode_inputs(np.random.default_rng(2002), [0] * ATTN_DEC_B, 1, ATTN_HQ, ATTN_HKV, ATTN_D)
+    dq, dk, dv, dg = (to_dev(dd[n], torch) for n in ("q", "k", "v", "gate"))
+    dkc = torch.randn((ATTN_DEC_B, ATTN_DEC_LEN, ATTN_HKV, ATTN_D), device="cuda").to(torch.bfloat16)
+    dvc = (torch.randn((ATTN_DEC_B, ATTN_DEC_LEN, ATTN_HKV, ATTN_D), device="cuda") * 1.43).to(torch.bfloat16)
+    dlens = torch.full((ATTN_DEC_B,), ATTN_DEC_LEN - 1, dtype=torch.int32, device="cuda")
+    dao = torch.empty((ATTN_DEC_B, ATTN_HQ, ATTN_D), dtype=torch.bfloat16, device="cuda")
+    dws = torch.empty(gdn.attn_decode_workspace_size(ATTN_DEC_B, ATTN_HQ, ATTN_HKV, ATTN_DEC_LEN), dtype=torch.uint8,
+                      device="cuda")
+
+    def adstep():
+        gdn.attn_decode(dq, dk, dv, dg, aqw, akw, dkc, dvc, dlens, o=dao, workspace=dws)
+
+    for _ in range(3):
+        adstep()
+    torch.cuda.synchronize()
+    devs2 = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.decode_steps)]
+    for i in range(args.decode_steps):
+        devs2[i][0].record()
+        adstep()
+        devs2[i][1].record()
+    torch.cuda.synchronize()
+    ms_adec = np.mean([e[0].elapsed_time(e[1]) for e in devs2])
+    adec_gbs = ATTN_DEC_BYTES / (ms_adec * 1e-3) / 1e9
+    del dkc, dvc
 
     pre_tflops = FLOP_PER_TOKEN * T / (ms_fpre * 1e-3) / 1e12
     res = {
@@ -339,6 +373,14 @@ def main():
                                            "achieved": round(attn_tflops, 2), "peak": MFMA_PEAK_TFLOPS,
                                            "unit": "TFLOP/s", "frac": round(attn_tflops / MFMA_PEAK_TFLOPS, 4),
                                            "flops_per_launch": ATTN_FLOP, "operands": "bf16"}},
+        "attention_decode": {"batch": ATTN_DEC_B, "cached_tokens": ATTN_DEC_LEN - 1, "steps": args.decode_steps,
+                             "us_per_step": round(ms_adec * 1e3, 2),
+                             "tokens_per_s": round(ATTN_DEC_B / (ms_adec * 1e-3), 1),
+                             "roofline": {"bound": "hbm",
+                                          "kernel": "agnes_attn_decode call (prep + split-K attention + combine)",
+                                          "achieved": round(adec_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                          "frac": round(adec_gbs / HBM_PEAK_GBS, 4),
+                                          "bytes_per_launch": ATTN_DEC_BYTES}},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
