@@ -22,7 +22,7 @@ import torch
 from . import _lib
 
 __all__ = ["conv", "prefill_chunked", "prefill_fused", "decode_step", "gated_rmsnorm", "decode_fused",
-           "prefill_workspace_size", "attn_prefill", "attn_prefill_workspace_size",
+           "prefill_workspace_size", "layer_prefill", "layer_prefill_workspace_size", "attn_prefill", "attn_prefill_workspace_size",
            "attn_decode", "attn_decode_workspace_size",
            "AgnesError", "version", "LIB_PATH"]
 
@@ -219,6 +219,66 @@ def prefill_fused(x, conv_weight, g, beta, cu_seqlens, *, num_k_heads, conv_bias
         _stream(x.device))
     _check("agnes_gdn_prefill_fused", st)
     return o, final_state
+
+
+def layer_prefill_workspace_size(num_seqs, total_tokens, num_k_heads, num_v_heads):
+    return _lib.load().agnes_gdn_layer_prefill_workspace_size(num_seqs, total_tokens, num_k_heads, num_v_heads,
+                                                              HEAD_DIM)
+
+
+def layer_prefill(x, conv_weight, g, beta, cu_seqlens, z, norm_weight, *, num_k_heads, conv_bias=None,
+                  conv_state=None, initial_state=None, final_state=None, output_final_state=True, scale=1.0,
+                  l2norm_eps=1e-6, norm_eps=1e-6, y=None, o=None, out_dtype=None, workspace=None):
+    """The whole delta-rule layer in prefill: conv + SiLU + L2(q, k), the chunked delta rule and
+    the gated RMS-norm in one call (the recurrence output need not go to memory).
+
+    x, conv_*, g, beta, cu_seqlens, states: as ``prefill_fused``; z: bf16 [T, Hv, 128] (heads
+    contiguous, token stride free); norm_weight: bf16 [128].  o, if given, also receives the
+    un-normalised recurrence output.  Returns (y [T, Hv, 128], final_state or None).
+    """
+    T, C = x.shape
+    Hk = num_k_heads
+    Hv = C // HEAD_DIM - 2 * Hk
+    if Hv <= 0 or C != (2 * Hk + Hv) * HEAD_DIM:
+        raise ValueError(f"x: {C} channels do not hold 2 x {Hk} key heads and whole value heads")
+    xs = _rows(x, "x", C)
+    zs = _heads(z, "z", Hv)
+    for t, name in ((conv_weight, "conv_weight"), (conv_bias, "conv_bias"), (conv_state, "conv_state"),
+                    (norm_weight, "norm_weight")):
+        if t is not None and (t.dtype != x.dtype or not t.is_contiguous()):
+            raise ValueError(f"{name}: contiguous, with x's dtype {x.dtype}")
+    if tuple(conv_weight.shape) != (C, 4) or norm_weight.numel() != HEAD_DIM or z.dtype != x.dtype:
+        raise ValueError("conv_weight [C, 4], norm_weight [128] and z of x's dtype expected")
+    for t, name in ((g, "g"), (beta, "beta")):
+        if t.dtype != torch.float32 or tuple(t.shape) != (T, Hv) or not t.is_contiguous():
+            raise ValueError(f"{name}: expected contiguous fp32 [{T}, {Hv}]")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    n = cu_seqlens.numel() - 1
+    if conv_state is not None and tuple(conv_state.shape) != (n, C, 3):
+        raise ValueError(f"conv_state: expected [{n}, {C}, 3]")
+    out_dtype = out_dtype or (y.dtype if y is not None else x.dtype)
+    if y is None:
+        y = torch.empty((T, Hv, HEAD_DIM), dtype=out_dtype, device=x.device)
+    for t, name in ((y, "y"), (o, "o")):
+        if t is not None and (not t.is_contiguous() or t.dtype != out_dtype or tuple(t.shape) != (T, Hv, HEAD_DIM)):
+            raise ValueError(f"{name}: contiguous {out_dtype} [{T}, {Hv}, 128] expected")
+    for s, name in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if s is not None and (s.dtype != torch.float32 or not s.is_contiguous()
+                              or tuple(s.shape) != (n, Hv, HEAD_DIM, HEAD_DIM)):
+            raise ValueError(f"{name}: expected contiguous fp32 [{n}, {Hv}, 128, 128]")
+    if final_state is None and output_final_state:
+        final_state = torch.empty((n, Hv, HEAD_DIM, HEAD_DIM), dtype=torch.float32, device=x.device)
+    need = layer_prefill_workspace_size(n, T, Hk, Hv)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    st = _lib.load().agnes_gdn_layer_prefill(
+        _ptr(x), xs, _dt(x), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state), _ptr(g), _ptr(beta),
+        _ptr(cu_seqlens), n, T, Hk, Hv, HEAD_DIM, scale, l2norm_eps, _ptr(initial_state), _ptr(final_state),
+        _ptr(z), zs, _ptr(norm_weight), norm_eps, _ptr(y), _ptr(o), _dt(y), _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(x.device))
+    _check("agnes_gdn_layer_prefill", st)
+    return y, final_state
 
 
 def decode_step(q, k, v, g, beta, state, *, scale=1.0, o=None, o_dtype=None):

@@ -30,6 +30,11 @@ SIGNATURES = {
                                        c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                        c_int, c_int, c_int, c_int, c_int, c_float, c_float, c_float,
                                        c_void_p, c_void_p, c_int, c_void_p]),
+    "agnes_gdn_layer_prefill_workspace_size": (c_size_t, [c_int, c_int64, c_int, c_int, c_int]),
+    "agnes_gdn_layer_prefill": (c_int, [c_void_p, c_int64, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                        c_void_p, c_void_p, c_int, c_int64, c_int, c_int, c_int, c_float,
+                                        c_float, c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_float,
+                                        c_void_p, c_void_p, c_int, c_void_p, c_size_t, c_void_p]),
     "agnes_attn_prefill_workspace_size": (c_size_t, [c_int, c_int64]),
     "agnes_attn_prefill": (c_int, [c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64, c_void_p, c_int64,
                                    c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_int, c_int64, c_int,

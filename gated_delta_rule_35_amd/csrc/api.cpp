@@ -404,3 +404,70 @@ AGNES_API int agnes_attn_decode(const void* q, int64_t q_stride, const void* k, 
   a.k_cache = k_cache; a.v_cache = v_cache; a.max_len = max_len; a.cache_lens = cache_lens;
   return hip_status(agnes::launch_attn_decode(a, static_cast<hipStream_t>(stream)));
 }
+
+AGNES_API size_t agnes_gdn_layer_prefill_workspace_size(int num_seqs, int64_t total_tokens, int num_k_heads,
+                                                       int num_v_heads, int head_dim) {
+  if (num_seqs < 0 || total_tokens < 0 || num_k_heads <= 0 || num_v_heads <= 0 || head_dim != kHeadDim ||
+      num_v_heads % num_k_heads)
+    return 0;
+  return agnes::layer_prefill_workspace(num_seqs, total_tokens, num_k_heads, num_v_heads);
+}
+
+AGNES_API int agnes_gdn_layer_prefill(const void* x, int64_t x_token_stride, agnes_dtype dtype,
+                                      const void* conv_weight, const void* conv_bias, void* conv_state,
+                                      const float* g, const float* beta, const int32_t* cu_seqlens, int num_seqs,
+                                      int64_t total_tokens, int num_k_heads, int num_v_heads, int head_dim,
+                                      float scale, float l2norm_eps, const float* initial_state, float* final_state,
+                                      const void* z, int64_t z_token_stride, const void* norm_weight, float norm_eps,
+                                      void* y, void* o, agnes_dtype out_dtype, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return AGNES_ERR_INVALID_ARG;
+  if (num_seqs < 0 || total_tokens < 0 || num_k_heads <= 0 || num_v_heads <= 0) return AGNES_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim || num_v_heads % num_k_heads || dtype != AGNES_BF16) return AGNES_ERR_UNSUPPORTED;
+  if (num_seqs == 0 && total_tokens != 0) return AGNES_ERR_INVALID_ARG;
+  if (num_seqs > 0 && (!cu_seqlens || !conv_weight || !norm_weight)) return AGNES_ERR_INVALID_ARG;
+  if (total_tokens > 0 && (!x || !g || !beta || !z || !y)) return AGNES_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(conv_weight, 16) || !aligned(conv_bias, 16) || !aligned(conv_state, 4) ||
+      !aligned(o, 16) || !aligned(y, 16) || !aligned(z, 16) || !aligned(norm_weight, 16) || !aligned(g, 4) ||
+      !aligned(beta, 4) || !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(cu_seqlens, 4))
+    return AGNES_ERR_INVALID_ARG;
+  const int64_t C = (int64_t)(2 * num_k_heads + num_v_heads) * head_dim;
+  const int64_t rowo = (int64_t)num_v_heads * head_dim;
+  if (x_token_stride < C || x_token_stride % 8 || z_token_stride < rowo || z_token_stride % 8)
+    return AGNES_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(l2norm_eps >= 0.f) || !std::isfinite(l2norm_eps) || !(norm_eps >= 0.f) ||
+      !std::isfinite(norm_eps))
+    return AGNES_ERR_INVALID_ARG;
+  if ((int64_t)num_seqs * num_v_heads * 8 > INT32_MAX || (int64_t)num_seqs > 65535) return AGNES_ERR_UNSUPPORTED;
+  const int64_t sbytes = (int64_t)num_seqs * num_v_heads * head_dim * head_dim;
+  const Span s0 = span(initial_state, 1, 0, sbytes, 4), s1 = span(final_state, 1, 0, sbytes, 4);
+  if (initial_state && final_state && initial_state != final_state && overlap(s0, s1)) return AGNES_ERR_INVALID_ARG;
+  const Span os = span(o, o ? total_tokens : 0, rowo, rowo, esize(out_dtype));
+  const Span ys = span(y, total_tokens, rowo, rowo, esize(out_dtype));
+  const Span xs = span(x, total_tokens, x_token_stride, C, 2);
+  const Span zs = span(z, total_tokens, z_token_stride, rowo, 2);
+  const Span cs = span(conv_state, conv_state ? 1 : 0, 0, (int64_t)num_seqs * C * 3, 2);
+  const Span ws_span = span(workspace, workspace ? 1 : 0, 0, (int64_t)workspace_bytes, 1);
+  const Span outs[5] = {os, ys, cs, s1, ws_span};
+  const Span ins[4] = {xs, zs, s0, span(norm_weight, 1, 0, head_dim, 2)};
+  for (int i = 0; i < 5; ++i) {
+    for (const Span& in : ins)
+      if (overlap(outs[i], in) && !(i == 3 && in.lo == s0.lo && initial_state == final_state)) return AGNES_ERR_INVALID_ARG;
+    for (int k = i + 1; k < 5; ++k)
+      if (overlap(outs[i], outs[k])) return AGNES_ERR_INVALID_ARG;
+  }
+  const size_t need = agnes::layer_prefill_workspace(num_seqs, total_tokens, num_k_heads, num_v_heads);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return AGNES_ERR_WORKSPACE;
+
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  agnes::PrefillArgs a{xb, xb + (int64_t)num_k_heads * head_dim, xb + (int64_t)2 * num_k_heads * head_dim,
+                       (int)AGNES_BF16, x_token_stride, x_token_stride, g, beta, cu_seqlens, num_seqs, total_tokens,
+                       num_k_heads, num_v_heads, scale, initial_state, final_state, o, (int)out_dtype, workspace,
+                       workspace_bytes, conv_weight, conv_bias, conv_state, l2norm_eps};
+  a.z = z;
+  a.z_stride = z_token_stride;
+  a.norm_w = norm_weight;
+  a.norm_eps = norm_eps;
+  a.y = y;
+  return hip_status(agnes::launch_layer_prefill(a, static_cast<hipStream_t>(stream)));
+}

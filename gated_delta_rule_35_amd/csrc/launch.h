@@ -53,6 +53,13 @@ struct PrefillArgs {
   const void* conv_b;     // [(2 hk + hv) * 128] bf16 or nullptr
   void* conv_hist;        // [num_seqs, (2 hk + hv) * 128, 3] bf16 or nullptr (zeros); advanced after the call
   float l2_eps;
+  // Gated RMSNorm epilogue (whole-layer call; nullptr otherwise): y = rmsnorm(o) * w * silu(z)
+  // per 128-value head row, in the o dtype; o itself is then optional.
+  const void* z;          // [total, hv, 128] bf16, token stride z_stride
+  int64_t z_stride;
+  const void* norm_w;     // [128] bf16
+  float norm_eps;
+  void* y;                // [total, hv, 128] contiguous
 };
 
 struct DecodeArgs {
@@ -156,6 +163,10 @@ hipError_t launch_conv_history(const ConvArgs& a, hipStream_t s);  // final hist
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t s);
 size_t prefill_mfma_workspace(int num_seqs, int64_t total, int hk, int hv);
+// Whole-layer prefill (conv + recurrence + gated RMSNorm): the scan workgroups of one value head
+// exchange per-token partial sums, so every workgroup of the grid must be resident at once
+size_t layer_prefill_workspace(int num_seqs, int64_t total, int hk, int hv);
+hipError_t launch_layer_prefill(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_gated_rmsnorm(const NormArgs& a, hipStream_t s);
 hipError_t launch_decode_fused(const FusedDecodeArgs& a, hipStream_t s);

@@ -68,6 +68,9 @@ constexpr int NPAIR = NVT / TPW;  // chain waves (and as many output waves) per 
 constexpr int NCP = 6;       // copy waves
 constexpr int NWAVES = 2 * NPAIR + NCP;  // chain waves, output waves, copy waves
 constexpr int DVB = 16 * NVT;
+constexpr int NRG = 2 * TPW;  // rows of the output tile one output-wave lane holds (one per pass)
+constexpr int RING = 8;      // whole-layer call: chunk slots of the partial-sum exchange
+static_assert(RING >= 4 && (RING & (RING - 1)) == 0, "exchange ring: no slot reused before it is read");
 constexpr int NB = D / DVB;  // scan workgroups per value head
 constexpr int LDV = DVB + 8; // bf16 row stride of the staged V slice
 constexpr int VR_ROWS = 80;  // raw x rows of a V slice (fused): 3 halo + 64, to 5 x 1 KiB copies
@@ -96,10 +99,17 @@ constexpr int QK_BYTES = sizeof(QKImage);
 // Workspace: [chunk offsets (N+1) int32, 256-aligned] [records: Hv x maxch] [q/k images: Hk x maxch]
 struct WsLayout {
   size_t rec, qk, bytes;
+  // whole-layer call only: per (sequence, value head) RING chunk slots, each with one 64-bit
+  // (chunk tag, partial sum of squares) word per output row and workgroup of the head; then
+  // the workgroup ticket counter.  Both are zeroed by prep.
+  size_t ring, tick, layer_bytes;
   __host__ __device__ WsLayout(int num_seqs, int hv, int hk, int64_t maxch) {
     rec = (4 * (size_t)(num_seqs + 1) + 255) & ~size_t(255);
     qk = rec + (size_t)hv * (size_t)maxch * mp::REC_BYTES;
     bytes = qk + (size_t)hk * (size_t)maxch * mp::QK_BYTES;
+    ring = (bytes + 255) & ~size_t(255);
+    tick = ring + (size_t)num_seqs * hv * mp::RING * mp::NB * mp::C * 8;
+    layer_bytes = tick + 256;
   }
 };
 
@@ -284,6 +294,12 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
   const int rd = (int)(lid % rounds);
   const int j = (int)((lid / rounds) % (unsigned)maxch);
   const int kh = (int)(lid / (rounds * (unsigned)maxch));
+  if (a.y) {  // whole-layer call: no partial sum published yet (tag 0 matches no chunk), no ticket taken
+    uint4* r = reinterpret_cast<uint4*>(base + ws.ring);
+    const size_t n16 = (ws.layer_bytes - ws.ring) / 16;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)nblk * blockDim.x)
+      r[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
   if (j >= off[a.num_seqs]) return;
   const int n = seq_of_chunk(off, a.num_seqs, j);
   const int64_t start = cu_at(a.cu, n, a.total);
@@ -553,6 +569,8 @@ struct ScanSmem {
   ExBuf X[2];                        // by chunk parity
   uint16_t Vr[2][mp::VR_ROWS][mp::DVB];  // fused prologue: raw x rows of the V slice, by chunk parity
   int ks_done[mp::NPAIR];            // c + 1 once chain wave p's K S^T of chunk c is done
+  int os_ready;                      // whole-layer call: c + 1 once chunk c's output tile is in Os
+  unsigned ticket;                   // whole-layer call: this workgroup's place in start order
 };
 static_assert(sizeof(ScanSmem) <= 160 * 1024, "scan LDS");
 
@@ -799,8 +817,8 @@ __device__ __forceinline__ void qs_step(const ScanBuf& B, const ExBuf& exS, int 
 // Output wave, part 2 (the chunk c of part 1, one iteration later): O = diag(exp gamma) Q S^T
 // + P U for its tiles, staged in their columns of Os by this wave and written out from there
 // (rows < L, 2 TPW lanes per row, eight values each).
-template <int O_DT>
-__device__ __forceinline__ void o_step(const ExBuf& exU, float (*Os)[mp::DVB + 4], const PrefillArgs& a,
+template <int O_DT, bool STAGE>
+__device__ __forceinline__ void o_step(const ExBuf& exU, float (*Os)[mp::DVB + 4], int* os_ready, const PrefillArgs& a,
                                        const Geo& G, int c, int t0, const f4 (&qs)[mp::TPW][4], const h8 (&pa)[6],
                                        const float (&gg)[16]) {
   using namespace mp;
@@ -833,6 +851,14 @@ __device__ __forceinline__ void o_step(const ExBuf& exU, float (*Os)[mp::DVB + 4
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) Os[16 * i + 4 * lg + e][16 * (t0 + t) + ln] = a.scale * o[t][i][e];
+  if constexpr (STAGE) {
+    // hand the tile to the tile waves, which write it out: the wave's LDS writes are complete
+    // before the flag is raised, and the tile is not rewritten before the next barrier
+    static_assert(NPAIR == 1, "one output wave stages the whole tile");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    if (lane == 0) __hip_atomic_store(os_ready, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return;
+  }
   // Os is written and read back by this wave only: LDS keeps a wave's accesses in order.
   constexpr int LPR = 2 * TPW, RPP = 64 / LPR;  // lanes per row, rows per pass
   const int L = G.len(c);
@@ -855,23 +881,235 @@ __device__ __forceinline__ void o_step(const ExBuf& exU, float (*Os)[mp::DVB + 4
   }
 }
 
+// ---- tile waves (fused path): the output wave only stages its [64 x DVB] output tile in Os
+// and raises os_ready; the first NTW copy waves issue no copies and write the tile out.  They
+// are the only waves that store rows, and they load nothing while stores are in flight, so no
+// wait on the copies ever waits on a store.  Prefill call: one tile wave writes o.  Whole-layer
+// call: two tile waves (32 rows each) also run the gated RMSNorm y = o / sqrt(mean(o^2) + eps)
+// * w * silu(z), whose 128 values per row are spread over the NB workgroups of the value head.
+//
+// Exchange: a row's partial sum of squares over this block's DVB columns travels with its chunk
+// tag in one 64-bit word, written and read as a relaxed atomic at agent scope: a reader that
+// sees the tag sees the sum stored with it, so no fence (on this chip, a write-back or
+// invalidation of a whole L2) is needed.  Chunk c uses slot c mod RING.  In step c a tile wave
+// (1) waits for the words of chunk c - 3 (loaded at the end of step c - 1, reloaded while a tag
+// is older) and writes y of chunk c - 3; (2) takes chunk c - 1 from Os and publishes its sums;
+// (3) loads the words and gates of chunk c - 2.  Chunk k is published in step k + 1 and read in
+// steps k + 2 .. k + 3; slot k is next written (chunk k + RING) in step k + RING + 1, after the
+// writer's wait for chunk k + RING - 2, which every reader publishes in step k + RING - 1 after
+// its own read of chunk k (step k + 3): RING >= 4 suffices.  Every wait ends (the workgroups
+// take their roles in start order, see the kernel); the bound only keeps a lost word from
+// hanging the GPU.
+namespace mp {
+template <bool NORM> constexpr int ntw() { return NORM ? 2 : 1; }  // tile waves
+constexpr int TLPR = DVB / 8;           // lanes per row piece (8 values each)
+constexpr int TRPP = 64 / TLPR;         // rows per pass of a tile wave
+static_assert(TLPR == 4 && TRPP == 16, "tile-wave lane layout");
+}  // namespace mp
+
+struct NormCtx {
+  unsigned long long* ring;  // this (sequence, value head): [RING][NB][64] tagged words
+  int blk;                   // this block
+  int r0;                    // first row of this tile wave
+  float w[8];                // norm weights of the lane's 8 columns
+};
+
+// The lane's pieces of rows r0 + 16 g + lane / 4 (g < NG) of the staged tile, columns
+// 8 (lane % 4) .. + 7.
+template <int NG>
+__device__ __forceinline__ void tile_take(const float (*Os)[mp::DVB + 4], int r0, int lane, float (&x)[NG][8]) {
+  const int col = 8 * (lane % mp::TLPR);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int r = r0 + mp::TRPP * g + lane / mp::TLPR;
+    const f4 a0 = *reinterpret_cast<const f4*>(&Os[r][col]);
+    const f4 a1 = *reinterpret_cast<const f4*>(&Os[r][col + 4]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[g][e] = a0[e];
+      x[g][e + 4] = a1[e];
+    }
+  }
+}
+
+template <int O_DT, int NG>
+__device__ __forceinline__ void tile_store(void* dst, const PrefillArgs& a, const Geo& G, int c, int r0, int lane,
+                                           const float (&x)[NG][8]) {
+  const int L = G.len(c), col = 8 * (lane % mp::TLPR);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int r = r0 + mp::TRPP * g + lane / mp::TLPR;
+    if (r < L) store8<O_DT>(dst, ((G.start + (int64_t)c * mp::C + r) * a.hv + G.h) * (int64_t)mp::D + G.dv0 + col, x[g]);
+  }
+}
+
+__device__ __forceinline__ unsigned long long* ring_word(const NormCtx& nc_, int c, int b, int r) {
+  return nc_.ring + ((c & (mp::RING - 1)) * mp::NB + b) * mp::C + r;
+}
+
+// Partial sums of squares of the lane's rows over this block's columns (every lane of a row
+// gets the row's sum).
+template <int NG>
+__device__ __forceinline__ void row_sums(const float (&x)[NG][8], float (&ss)[NG]) {
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    float s2 = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s2 += x[g][e] * x[g][e];
+#pragma unroll
+    for (int m = 1; m < mp::TLPR; m <<= 1) s2 += __shfl_xor(s2, m);
+    ss[g] = s2;
+  }
+}
+
+template <int NG>
+__device__ __forceinline__ void norm_publish(const NormCtx& nc_, int c, int lane, const float (&ss)[NG]) {
+  if (lane % mp::TLPR) return;
+#pragma unroll
+  for (int g = 0; g < NG; ++g)
+    __hip_atomic_store(ring_word(nc_, c, nc_.blk, nc_.r0 + mp::TRPP * g + lane / mp::TLPR),
+                       ((unsigned long long)__float_as_uint(ss[g]) << 32) | (unsigned)(c + 1), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Loads of chunk c for the norm: lane l takes the other blocks' words of row r0 + (l % 32)
+// (lanes l and l + 32 alike) and the gates of its own row pieces.
+template <int NG>
+struct NormIn {
+  unsigned long long w[mp::NB - 1];
+  uint4 z[NG];
+};
+
+template <int NG>
+__device__ __forceinline__ void norm_load_words(const NormCtx& nc_, int c, int lane, NormIn<NG>& g) {
+  static_assert(NG * mp::TRPP == 32, "a tile wave's rows fit half a wave");
+#pragma unroll
+  for (int i = 0; i < mp::NB - 1; ++i)
+    g.w[i] = __hip_atomic_load(ring_word(nc_, c, i + (i >= nc_.blk), nc_.r0 + (lane & 31)), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int NG>
+__device__ __forceinline__ void norm_issue(const NormCtx& nc_, const PrefillArgs& a, const Geo& G, int c, int lane,
+                                           NormIn<NG>& g) {
+  norm_load_words(nc_, c, lane, g);
+  const int L = G.len(c), col = 8 * (lane % mp::TLPR);
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    const int r = nc_.r0 + mp::TRPP * q + lane / mp::TLPR;
+    g.z[q] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.z) +
+                                             (G.start + (int64_t)c * mp::C + (r < L ? r : 0)) * a.z_stride +
+                                             (int64_t)G.h * mp::D + G.dv0 + col);
+  }
+}
+
+// Waits until every other block has published chunk c, then writes y of chunk c from the
+// lane's row pieces x, their own sums ss and the gates in g.
+template <int O_DT, int NG>
+__device__ __forceinline__ void norm_finish(const NormCtx& nc_, const PrefillArgs& a, const Geo& G, int c, int lane,
+                                            NormIn<NG>& g, const float (&x)[NG][8], const float (&ss)[NG]) {
+  for (int it = 0; it < (1 << 24); ++it) {
+    bool ok = true;
+#pragma unroll
+    for (int i = 0; i < mp::NB - 1; ++i) ok = ok && (unsigned)g.w[i] == (unsigned)(c + 1);
+    if (__all(ok)) break;
+    __builtin_amdgcn_s_sleep(1);
+    norm_load_words(nc_, c, lane, g);
+  }
+  float oth = 0.f;
+#pragma unroll
+  for (int i = 0; i < mp::NB - 1; ++i) oth += __uint_as_float((unsigned)(g.w[i] >> 32));
+  float y[NG][8];
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    const float tot = ss[q] + __shfl(oth, mp::TRPP * q + lane / mp::TLPR);
+    const float rs = rsqrt_fast(tot * (1.0f / mp::D) + a.norm_eps);
+    const uint32_t zw[4] = {g.z[q].x, g.z[q].y, g.z[q].z, g.z[q].w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float zv = __uint_as_float((e & 1) ? (zw[e >> 1] & 0xffff0000u) : (zw[e >> 1] << 16));
+      y[q][e] = x[q][e] * rs * nc_.w[e] * silu(zv);
+    }
+  }
+  tile_store<O_DT, NG>(a.y, a, G, c, nc_.r0, lane, y);
+}
+
+// A tile wave's steps (as many LDS barriers as every other wave).  qt: this tile wave.
+template <int O_DT, bool NORM>
+__device__ __forceinline__ void tile_wave(ScanSmem& sm, const PrefillArgs& a, const Geo& G, const WsLayout& wl, int n,
+                                          int nc, int qt) {
+  using namespace mp;
+  constexpr int NG = C / TRPP / ntw<NORM>();  // row passes per tile wave
+  const int lane = G.lane;
+  const int r0 = qt * (C / ntw<NORM>());
+  lds_barrier();  // the copy waves' two prologue steps
+  lds_barrier();
+  if constexpr (!NORM) {
+    for (int c = 0; c < nc + 1; ++c) {
+      if (c >= 1) {
+        wait_flag(&sm.os_ready, c);  // chunk c - 1 staged
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        float x[NG][8];
+        tile_take<NG>(sm.Os, r0, lane, x);
+        tile_store<O_DT, NG>(a.o, a, G, c - 1, r0, lane, x);
+      }
+      lds_barrier();
+    }
+  } else {
+    NormCtx nctx;
+    nctx.ring = reinterpret_cast<unsigned long long*>(static_cast<unsigned char*>(a.workspace) + wl.ring) +
+                ((int64_t)n * a.hv + G.h) * (RING * NB * C);
+    nctx.blk = G.dv0 / DVB;
+    nctx.r0 = r0;
+    load8<DT_BF16>(a.norm_w, G.dv0 + 8 * (lane % TLPR), nctx.w);
+    float xa[NG][8], xb[NG][8], sa[NG], sb[NG];  // chunks c - 3 and c - 2 at the start of step c
+    NormIn<NG> gin;
+    for (int c = 0; c < nc + 1; ++c) {
+      if (c >= 3) norm_finish<O_DT, NG>(nctx, a, G, c - 3, lane, gin, xa, sa);
+#pragma unroll
+      for (int q = 0; q < NG; ++q) {
+        sa[q] = sb[q];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xa[q][e] = xb[q][e];
+      }
+      if (c >= 1) {
+        wait_flag(&sm.os_ready, c);  // chunk c - 1 staged
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+        tile_take<NG>(sm.Os, r0, lane, xb);
+        row_sums<NG>(xb, sb);
+        norm_publish<NG>(nctx, c - 1, lane, sb);
+        if (a.o) tile_store<O_DT, NG>(a.o, a, G, c - 1, r0, lane, xb);
+      }
+      if (c >= 2) norm_issue<NG>(nctx, a, G, c - 2, lane, gin);
+      lds_barrier();
+    }
+    // chunks nc - 2 (words and gates in flight) and nc - 1
+    if (nc >= 2) norm_finish<O_DT, NG>(nctx, a, G, nc - 2, lane, gin, xa, sa);
+    if (nc >= 1) {
+      norm_issue<NG>(nctx, a, G, nc - 1, lane, gin);
+      norm_finish<O_DT, NG>(nctx, a, G, nc - 1, lane, gin, xb, sb);
+    }
+  }
+}
+
 // Copy waves: issue the direct global -> LDS loads (no registers) of chunk c into buffer
 // B[c & 1] (c < 0: none) and, for the fused prologue, of the raw x rows of chunk cv's V slice
 // into Vr[cv & 1] (cv < 0: none).  A chunk is 58 copies of 1 KiB (q/k image 34, record 19, V
-// slice 5) landing back to back in the buffer; copy wave q of NCP issues the copies u = q,
-// q + NCP, ...  The q/k image and the record are contiguous; the V slice is gathered from
+// slice 5) landing back to back in the buffer; copy wave q of NCOPY issues the copies u = q,
+// q + NCOPY, ...  The q/k image and the record are contiguous; the V slice is gathered from
 // the strided tensor into padded rows, rows past the end of the chunk re-reading its first
 // row (finite values that only ever meet beta = 0).  The raw rows of the fused path are the
 // chunk's 64 rows after a 3-row halo (x rows c0 - 3 .. c0 + 76); rows outside the sequence
 // re-read row c0 (the halo before the sequence start comes from the conv history instead).
 // Each wave issues at most about one direct copy per 100 cycles, hence several.
 // First copy index u >= base with u = q (mod NCP).
+template <int NCOPY>
 __device__ __forceinline__ int first_copy(int base, int q) {
-  const int r = (q - base) % mp::NCP;
-  return base + (r < 0 ? r + mp::NCP : r);
+  const int r = (q - base) % NCOPY;
+  return base + (r < 0 ? r + NCOPY : r);
 }
 
-template <bool FUSED>
+template <bool FUSED, int NCOPY>
 __device__ __forceinline__ void issue_chunk(ScanSmem& sm, const PrefillArgs& a, const Geo& G,
                                             const unsigned char* ws, int c, int cv, int q) {
   using namespace mp;
@@ -885,15 +1123,15 @@ __device__ __forceinline__ void issue_chunk(ScanSmem& sm, const PrefillArgs& a, 
   if (c >= 0) {
     unsigned char* dst = reinterpret_cast<unsigned char*>(&sm.B[c & 1]);
     const unsigned char* qk = ws + G.qk0 + (size_t)c * QK_BYTES + 16 * lane;
-    for (int u = q; u < NQK; u += NCP)
+    for (int u = q; u < NQK; u += NCOPY)
       __builtin_amdgcn_global_load_lds((glb_void*)(qk + 1024 * u), (lds_void*)(dst + 1024 * u), 16, 0, 0);
     const unsigned char* rec = ws + G.rec0 + (size_t)c * REC_BYTES + 16 * lane - 1024 * NQK;
-    for (int u = first_copy(NQK, q); u < NQK + NREC; u += NCP)
+    for (int u = first_copy<NCOPY>(NQK, q); u < NQK + NREC; u += NCOPY)
       __builtin_amdgcn_global_load_lds((glb_void*)(rec + 1024 * u), (lds_void*)(dst + 1024 * u), 16, 0, 0);
     if constexpr (!FUSED) {
       constexpr int VPR = LDV / 8;  // 16-byte pieces per padded V row (5)
       const int L = G.len(c);
-      for (int u = first_copy(NQK + NREC, q); u < NQK + NREC + NV; u += NCP) {
+      for (int u = first_copy<NCOPY>(NQK + NREC, q); u < NQK + NREC + NV; u += NCOPY) {
         const int j = 64 * (u - NQK - NREC) + lane, r = j / VPR, pc = j % VPR;
         const uint16_t* src = vb + (G.start + (int64_t)c * C) * a.v_stride +
                               ((r < L && pc < DVB / 8) ? (int64_t)r * a.v_stride + 8 * pc : 0);
@@ -904,7 +1142,7 @@ __device__ __forceinline__ void issue_chunk(ScanSmem& sm, const PrefillArgs& a, 
   if constexpr (FUSED) {
     if (cv >= 0) {
       const int64_t c0 = G.start + (int64_t)cv * C;
-      for (int u = first_copy(NQK + NREC, q); u < NQK + NREC + NV; u += NCP) {
+      for (int u = first_copy<NCOPY>(NQK + NREC, q); u < NQK + NREC + NV; u += NCOPY) {
         const int jv = 64 * (u - NQK - NREC) + lane, i = jv >> 2, pc = jv & 3;
         const int64_t pos = c0 - 3 + i;
         const bool in = pos >= G.start && i < 3 + G.len(cv);
@@ -955,7 +1193,7 @@ __device__ __forceinline__ void conv_vslice(ScanSmem& sm, const PrefillArgs& a, 
 // then NCP copy waves.  Iteration c (one LDS barrier each, n + 1 in all): the chain waves on
 // chunk c; the output waves finish and write out chunk c-1 and start chunk c; the copy waves
 // fill the other buffer with chunk c+1.
-template <int O_DT, bool FUSED>
+template <int O_DT, bool FUSED, bool NORM = false>
 __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, int64_t maxch) {
   using namespace mp;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -969,6 +1207,17 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
   const unsigned nblk = gridDim.x;
   unsigned lid = blockIdx.x;
   if ((nblk & 7u) == 0) lid = (blockIdx.x & 7u) * (nblk >> 3) + (blockIdx.x >> 3);
+  if constexpr (NORM) {
+    // The NB workgroups of a value head wait for each other.  Their roles follow the order in
+    // which workgroups start (a ticket), not the block index: every workgroup with a smaller
+    // ticket has started, so at most one head has members still to start and all others run
+    // to the end and free their compute units.  No residency of the whole grid is assumed.
+    if (threadIdx.x == 0)
+      sm.ticket = __hip_atomic_fetch_add(reinterpret_cast<unsigned*>(const_cast<unsigned char*>(ws) + wl.tick), 1u,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    lid = sm.ticket;
+  }
   Geo G;
   const int blk = lid % NB;
   G.h = (lid / NB) % a.hv;
@@ -989,6 +1238,8 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
   const int ln = G.ln, lg = G.lg, lane = G.lane;
   const int nc = G.nchunks;
   if (threadIdx.x < NPAIR) sm.ks_done[threadIdx.x] = 0;  // ordered before every use by the prologue barrier
+  if (threadIdx.x == 0) sm.os_ready = 0;
+  static_assert(!NORM || FUSED, "the whole-layer call is the fused one");
 
   if (G.w < NPAIR) {  // chain wave
     const int pr = NPAIR == 1 ? 0 : G.w, t0 = TPW * pr;
@@ -1040,13 +1291,21 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
       // Start once the chain wave is past K S^T: run beside it, the output wave's LDS reads
       // slow the chain's operand reads (the serial path) by about a third.
       if (c < nc) wait_flag(&sm.ks_done[pr], c + 1);
-      if (c >= 1) o_step<O_DT>(sm.X[(c - 1) & 1], sm.Os, a, G, c - 1, t0, qs, pa, ge);
+      if (c >= 1) o_step<O_DT, FUSED>(sm.X[(c - 1) & 1], sm.Os, &sm.os_ready, a, G, c - 1, t0, qs, pa, ge);
       if (c < nc) qs_step(sm.B[c & 1], sm.X[c & 1], t0, lane, ln, lg, qs, pa, ge);
       lds_barrier();
     }
   } else {  // copy wave
     const int q = __builtin_amdgcn_readfirstlane(G.w - 2 * NPAIR);  // wave-uniform: scalar copy loop
     if constexpr (FUSED) {
+      // The first NTW copy waves are tile waves; the others copy (and the conv takes four of them).
+      constexpr int NTW = ntw<NORM>(), NCOPY = NCP - NTW;
+      static_assert(NCOPY >= 4, "the conv of a V slice takes four waves");
+      if (q < NTW) {
+        tile_wave<O_DT, NORM>(sm, a, G, wl, n, nc, q);
+        return;
+      }
+      const int qc = q - NTW, qv = q - (NCP - 4);  // copy index; conv index (qv < 0: none)
       // Step c: copies of chunk c+1 and raw rows of chunk c+2 in flight while the raw rows of
       // chunk c+1 (landed during step c-1) are convolved into its V slice.
       uint4 wt[4];  // conv taps of the lane's 8 value channels, packed bf16 as stored
@@ -1059,29 +1318,29 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
 #pragma unroll
         for (int e = 0; e < 8; ++e) bs[e] = 0.f;
       }
-      if (nc > 0) issue_chunk<true>(sm, a, G, ws, 0, 0, q);
-      if (nc > 1) issue_chunk<true>(sm, a, G, ws, -1, 1, q);
+      if (nc > 0) issue_chunk<true, NCOPY>(sm, a, G, ws, 0, 0, qc);
+      if (nc > 1) issue_chunk<true, NCOPY>(sm, a, G, ws, -1, 1, qc);
       __builtin_amdgcn_s_waitcnt(0);
       lds_barrier();  // raw rows of chunk 0 visible to every copy wave
-      if (nc > 0) conv_vslice(sm, a, G, n, 0, q, wt, bs);
+      if (nc > 0 && qv >= 0) conv_vslice(sm, a, G, n, 0, qv, wt, bs);
       lds_barrier();
       for (int c = 0; c < nc + 1; ++c) {
         if (c + 1 < nc) {
-          issue_chunk<true>(sm, a, G, ws, c + 1, c + 2 < nc ? c + 2 : -1, q);
-          conv_vslice(sm, a, G, n, c + 1, q, wt, bs);
+          issue_chunk<true, NCOPY>(sm, a, G, ws, c + 1, c + 2 < nc ? c + 2 : -1, qc);
+          if (qv >= 0) conv_vslice(sm, a, G, n, c + 1, qv, wt, bs);
           __builtin_amdgcn_s_waitcnt(0);
         }
         lds_barrier();
       }
     } else {
       if (nc > 0) {
-        issue_chunk<false>(sm, a, G, ws, 0, -1, q);
+        issue_chunk<false, NCP>(sm, a, G, ws, 0, -1, q);
         __builtin_amdgcn_s_waitcnt(0);
       }
       lds_barrier();
       for (int c = 0; c < nc + 1; ++c) {
         if (c + 1 < nc) {
-          issue_chunk<false>(sm, a, G, ws, c + 1, -1, q);
+          issue_chunk<false, NCP>(sm, a, G, ws, c + 1, -1, q);
           __builtin_amdgcn_s_waitcnt(0);
         }
         lds_barrier();
@@ -1096,10 +1355,22 @@ size_t prefill_mfma_workspace(int num_seqs, int64_t total, int hk, int hv) {
   return WsLayout(num_seqs, hv, hk, max_chunks(total, num_seqs)).bytes;
 }
 
-template <int O_DT, bool FUSED>
-static hipError_t launch_o(const PrefillArgs& a, hipStream_t st) {
+size_t layer_prefill_workspace(int num_seqs, int64_t total, int hk, int hv) {
+  if (num_seqs <= 0) return 0;
+  return WsLayout(num_seqs, hv, hk, max_chunks(total, num_seqs)).layer_bytes;
+}
+
+template <int O_DT, bool FUSED, bool NORM>
+static hipError_t scan_attr() {
+  static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan_kernel<O_DT, FUSED, NORM>),
+                                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)sizeof(ScanSmem));
+  return e;
+}
+
+template <int O_DT, bool FUSED, bool NORM>
+static hipError_t launch_o(PrefillArgs a, hipStream_t st) {
   if (a.num_seqs == 0) return hipSuccess;
-  const int64_t maxch = max_chunks(a.total, a.num_seqs);
+  int64_t maxch = max_chunks(a.total, a.num_seqs);
   hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(256), 0, st, a.cu, a.num_seqs, a.total,
                      static_cast<int32_t*>(a.workspace));
   hipError_t e = hipGetLastError();
@@ -1112,12 +1383,10 @@ static hipError_t launch_o(const PrefillArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   const size_t smem = sizeof(ScanSmem);
-  auto k = scan_kernel<O_DT, FUSED>;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL(k, dim3((unsigned)((int64_t)a.num_seqs * a.hv * mp::NB)), dim3(64 * mp::NWAVES), smem, st, a,
-                     maxch);
+  e = scan_attr<O_DT, FUSED, NORM>();
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((int64_t)a.num_seqs * a.hv * mp::NB)), block(64 * mp::NWAVES);
+  hipLaunchKernelGGL((scan_kernel<O_DT, FUSED, NORM>), grid, block, smem, st, a, maxch);
   e = hipGetLastError();
   if (e != hipSuccess || !FUSED || !a.conv_hist) return e;
   // advance the conv history once every read of the old one (prep, scan) is done
@@ -1126,9 +1395,14 @@ static hipError_t launch_o(const PrefillArgs& a, hipStream_t st) {
   return launch_conv_history(h, st);
 }
 
+hipError_t launch_layer_prefill(const PrefillArgs& a, hipStream_t st) {
+  return a.o_dtype == DT_BF16 ? launch_o<DT_BF16, true, true>(a, st) : launch_o<DT_F32, true, true>(a, st);
+}
+
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st) {
-  if (a.conv_w) return a.o_dtype == DT_BF16 ? launch_o<DT_BF16, true>(a, st) : launch_o<DT_F32, true>(a, st);
-  return a.o_dtype == DT_BF16 ? launch_o<DT_BF16, false>(a, st) : launch_o<DT_F32, false>(a, st);
+  if (a.conv_w)
+    return a.o_dtype == DT_BF16 ? launch_o<DT_BF16, true, false>(a, st) : launch_o<DT_F32, true, false>(a, st);
+  return a.o_dtype == DT_BF16 ? launch_o<DT_BF16, false, false>(a, st) : launch_o<DT_F32, false, false>(a, st);
 }
 
 }  // namespace agnes

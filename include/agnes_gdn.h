@@ -254,6 +254,45 @@ int agnes_gdn_decode_fused(const void* x, int64_t x_token_stride, agnes_dtype dt
 
 /* Human-readable name of an agnes_status value (static string). */
 /*
+ * agnes_gdn_layer_prefill_workspace_size — bytes of device workspace
+ * agnes_gdn_layer_prefill needs (0 for an empty batch or arguments outside the
+ * supported set).
+ */
+size_t agnes_gdn_layer_prefill_workspace_size(int num_seqs, int64_t total_tokens, int num_k_heads,
+                                              int num_v_heads, int head_dim);
+
+/*
+ * agnes_gdn_layer_prefill — the whole delta-rule layer in prefill mode: the
+ * causal conv + SiLU + L2 of q, k, the chunked gated delta rule and the gated
+ * RMSNorm (model card "Agnes-3.0-Flash Preview", 架构 table, delta-rule row:
+ * conv in front, gated RMS-norm behind; discosf article, section 二.1: chunked
+ * prefill, chunk 64), with the recurrence output normalised inside the prefill:
+ * o need not go to memory.
+ *
+ *   x ... final_state   as agnes_gdn_prefill_fused
+ *   z             bf16 [total_tokens, num_v_heads, head_dim], row stride z_token_stride
+ *   norm_weight   bf16 [head_dim];  norm_eps as agnes_gdn_gated_rmsnorm
+ *   y             [total_tokens, num_v_heads, head_dim] contiguous, out_dtype:
+ *                 y = o / sqrt(mean(o^2) + norm_eps) * w * silu(z) per head row
+ *   o             the same shape and out_dtype, or NULL (not written)
+ *   workspace     >= agnes_gdn_layer_prefill_workspace_size() bytes, 256-byte aligned
+ *
+ * The four workgroups that share a value head exchange per-token partial sums
+ * of squares through the workspace; they take their roles in the order they
+ * start, so any batch size runs (no co-residency of the grid is assumed).
+ * Errors as agnes_gdn_prefill_fused; the workspace is cleared by the call.
+ */
+int agnes_gdn_layer_prefill(const void* x, int64_t x_token_stride, agnes_dtype dtype,
+                            const void* conv_weight, const void* conv_bias, void* conv_state,
+                            const float* g, const float* beta, const int32_t* cu_seqlens,
+                            int num_seqs, int64_t total_tokens, int num_k_heads, int num_v_heads,
+                            int head_dim, float scale, float l2norm_eps,
+                            const float* initial_state, float* final_state, const void* z,
+                            int64_t z_token_stride, const void* norm_weight, float norm_eps,
+                            void* y, void* o, agnes_dtype out_dtype, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * agnes_attn_prefill_workspace_size — bytes of device workspace agnes_attn_prefill
  * needs (0 for an empty batch).
  */

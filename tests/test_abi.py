@@ -210,6 +210,39 @@ def test_prefill_fused_checks(lib):
     assert lib.agnes_gdn_last_hip_error() == 0
 
 
+def layer(lib, **kw):
+    a = dict(x=P[0], xs=10 * 128, dt=BF16, w=P[1], b=None, cs=None, g=P[3], be=P[4], cu=P[5], n=1, T=64, hk=2, hv=6,
+             hd=128, sc=1.0, eps=1e-6, s0=None, s1=P[7], z=P[2], zs=6 * 128, nw=P[6], neps=1e-6, y=P[8], o=None,
+             odt=BF16, ws=None, wsb=0)
+    a.update(kw)
+    return lib.agnes_gdn_layer_prefill(a["x"], a["xs"], a["dt"], a["w"], a["b"], a["cs"], a["g"], a["be"], a["cu"],
+                                       a["n"], a["T"], a["hk"], a["hv"], a["hd"], a["sc"], a["eps"], a["s0"], a["s1"],
+                                       a["z"], a["zs"], a["nw"], a["neps"], a["y"], a["o"], a["odt"], a["ws"],
+                                       a["wsb"], None)
+
+
+def test_layer_prefill_checks(lib):
+    assert layer(lib, dt=F32) == UNS                    # bf16 x only
+    assert layer(lib, hd=64) == UNS
+    assert layer(lib, z=None) == INV
+    assert layer(lib, y=None) == INV
+    assert layer(lib, nw=None) == INV
+    assert layer(lib, zs=6 * 128 - 8) == INV            # z stride below a token's heads
+    assert layer(lib, zs=6 * 128 + 4) == INV            # z rows must stay 16-byte aligned
+    assert layer(lib, neps=-1.0) == INV
+    assert layer(lib, neps=float("nan")) == INV
+    assert layer(lib, y=P[2] + 256) == INV              # y overlaps z
+    assert layer(lib, o=P[8] + 512) == INV              # o overlaps y
+    assert layer(lib, y=P[0] + 64) == INV               # y overlaps x
+    assert layer(lib, n=0) == INV
+    need = lib.agnes_gdn_layer_prefill_workspace_size(1, 64, 2, 6, 128)
+    assert need >= lib.agnes_gdn_prefill_workspace_size(1, 64, 2, 6, 128, BF16)
+    assert layer(lib) == WS
+    assert layer(lib, ws=P[9], wsb=need - 1) == WS
+    assert lib.agnes_gdn_layer_prefill_workspace_size(1, 64, 2, 5, 128) == 0
+    assert lib.agnes_gdn_last_hip_error() == 0
+
+
 def attn(lib, **kw):
     T, hq, hkv = 100, 24, 4
     a = dict(q=P[0], qs=hq * 256, k=P[1], ks=hkv * 256, v=P[2], vs=hkv * 256, g=P[3], gs=hq * 256, qw=P[4], kw=P[4] + 512,

@@ -1,0 +1,177 @@
+"""GPU parity of agnes_gdn_layer_prefill (conv + SiLU + L2(q, k), the chunked delta rule and the
+gated RMS-norm in one call) against the fp64 oracle of the same composition, with nothing
+rounded between the steps.
+
+Tolerances: the recurrence output carries the chunked prefill's error (matrix-core operands in
+fp16, rel-L2 2e-3 on fp32 outputs); the norm divides each row by its own RMS, which the same
+relative error enters once more, so y is gated at rel-L2 3e-3.  Against the two-call path
+(agnes_gdn_prefill_fused then agnes_gdn_gated_rmsnorm) the recurrence output is the same
+arithmetic and must agree bit for bit; y then differs only by the order of the 128-term sum of
+squares and the reciprocal square root (a few fp32 ulps), gated at 1e-5 elementwise relative.
+A bf16 y is the round-to-nearest-even of the fp32 y of the same inputs, bit for bit.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from synth import f32_to_bf16_bits, make_config, LAYER
+from tests.helpers import dev, host, rel_l2, as_f64
+
+torch = pytest.importorskip("torch")
+import gated_delta_rule_35_amd as gdn  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+TOL_Y = 3e-3
+
+
+def _case(rng, lens, hk, hv, hist=True, init=True):
+    T = int(sum(lens))
+    C = (2 * hk + hv) * D
+    f = np.float32
+    return dict(
+        x=f32_to_bf16_bits(rng.standard_normal((T, C)).astype(f) * f(1.43)),
+        w=f32_to_bf16_bits(rng.uniform(-0.5, 0.5, (C, 4)).astype(f)),
+        cs=f32_to_bf16_bits(rng.standard_normal((len(lens), C, 3)).astype(f) * f(1.43)) if hist else None,
+        g=(-0.05 * np.logaddexp(0, rng.standard_normal((T, hv)))).astype(f),
+        beta=(1 / (1 + np.exp(-rng.standard_normal((T, hv))))).astype(f),
+        s0=(rng.standard_normal((len(lens), hv, D, D)) * 0.01).astype(f) if init else None,
+        z=f32_to_bf16_bits(rng.standard_normal((T, hv, D)).astype(f)),
+        nw=f32_to_bf16_bits((1 + 0.1 * rng.standard_normal(D)).astype(f)),
+        cu=np.concatenate([[0], np.cumsum(lens)]).astype(np.int32),
+        hk=hk, hv=hv,
+    )
+
+
+def _layer(d, out_dtype=torch.float32, want_o=False, z_pad=0):
+    T, hv = d["g"].shape
+    cs = None if d["cs"] is None else dev(d["cs"])
+    if z_pad:  # z as a view with a wider token stride
+        zb = torch.zeros((T, hv * D + z_pad), dtype=torch.bfloat16, device="cuda")
+        zb[:, :hv * D] = dev(d["z"]).view(T, hv * D)
+        z = zb[:, :hv * D].view(T, hv, D)
+    else:
+        z = dev(d["z"])
+    o = torch.empty((T, hv, D), dtype=out_dtype, device="cuda") if want_o else None
+    y, fin = gdn.layer_prefill(dev(d["x"]), dev(d["w"]), dev(d["g"]), dev(d["beta"]), dev(d["cu"]), z, dev(d["nw"]),
+                               num_k_heads=d["hk"], conv_state=cs,
+                               initial_state=None if d["s0"] is None else dev(d["s0"]), o=o, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    return host(y), host(fin), (None if cs is None else host(cs)), (None if o is None else host(o))
+
+
+def _two_calls(d, out_dtype=torch.float32):
+    cs = None if d["cs"] is None else dev(d["cs"])
+    o, fin = gdn.prefill_fused(dev(d["x"]), dev(d["w"]), dev(d["g"]), dev(d["beta"]), dev(d["cu"]),
+                               num_k_heads=d["hk"], conv_state=cs,
+                               initial_state=None if d["s0"] is None else dev(d["s0"]), o_dtype=out_dtype)
+    y = gdn.gated_rmsnorm(o, dev(d["z"]), dev(d["nw"]))
+    torch.cuda.synchronize()
+    return host(y), host(fin), host(o)
+
+
+def _oracle(d):
+    ro, rcs, rfin = oracle.prefill_conv_recurrence(d["x"], d["w"], d["cu"], d["cs"], d["g"], d["beta"], d["s0"],
+                                                   d["hk"], d["hv"])
+    return oracle.gated_rmsnorm(ro, d["z"], d["nw"]), ro, rcs, rfin
+
+
+def _first128(y, ry, cu):
+    rows = np.concatenate([np.arange(a, min(b, a + 128)) for a, b in zip(cu[:-1], cu[1:])])
+    return rel_l2(y[rows], ry[rows])
+
+
+@pytest.mark.parametrize("hist,init,z_pad", [(True, True, 0), (False, False, 64)])
+def test_layer_prefill_varlen(hist, init, z_pad):
+    """Ragged sequences in one grid: 1 and 2 tokens, an empty one, an exact chunk, partial chunks
+    and several chunks; the norm's partial sums cross the value head's four workgroups at every
+    chunk, ragged tails included."""
+    rng = np.random.default_rng(600 + 2 * hist + init)
+    lens = [70, 1, 0, 131, 64, 2, 200]
+    d = _case(rng, lens, 2, 6, hist, init)
+    y, fin, cs, o = _layer(d, want_o=True, z_pad=z_pad)
+    ry, ro, rcs, rfin = _oracle(d)
+    ey, ef, eo, ew = rel_l2(y, ry), rel_l2(fin, rfin), rel_l2(o, ro), _first128(y, ry, d["cu"])
+    print(f"layer prefill varlen: y {ey:.3e} o {eo:.3e} state {ef:.3e} first-128 {ew:.3e}")
+    assert ey <= TOL_Y and ew <= TOL_Y and eo <= 2e-3 and ef <= 2e-3
+    if cs is not None:
+        np.testing.assert_array_equal(as_f64(cs), rcs)
+
+
+def test_layer_prefill_equals_two_calls():
+    """Same inputs through agnes_gdn_prefill_fused + agnes_gdn_gated_rmsnorm: identical o and final
+    state, y within a few fp32 ulps."""
+    rng = np.random.default_rng(610)
+    d = _case(rng, [100, 64, 9, 300], 2, 6)
+    y1, f1, cs1, o1 = _layer(d, want_o=True)
+    y2, f2, o2 = _two_calls(d)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(f1, f2)
+    rel = np.abs(y1 - y2) / np.maximum(np.abs(y2), 1e-30)
+    print(f"layer prefill vs two calls: max rel diff of y {rel.max():.3e}")
+    assert float(rel.max()) <= 1e-5
+
+
+def test_layer_prefill_bf16_outputs_are_rne_of_fp32_outputs():
+    rng = np.random.default_rng(620)
+    d = _case(rng, [150, 37], 1, 3)
+    y32, f32_, _, o32 = _layer(d, want_o=True)
+    y16, f16_, _, o16 = _layer(d, torch.bfloat16, want_o=True)
+    np.testing.assert_array_equal(y16, f32_to_bf16_bits(y32))
+    np.testing.assert_array_equal(o16, f32_to_bf16_bits(o32))
+    np.testing.assert_array_equal(f16_, f32_)
+
+
+def test_layer_prefill_grid_larger_than_the_chip():
+    """Three sequences of the 48-value-head layer need 576 workgroups, more than the chip holds at
+    once: heads whose workgroups start late wait for earlier ones to finish, and every row still
+    gets its four partial sums (a late partner, a ragged tail, a one-token sequence)."""
+    rng = np.random.default_rng(630)
+    d = _case(rng, [70, 5, 1], LAYER["num_k_heads"], LAYER["num_v_heads"])
+    y, fin, cs, _ = _layer(d)
+    ry, _, rcs, rfin = _oracle(d)
+    ey, ef = rel_l2(y, ry), rel_l2(fin, rfin)
+    print(f"layer prefill, 576 workgroups: y {ey:.3e} state {ef:.3e}")
+    assert ey <= TOL_Y and ef <= 2e-3
+    np.testing.assert_array_equal(as_f64(cs), rcs)
+
+
+def test_layer_prefill_repeated_calls_reuse_the_workspace():
+    """The same workspace twice in a row (the exchange words and the ticket counter of the first
+    call are cleared by the second) and a different batch in between."""
+    rng = np.random.default_rng(640)
+    d1 = _case(rng, [130, 64], 2, 6)
+    d2 = _case(rng, [7, 200, 3], 2, 6)
+    ws = torch.empty(gdn.layer_prefill_workspace_size(3, 210, 2, 6), dtype=torch.uint8, device="cuda")
+    outs = []
+    for d in (d1, d2, d1):
+        T = d["g"].shape[0]
+        y, _ = gdn.layer_prefill(dev(d["x"]), dev(d["w"]), dev(d["g"]), dev(d["beta"]), dev(d["cu"]), dev(d["z"]),
+                                 dev(d["nw"]), num_k_heads=2, conv_state=dev(d["cs"]), initial_state=dev(d["s0"]),
+                                 out_dtype=torch.float32, workspace=ws)
+        torch.cuda.synchronize()
+        outs.append(host(y))
+    np.testing.assert_array_equal(outs[0], outs[2])
+    ry, _, _, _ = _oracle(d2)
+    assert rel_l2(outs[1], ry) <= TOL_Y
+
+
+def test_layer_prefill_full_layer_t8192():
+    """The layer's prefill workload (T = 8192, 16 key / 48 value heads, bf16 projection x, gate z
+    and norm weight of the chain workload); the oracle follows value heads 0, 1, 2, 23, 46, 47."""
+    cfg = make_config(1)
+    T, HK, HV = 8192, LAYER["num_k_heads"], LAYER["num_v_heads"]
+    cu = cfg["cu_seqlens"]
+    y, fin = gdn.layer_prefill(dev(cfg["x"]), dev(cfg["conv_w"]), dev(cfg["g"]), dev(cfg["beta"]), dev(cu),
+                               dev(cfg["z"]), dev(cfg["norm_w"]), num_k_heads=HK, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    y, fin = host(y), host(fin)
+    heads = [0, 1, 2, 23, 46, 47]
+    u, _ = oracle.causal_conv(cfg["x"], cfg["conv_w"], cu, None, l2_heads=2 * HK)
+    q, k, v = u[:, :HK * D].reshape(T, HK, D), u[:, HK * D:2 * HK * D].reshape(T, HK, D), u[:, 2 * HK * D:].reshape(T, HV, D)
+    ro, rf = oracle.recurrence(q, k, v, cfg["g"], cfg["beta"], cu, heads=heads)
+    ry = oracle.gated_rmsnorm(ro[:, heads], cfg["z"][:, heads], cfg["norm_w"])
+    ey, ef = rel_l2(y[:, heads], ry), rel_l2(fin[:, heads], rf[:, heads])
+    print(f"layer prefill T=8192 rel-L2 y={ey:.3e} state={ef:.3e}")
+    assert ey <= TOL_Y and ef <= 2e-3
