@@ -3,8 +3,9 @@
 One step = the full-layer prefill chain on T = 8192 tokens of one sequence with the layer's
 shapes (16 key / 48 value heads of 128, hidden 5120): kernel-4 causal conv + SiLU + L2 norm of
 q/k over the 10240 q|k|v channels -> chunked gated delta rule (chunk 64, fp32 state) -> gated
-RMSNorm.  `value` is tokens/s of that chain as the library runs it fastest: the conv inside the
-prefill call (agnes_gdn_prefill_fused), then the norm.  The same chain as three separate calls
+RMSNorm.  `value` is tokens/s of that chain as the library runs it fastest: the whole layer in
+one call (agnes_gdn_layer_prefill: conv, recurrence and norm, the recurrence output never
+written).  The same chain as two calls (agnes_gdn_prefill_fused, then the norm) and as three
 (conv, prefill, norm) is timed beside it.  The same run also times the batched decode step
 (256 sequences, one token each, fp32 states updated in place) and reports its state HBM GB/s,
 and the fused decode step (conv-history update + conv + L2 + recurrence + gated norm in one
@@ -43,6 +44,8 @@ FLOP_PER_TOKEN = FLOP_PER_CHUNK_GROUP * HK // CH                      # 7,602,17
 PREFILL_BYTES = T * (2 * HK * D * 2 + HV * D * 2 + HV * D * 2 + 2 * HV * 4) + HV * D * D * 4  # q,k,v,o,g,beta + final state
 # fused call: x (q|k|v channels) in, conv weights, g, beta, o out, final state
 PREFILL_FUSED_BYTES = T * (10240 * 2 + 2 * HV * 4 + HV * D * 2) + 10240 * 4 * 2 + HV * D * D * 4
+# whole-layer call: x in, conv weights, g, beta, z in, y out, norm weight, final state
+LAYER_BYTES = T * (10240 * 2 + 2 * HV * 4 + HV * D * 2 * 2) + 10240 * 4 * 2 + D * 2 + HV * D * D * 4
 CONV_BYTES = T * 10240 * 2 * 2 + 10240 * 4 * 2                        # x in, y out, weights
 NORM_BYTES = T * HV * D * 2 * 3 + D * 2                               # o, z in, y out, weight
 DECODE_B = 256
@@ -148,6 +151,7 @@ def main():
     fin = torch.empty((1, HV, D, D), dtype=torch.float32, device="cuda")
     out = torch.empty((T, HV, D), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(gdn.prefill_workspace_size(1, T, HK, HV, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    ws_l = torch.empty(gdn.layer_prefill_workspace_size(1, T, HK, HV), dtype=torch.uint8, device="cuda")
     q = y[:, :2048].view(T, HK, D)
     k = y[:, 2048:4096].view(T, HK, D)
     v = y[:, 4096:].view(T, HV, D)
@@ -175,9 +179,17 @@ def main():
         if ev is not None:
             ev[2].record()
 
+    def lstep(ev=None):  # the whole layer in one call
+        if ev is not None:
+            ev[0].record()
+        gdn.layer_prefill(x, w, g, beta, cu, z, nw, num_k_heads=HK, final_state=fin, y=out, workspace=ws_l)
+        if ev is not None:
+            ev[1].record()
+
     for _ in range(args.warmup):
         step()
         fstep()
+        lstep()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
@@ -188,14 +200,21 @@ def main():
     ms_norm = np.mean([e[2].elapsed_time(e[3]) for e in evs])
     ms_step = np.mean([e[0].elapsed_time(e[3]) for e in evs])
     fevs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
     for i in range(args.steps):
         fstep(fevs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     ms_fpre = np.mean([e[0].elapsed_time(e[1]) for e in fevs])
     ms_fnorm = np.mean([e[1].elapsed_time(e[2]) for e in fevs])
     ms_fstep = np.mean([e[0].elapsed_time(e[2]) for e in fevs])
+    # headline: K whole-layer calls, bracketed by synchronisations
+    levs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        lstep(levs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_layer = np.mean([e[0].elapsed_time(e[1]) for e in levs])
     value = T * args.steps / wall
 
     # ---- calibration copy of known size (untimed; read by the HBM counter runs)
@@ -315,7 +334,7 @@ def main():
     adec_gbs = ATTN_DEC_BYTES / (ms_adec * 1e-3) / 1e9
     del dkc, dvc
 
-    pre_tflops = FLOP_PER_TOKEN * T / (ms_fpre * 1e-3) / 1e12
+    layer_tflops = FLOP_PER_TOKEN * T / (ms_layer * 1e-3) / 1e12
     res = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -330,24 +349,29 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "delta-layer prefill chain, T=8192, 1 sequence: conv(k=4)+SiLU+L2 -> "
-                               "chunked gated delta rule (chunk 64) -> gated RMSNorm; conv and prefill in "
-                               "one call (agnes_gdn_prefill_fused)",
+                               "chunked gated delta rule (chunk 64) -> gated RMSNorm, the whole layer in "
+                               "one call (agnes_gdn_layer_prefill)",
                    "T": T, "num_k_heads": HK, "num_v_heads": HV, "head_dim": D, "chunk": CH,
                    "io_dtype": "bf16", "matrix_core_operands": "fp16", "accumulate": "fp32",
                    "state": "fp32", "parallelism": "none (1 GPU)"},
-        "kernels_ms": {"prefill_fused": round(ms_fpre, 4), "gated_rmsnorm": round(ms_fnorm, 4),
-                       "chain_events": round(ms_fstep, 4)},
+        "kernels_ms": {"layer_prefill": round(ms_layer, 4)},
+        "two_call_chain": {"prefill_fused": round(ms_fpre, 4), "gated_rmsnorm": round(ms_fnorm, 4),
+                           "chain_events": round(ms_fstep, 4), "tokens_per_s": round(T / (ms_fstep * 1e-3), 1),
+                           "prefill_fused_TFLOPs": round(FLOP_PER_TOKEN * T / (ms_fpre * 1e-3) / 1e12, 2),
+                           "prefill_fused_traffic": measured_traffic("prefill_fused"),
+                           "prefill_fused_GBps_algorithmic": round(PREFILL_FUSED_BYTES / (ms_fpre * 1e-3) / 1e9, 1)},
         "unfused_chain": {"conv": round(ms_conv, 4), "prefill_chunked": round(ms_pre, 4),
                           "gated_rmsnorm": round(ms_norm, 4), "chain_events": round(ms_step, 4),
                           "tokens_per_s": round(T / (ms_step * 1e-3), 1),
                           "prefill_chunked_TFLOPs": round(FLOP_PER_TOKEN * T / (ms_pre * 1e-3) / 1e12, 2),
                           "prefill_chunked_traffic": measured_traffic("prefill_chunked")},
         "roofline": {"bound": "mfma",
-                     "kernel": "agnes_gdn_prefill_fused call (chunk_offsets + prep + scan launches)",
-                     "achieved": round(pre_tflops, 2),
-                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(pre_tflops / MFMA_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("prefill_fused"), "flops_per_launch": FLOP_PER_TOKEN * T,
-                     "hbm_GBps_algorithmic": round(PREFILL_FUSED_BYTES / (ms_fpre * 1e-3) / 1e9, 1)},
+                     "kernel": "agnes_gdn_layer_prefill call (chunk_offsets + prep + scan launches)",
+                     "achieved": round(layer_tflops, 2),
+                     "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(layer_tflops / MFMA_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic("layer_prefill"), "flops_per_launch": FLOP_PER_TOKEN * T,
+                     "bytes_per_launch": LAYER_BYTES,
+                     "hbm_GBps_algorithmic": round(LAYER_BYTES / (ms_layer * 1e-3) / 1e9, 1)},
         "streaming_kernels": {
             "conv_GBps": round(CONV_BYTES / (ms_conv * 1e-3) / 1e9, 1),
             "gated_rmsnorm_GBps": round(NORM_BYTES / (ms_norm * 1e-3) / 1e9, 1)},

@@ -881,12 +881,12 @@ __device__ __forceinline__ void o_step(const ExBuf& exU, float (*Os)[mp::DVB + 4
   }
 }
 
-// ---- tile waves (fused path): the output wave only stages its [64 x DVB] output tile in Os
-// and raises os_ready; the first NTW copy waves issue no copies and write the tile out.  They
-// are the only waves that store rows, and they load nothing while stores are in flight, so no
-// wait on the copies ever waits on a store.  Prefill call: one tile wave writes o.  Whole-layer
-// call: two tile waves (32 rows each) also run the gated RMSNorm y = o / sqrt(mean(o^2) + eps)
-// * w * silu(z), whose 128 values per row are spread over the NB workgroups of the value head.
+// ---- whole-layer call: gated RMSNorm y = o / sqrt(mean(o^2) + eps) * w * silu(z) of the output
+// rows, whose 128 values are spread over the NB workgroups of a value head.  The output wave
+// only stages its [64 x DVB] tile in Os and raises os_ready; the first NTW copy waves (tile
+// waves, 32 rows each) issue no copies and run the norm.  They are the only waves that store
+// rows, and their loads and stores never share a wait counter with the copies: a copy wave
+// waiting for its copies never waits on a row store or an exchange load.
 //
 // Exchange: a row's partial sum of squares over this block's DVB columns travels with its chunk
 // tag in one 64-bit word, written and read as a relaxed atomic at agent scope: a reader that
@@ -901,7 +901,7 @@ __device__ __forceinline__ void o_step(const ExBuf& exU, float (*Os)[mp::DVB + 4
 // take their roles in start order, see the kernel); the bound only keeps a lost word from
 // hanging the GPU.
 namespace mp {
-template <bool NORM> constexpr int ntw() { return NORM ? 2 : 1; }  // tile waves
+constexpr int NTW = 2;                  // tile waves
 constexpr int TLPR = DVB / 8;           // lanes per row piece (8 values each)
 constexpr int TRPP = 64 / TLPR;         // rows per pass of a tile wave
 static_assert(TLPR == 4 && TRPP == 16, "tile-wave lane layout");
@@ -1035,60 +1035,47 @@ __device__ __forceinline__ void norm_finish(const NormCtx& nc_, const PrefillArg
 }
 
 // A tile wave's steps (as many LDS barriers as every other wave).  qt: this tile wave.
-template <int O_DT, bool NORM>
+template <int O_DT>
 __device__ __forceinline__ void tile_wave(ScanSmem& sm, const PrefillArgs& a, const Geo& G, const WsLayout& wl, int n,
                                           int nc, int qt) {
   using namespace mp;
-  constexpr int NG = C / TRPP / ntw<NORM>();  // row passes per tile wave
+  constexpr int NG = C / TRPP / NTW;  // row passes per tile wave
   const int lane = G.lane;
-  const int r0 = qt * (C / ntw<NORM>());
+  const int r0 = qt * (C / NTW);
   lds_barrier();  // the copy waves' two prologue steps
   lds_barrier();
-  if constexpr (!NORM) {
-    for (int c = 0; c < nc + 1; ++c) {
-      if (c >= 1) {
-        wait_flag(&sm.os_ready, c);  // chunk c - 1 staged
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-        float x[NG][8];
-        tile_take<NG>(sm.Os, r0, lane, x);
-        tile_store<O_DT, NG>(a.o, a, G, c - 1, r0, lane, x);
-      }
-      lds_barrier();
-    }
-  } else {
-    NormCtx nctx;
-    nctx.ring = reinterpret_cast<unsigned long long*>(static_cast<unsigned char*>(a.workspace) + wl.ring) +
-                ((int64_t)n * a.hv + G.h) * (RING * NB * C);
-    nctx.blk = G.dv0 / DVB;
-    nctx.r0 = r0;
-    load8<DT_BF16>(a.norm_w, G.dv0 + 8 * (lane % TLPR), nctx.w);
-    float xa[NG][8], xb[NG][8], sa[NG], sb[NG];  // chunks c - 3 and c - 2 at the start of step c
-    NormIn<NG> gin;
-    for (int c = 0; c < nc + 1; ++c) {
-      if (c >= 3) norm_finish<O_DT, NG>(nctx, a, G, c - 3, lane, gin, xa, sa);
+  NormCtx nctx;
+  nctx.ring = reinterpret_cast<unsigned long long*>(static_cast<unsigned char*>(a.workspace) + wl.ring) +
+              ((int64_t)n * a.hv + G.h) * (RING * NB * C);
+  nctx.blk = G.dv0 / DVB;
+  nctx.r0 = r0;
+  load8<DT_BF16>(a.norm_w, G.dv0 + 8 * (lane % TLPR), nctx.w);
+  float xa[NG][8], xb[NG][8], sa[NG], sb[NG];  // chunks c - 3 and c - 2 at the start of step c
+  NormIn<NG> gin;
+  for (int c = 0; c < nc + 1; ++c) {
+    if (c >= 3) norm_finish<O_DT, NG>(nctx, a, G, c - 3, lane, gin, xa, sa);
 #pragma unroll
-      for (int q = 0; q < NG; ++q) {
-        sa[q] = sb[q];
+    for (int q = 0; q < NG; ++q) {
+      sa[q] = sb[q];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xa[q][e] = xb[q][e];
-      }
-      if (c >= 1) {
-        wait_flag(&sm.os_ready, c);  // chunk c - 1 staged
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-        tile_take<NG>(sm.Os, r0, lane, xb);
-        row_sums<NG>(xb, sb);
-        norm_publish<NG>(nctx, c - 1, lane, sb);
-        if (a.o) tile_store<O_DT, NG>(a.o, a, G, c - 1, r0, lane, xb);
-      }
-      if (c >= 2) norm_issue<NG>(nctx, a, G, c - 2, lane, gin);
-      lds_barrier();
+      for (int e = 0; e < 8; ++e) xa[q][e] = xb[q][e];
     }
-    // chunks nc - 2 (words and gates in flight) and nc - 1
-    if (nc >= 2) norm_finish<O_DT, NG>(nctx, a, G, nc - 2, lane, gin, xa, sa);
-    if (nc >= 1) {
-      norm_issue<NG>(nctx, a, G, nc - 1, lane, gin);
-      norm_finish<O_DT, NG>(nctx, a, G, nc - 1, lane, gin, xb, sb);
+    if (c >= 1) {
+      wait_flag(&sm.os_ready, c);  // chunk c - 1 staged
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+      tile_take<NG>(sm.Os, r0, lane, xb);
+      row_sums<NG>(xb, sb);
+      norm_publish<NG>(nctx, c - 1, lane, sb);
+      if (a.o) tile_store<O_DT, NG>(a.o, a, G, c - 1, r0, lane, xb);
     }
+    if (c >= 2) norm_issue<NG>(nctx, a, G, c - 2, lane, gin);
+    lds_barrier();
+  }
+  // chunks nc - 2 (words and gates in flight) and nc - 1
+  if (nc >= 2) norm_finish<O_DT, NG>(nctx, a, G, nc - 2, lane, gin, xa, sa);
+  if (nc >= 1) {
+    norm_issue<NG>(nctx, a, G, nc - 1, lane, gin);
+    norm_finish<O_DT, NG>(nctx, a, G, nc - 1, lane, gin, xb, sb);
   }
 }
 
@@ -1212,6 +1199,7 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
     // which workgroups start (a ticket), not the block index: every workgroup with a smaller
     // ticket has started, so at most one head has members still to start and all others run
     // to the end and free their compute units.  No residency of the whole grid is assumed.
+    // (Dealing tickets over the XCDs like the block index above measured slower.)
     if (threadIdx.x == 0)
       sm.ticket = __hip_atomic_fetch_add(reinterpret_cast<unsigned*>(const_cast<unsigned char*>(ws) + wl.tick), 1u,
                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1291,21 +1279,24 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
       // Start once the chain wave is past K S^T: run beside it, the output wave's LDS reads
       // slow the chain's operand reads (the serial path) by about a third.
       if (c < nc) wait_flag(&sm.ks_done[pr], c + 1);
-      if (c >= 1) o_step<O_DT, FUSED>(sm.X[(c - 1) & 1], sm.Os, &sm.os_ready, a, G, c - 1, t0, qs, pa, ge);
+      if (c >= 1) o_step<O_DT, NORM>(sm.X[(c - 1) & 1], sm.Os, &sm.os_ready, a, G, c - 1, t0, qs, pa, ge);
       if (c < nc) qs_step(sm.B[c & 1], sm.X[c & 1], t0, lane, ln, lg, qs, pa, ge);
       lds_barrier();
     }
   } else {  // copy wave
     const int q = __builtin_amdgcn_readfirstlane(G.w - 2 * NPAIR);  // wave-uniform: scalar copy loop
     if constexpr (FUSED) {
-      // The first NTW copy waves are tile waves; the others copy (and the conv takes four of them).
-      constexpr int NTW = ntw<NORM>(), NCOPY = NCP - NTW;
+      // Whole-layer call: the first NTW copy waves are tile waves; the others copy (and the conv
+      // takes four of them).
+      constexpr int NTWF = NORM ? NTW : 0, NCOPY = NCP - NTWF;
       static_assert(NCOPY >= 4, "the conv of a V slice takes four waves");
-      if (q < NTW) {
-        tile_wave<O_DT, NORM>(sm, a, G, wl, n, nc, q);
-        return;
+      if constexpr (NORM) {
+        if (q < NTW) {
+          tile_wave<O_DT>(sm, a, G, wl, n, nc, q);
+          return;
+        }
       }
-      const int qc = q - NTW, qv = q - (NCP - 4);  // copy index; conv index (qv < 0: none)
+      const int qc = q - NTWF, qv = NORM ? q - (NCP - 4) : q;  // copy index; conv index (< 0 or > 3: none)
       // Step c: copies of chunk c+1 and raw rows of chunk c+2 in flight while the raw rows of
       // chunk c+1 (landed during step c-1) are convolved into its V slice.
       uint4 wt[4];  // conv taps of the lane's 8 value channels, packed bf16 as stored
@@ -1322,12 +1313,12 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
       if (nc > 1) issue_chunk<true, NCOPY>(sm, a, G, ws, -1, 1, qc);
       __builtin_amdgcn_s_waitcnt(0);
       lds_barrier();  // raw rows of chunk 0 visible to every copy wave
-      if (nc > 0 && qv >= 0) conv_vslice(sm, a, G, n, 0, qv, wt, bs);
+      if (nc > 0 && qv >= 0 && qv < 4) conv_vslice(sm, a, G, n, 0, qv, wt, bs);
       lds_barrier();
       for (int c = 0; c < nc + 1; ++c) {
         if (c + 1 < nc) {
           issue_chunk<true, NCOPY>(sm, a, G, ws, c + 1, c + 2 < nc ? c + 2 : -1, qc);
-          if (qv >= 0) conv_vslice(sm, a, G, n, c + 1, qv, wt, bs);
+          if (qv >= 0 && qv < 4) conv_vslice(sm, a, G, n, c + 1, qv, wt, bs);
           __builtin_amdgcn_s_waitcnt(0);
         }
         lds_barrier();
