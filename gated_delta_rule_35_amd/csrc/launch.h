@@ -60,6 +60,10 @@ struct PrefillArgs {
   const void* norm_w;     // [128] bf16
   float norm_eps;
   void* y;                // [total, hv, 128] contiguous
+  // Chunk range of this launch (whole-layer call in stages): local chunks [n_c lo / den,
+  // n_c hi / den) of each sequence of n_c chunks; s0 / s1 are then the states at its ends.
+  int part_lo = 0, part_hi = 1, part_den = 1;
+  int stage = 0;          // whole-layer call: this stage's workgroup ticket counter
 };
 
 struct DecodeArgs {

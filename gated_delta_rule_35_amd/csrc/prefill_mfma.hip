@@ -48,6 +48,10 @@
 // Number formats: bf16 inputs widen exactly to fp16 (normal range); fp32 intermediates
 // (S, R', U, P, X) are rounded to fp16 once per use (2^-11 relative); every product
 // accumulates in fp32 and the state itself stays fp32.
+#include <hip/hip_ext.h>
+
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -100,16 +104,18 @@ constexpr int QK_BYTES = sizeof(QKImage);
 struct WsLayout {
   size_t rec, qk, bytes;
   // whole-layer call only: per (sequence, value head) RING chunk slots, each with one 64-bit
-  // (chunk tag, partial sum of squares) word per output row and workgroup of the head; then
-  // the workgroup ticket counter.  Both are zeroed by prep.
-  size_t ring, tick, layer_bytes;
+  // (chunk tag, partial sum of squares) word per output row and workgroup of the head; the
+  // workgroup ticket counters of the stages (both zeroed by the first stage's prep); the states
+  // between stages.
+  size_t ring, tick, state, layer_bytes;
   __host__ __device__ WsLayout(int num_seqs, int hv, int hk, int64_t maxch) {
     rec = (4 * (size_t)(num_seqs + 1) + 255) & ~size_t(255);
     qk = rec + (size_t)hv * (size_t)maxch * mp::REC_BYTES;
     bytes = qk + (size_t)hk * (size_t)maxch * mp::QK_BYTES;
     ring = (bytes + 255) & ~size_t(255);
     tick = ring + (size_t)num_seqs * hv * mp::RING * mp::NB * mp::C * 8;
-    layer_bytes = tick + 256;
+    state = tick + 256;
+    layer_bytes = state + (size_t)num_seqs * hv * mp::D * mp::D * 4;
   }
 };
 
@@ -294,14 +300,19 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
   const int rd = (int)(lid % rounds);
   const int j = (int)((lid / rounds) % (unsigned)maxch);
   const int kh = (int)(lid / (rounds * (unsigned)maxch));
-  if (a.y) {  // whole-layer call: no partial sum published yet (tag 0 matches no chunk), no ticket taken
+  if (a.y && a.part_lo == 0) {  // whole-layer call, first stage: no partial sum published yet
+    // (tag 0 matches no chunk), no ticket taken
     uint4* r = reinterpret_cast<uint4*>(base + ws.ring);
-    const size_t n16 = (ws.layer_bytes - ws.ring) / 16;
+    const size_t n16 = (ws.state - ws.ring) / 16;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)nblk * blockDim.x)
       r[i] = make_uint4(0u, 0u, 0u, 0u);
   }
   if (j >= off[a.num_seqs]) return;
   const int n = seq_of_chunk(off, a.num_seqs, j);
+  if (a.part_den > 1) {  // a stage of the whole-layer call: its chunk range only
+    const int ncs = off[n + 1] - off[n], jl = j - off[n];
+    if (jl < (int)((int64_t)ncs * a.part_lo / a.part_den) || jl >= (int)((int64_t)ncs * a.part_hi / a.part_den)) return;
+  }
   const int64_t start = cu_at(a.cu, n, a.total);
   const int64_t c0 = start + (int64_t)(j - off[n]) * C;
   const int64_t end = cu_at(a.cu, n + 1, a.total);
@@ -575,7 +586,9 @@ struct ScanSmem {
 static_assert(sizeof(ScanSmem) <= 160 * 1024, "scan LDS");
 
 struct Geo {
-  int64_t start, end;
+  int64_t start, end;  // rows of this launch's chunks (a stage: the chunk range only)
+  int64_t hstart;      // the sequence's first row: the conv reads the history before it
+  int cbase;           // the sequence's chunk index of local chunk 0 (stages)
   int nchunks, h, kh, dv0, w, lane, ln, lg;
   int64_t sbase;
   size_t rec0;  // workspace byte offset of this sequence's first record for value head h
@@ -891,7 +904,8 @@ __device__ __forceinline__ void o_step(const ExBuf& exU, float (*Os)[mp::DVB + 4
 // Exchange: a row's partial sum of squares over this block's DVB columns travels with its chunk
 // tag in one 64-bit word, written and read as a relaxed atomic at agent scope: a reader that
 // sees the tag sees the sum stored with it, so no fence (on this chip, a write-back or
-// invalidation of a whole L2) is needed.  Chunk c uses slot c mod RING.  In step c a tile wave
+// invalidation of a whole L2) is needed.  Chunk c (counted from the sequence start, so that
+// the stages of a call never take each other's words) uses slot c mod RING.  In step c a tile wave
 // (1) waits for the words of chunk c - 3 (loaded at the end of step c - 1, reloaded while a tag
 // is older) and writes y of chunk c - 3; (2) takes chunk c - 1 from Os and publishes its sums;
 // (3) loads the words and gates of chunk c - 2.  Chunk k is published in step k + 1 and read in
@@ -911,6 +925,7 @@ struct NormCtx {
   unsigned long long* ring;  // this (sequence, value head): [RING][NB][64] tagged words
   int blk;                   // this block
   int r0;                    // first row of this tile wave
+  int cbase;                 // the sequence's chunk index of local chunk 0: tags and slots use it
   float w[8];                // norm weights of the lane's 8 columns
 };
 
@@ -944,7 +959,7 @@ __device__ __forceinline__ void tile_store(void* dst, const PrefillArgs& a, cons
 }
 
 __device__ __forceinline__ unsigned long long* ring_word(const NormCtx& nc_, int c, int b, int r) {
-  return nc_.ring + ((c & (mp::RING - 1)) * mp::NB + b) * mp::C + r;
+  return nc_.ring + (((c + nc_.cbase) & (mp::RING - 1)) * mp::NB + b) * mp::C + r;
 }
 
 // Partial sums of squares of the lane's rows over this block's columns (every lane of a row
@@ -968,7 +983,7 @@ __device__ __forceinline__ void norm_publish(const NormCtx& nc_, int c, int lane
 #pragma unroll
   for (int g = 0; g < NG; ++g)
     __hip_atomic_store(ring_word(nc_, c, nc_.blk, nc_.r0 + mp::TRPP * g + lane / mp::TLPR),
-                       ((unsigned long long)__float_as_uint(ss[g]) << 32) | (unsigned)(c + 1), __ATOMIC_RELAXED,
+                       ((unsigned long long)__float_as_uint(ss[g]) << 32) | (unsigned)(c + nc_.cbase + 1), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
 }
 
@@ -1011,7 +1026,7 @@ __device__ __forceinline__ void norm_finish(const NormCtx& nc_, const PrefillArg
   for (int it = 0; it < (1 << 24); ++it) {
     bool ok = true;
 #pragma unroll
-    for (int i = 0; i < mp::NB - 1; ++i) ok = ok && (unsigned)g.w[i] == (unsigned)(c + 1);
+    for (int i = 0; i < mp::NB - 1; ++i) ok = ok && (unsigned)g.w[i] == (unsigned)(c + nc_.cbase + 1);
     if (__all(ok)) break;
     __builtin_amdgcn_s_sleep(1);
     norm_load_words(nc_, c, lane, g);
@@ -1049,6 +1064,7 @@ __device__ __forceinline__ void tile_wave(ScanSmem& sm, const PrefillArgs& a, co
               ((int64_t)n * a.hv + G.h) * (RING * NB * C);
   nctx.blk = G.dv0 / DVB;
   nctx.r0 = r0;
+  nctx.cbase = G.cbase;
   load8<DT_BF16>(a.norm_w, G.dv0 + 8 * (lane % TLPR), nctx.w);
   float xa[NG][8], xb[NG][8], sa[NG], sb[NG];  // chunks c - 3 and c - 2 at the start of step c
   NormIn<NG> gin;
@@ -1132,7 +1148,7 @@ __device__ __forceinline__ void issue_chunk(ScanSmem& sm, const PrefillArgs& a, 
       for (int u = first_copy<NCOPY>(NQK + NREC, q); u < NQK + NREC + NV; u += NCOPY) {
         const int jv = 64 * (u - NQK - NREC) + lane, i = jv >> 2, pc = jv & 3;
         const int64_t pos = c0 - 3 + i;
-        const bool in = pos >= G.start && i < 3 + G.len(cv);
+        const bool in = pos >= G.hstart && i < 3 + G.len(cv);
         const uint16_t* src = vb + (in ? pos : c0) * a.v_stride + 8 * pc;
         __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)(&sm.Vr[cv & 1][0][0] + 512 * (u - NQK - NREC)), 16,
                                          0, 0);
@@ -1156,7 +1172,7 @@ __device__ __forceinline__ void conv_vslice(ScanSmem& sm, const PrefillArgs& a, 
 #pragma unroll
   for (int jt = 0; jt < 4; ++jt) {
     const int i = r + jt;
-    if (cc == 0 && i < 3) {
+    if (cc == 0 && i < 3 && G.start == G.hstart) {
       const uint16_t* hist = static_cast<const uint16_t*>(a.conv_hist);
       const int64_t ch = (int64_t)(2 * a.hk + G.h) * D + G.dv0 + 8 * cg;
       const int64_t Ctot = (int64_t)(2 * a.hk + a.hv) * D;
@@ -1201,8 +1217,8 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
     // to the end and free their compute units.  No residency of the whole grid is assumed.
     // (Dealing tickets over the XCDs like the block index above measured slower.)
     if (threadIdx.x == 0)
-      sm.ticket = __hip_atomic_fetch_add(reinterpret_cast<unsigned*>(const_cast<unsigned char*>(ws) + wl.tick), 1u,
-                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sm.ticket = __hip_atomic_fetch_add(reinterpret_cast<unsigned*>(const_cast<unsigned char*>(ws) + wl.tick) + a.stage,
+                                         1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     lid = sm.ticket;
   }
@@ -1219,10 +1235,17 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
   G.start = cu_at(a.cu, n, a.total);
   G.end = cu_at(a.cu, n + 1, a.total);
   if (G.end < G.start) G.end = G.start;
-  G.nchunks = (int)((G.end - G.start + C - 1) / C);
+  G.hstart = G.start;
+  const int ncs = (int)((G.end - G.start + C - 1) / C);
+  const int cb = (int)((int64_t)ncs * a.part_lo / a.part_den), ce = (int)((int64_t)ncs * a.part_hi / a.part_den);
+  G.cbase = cb;
+  G.start += (int64_t)cb * C;
+  if (G.end > G.hstart + (int64_t)ce * C) G.end = G.hstart + (int64_t)ce * C;
+  if (G.end < G.start) G.end = G.start;
+  G.nchunks = ce - cb;
   G.sbase = ((int64_t)n * a.hv + G.h) * (D * D);
-  G.rec0 = wl.rec + ((size_t)G.h * (size_t)maxch + (size_t)off[n]) * REC_BYTES;
-  G.qk0 = wl.qk + ((size_t)G.kh * (size_t)maxch + (size_t)off[n]) * QK_BYTES;
+  G.rec0 = wl.rec + ((size_t)G.h * (size_t)maxch + (size_t)(off[n] + cb)) * REC_BYTES;
+  G.qk0 = wl.qk + ((size_t)G.kh * (size_t)maxch + (size_t)(off[n] + cb)) * QK_BYTES;
   const int ln = G.ln, lg = G.lg, lane = G.lane;
   const int nc = G.nchunks;
   if (threadIdx.x < NPAIR) sm.ks_done[threadIdx.x] = 0;  // ordered before every use by the prologue barrier
@@ -1358,36 +1381,118 @@ static hipError_t scan_attr() {
   return e;
 }
 
-template <int O_DT, bool FUSED, bool NORM>
-static hipError_t launch_o(PrefillArgs a, hipStream_t st) {
-  if (a.num_seqs == 0) return hipSuccess;
-  int64_t maxch = max_chunks(a.total, a.num_seqs);
+static hipError_t launch_offsets(const PrefillArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(256), 0, st, a.cu, a.num_seqs, a.total,
                      static_cast<int32_t*>(a.workspace));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (a.total > 0) {
-    const int64_t rounds = (a.hv / a.hk + mp::PH - 1) / mp::PH;
-    hipLaunchKernelGGL((prep_kernel<FUSED>), dim3((unsigned)(maxch * a.hk * rounds)), dim3(256 * mp::PH), 0, st, a,
-                       maxch);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+// done (optional): an event completed with the kernel itself (no marker of its own in the queue)
+template <bool FUSED>
+static hipError_t launch_prep(const PrefillArgs& a, int64_t maxch, hipStream_t st, hipEvent_t done = nullptr) {
+  const int64_t rounds = (a.hv / a.hk + mp::PH - 1) / mp::PH;
+  const dim3 grid((unsigned)(maxch * a.hk * rounds)), block(256 * mp::PH);
+  if (done) {
+    hipExtLaunchKernelGGL((prep_kernel<FUSED>), grid, block, 0, st, nullptr, done, 0, a, maxch);
+  } else {
+    if (a.total == 0) return hipSuccess;
+    hipLaunchKernelGGL((prep_kernel<FUSED>), grid, block, 0, st, a, maxch);
   }
-  const size_t smem = sizeof(ScanSmem);
-  e = scan_attr<O_DT, FUSED, NORM>();
+  return hipGetLastError();
+}
+
+template <int O_DT, bool FUSED, bool NORM>
+static hipError_t launch_scan(const PrefillArgs& a, int64_t maxch, hipStream_t st) {
+  const hipError_t e = scan_attr<O_DT, FUSED, NORM>();
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((int64_t)a.num_seqs * a.hv * mp::NB)), block(64 * mp::NWAVES);
-  hipLaunchKernelGGL((scan_kernel<O_DT, FUSED, NORM>), grid, block, smem, st, a, maxch);
-  e = hipGetLastError();
-  if (e != hipSuccess || !FUSED || !a.conv_hist) return e;
-  // advance the conv history once every read of the old one (prep, scan) is done
+  hipLaunchKernelGGL((scan_kernel<O_DT, FUSED, NORM>), grid, block, sizeof(ScanSmem), st, a, maxch);
+  return hipGetLastError();
+}
+
+// advance the conv history once every read of the old one (prep, scan) is done
+static hipError_t launch_history(const PrefillArgs& a, hipStream_t st) {
+  if (!a.conv_hist) return hipSuccess;
   const ConvArgs h{a.q, a.qk_stride, nullptr, 0, DT_BF16, a.conv_w, a.conv_b, a.cu, a.num_seqs, a.total,
                    (2 * a.hk + a.hv) * mp::D, a.conv_hist, 0, 0.f};
   return launch_conv_history(h, st);
 }
 
+template <int O_DT, bool FUSED, bool NORM>
+static hipError_t launch_o(const PrefillArgs& a, hipStream_t st) {
+  if (a.num_seqs == 0) return hipSuccess;
+  const int64_t maxch = max_chunks(a.total, a.num_seqs);
+  hipError_t e = launch_offsets(a, st);
+  if (e == hipSuccess) e = launch_prep<FUSED>(a, maxch, st);
+  if (e == hipSuccess) e = launch_scan<O_DT, FUSED, NORM>(a, maxch, st);
+  if (e == hipSuccess && FUSED) e = launch_history(a, st);
+  return e;
+}
+
+// ---- whole-layer call in two stages.  The scan of a single long sequence occupies 4 compute
+// units per value head (192 of 256 for the layer) for its whole length, while prep uses the
+// whole chip for a short time before it.  So the call runs as prep(first part of every
+// sequence) -> scan(first part) on the caller's stream, with prep(rest) on a side stream beside
+// that scan (on the compute units the scan leaves free), then scan(rest) carrying the state
+// over.  Used when the scan leaves a quarter of the chip free and sequences are long enough.
+constexpr int SPLIT_NUM = 3, SPLIT_DEN = 5;  // first stage: the first 3/5 of each sequence's chunks
+
+namespace {
+struct SideQueue {
+  hipStream_t s = nullptr;
+  hipEvent_t prepped_a = nullptr, prepped_b = nullptr;
+  int cus = 0;
+};
+std::mutex g_side_mu;  // held while a call enqueues: the side queue's events are shared
+SideQueue g_side[64];
+}  // namespace
+
+static hipError_t side_queue(SideQueue*& q) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  q = &g_side[dev];
+  if (q->s) return hipSuccess;
+  if ((e = hipDeviceGetAttribute(&q->cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  if ((e = hipEventCreate(&q->prepped_a)) != hipSuccess) return e;
+  if ((e = hipEventCreate(&q->prepped_b)) != hipSuccess) return e;
+  return hipStreamCreateWithFlags(&q->s, hipStreamNonBlocking);  // default priority
+}
+
+template <int O_DT>
+static hipError_t launch_layer(const PrefillArgs& a, hipStream_t st) {
+  if (a.num_seqs == 0) return hipSuccess;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  SideQueue* q = nullptr;
+  hipError_t e = side_queue(q);
+  if (e != hipSuccess) return e;
+  const int64_t grid = (int64_t)a.num_seqs * a.hv * mp::NB;
+  const bool split = 4 * grid <= 3 * (int64_t)q->cus && a.total >= (int64_t)a.num_seqs * 8 * mp::C;
+  if (!split) return launch_o<O_DT, true, true>(a, st);
+  const int64_t maxch = max_chunks(a.total, a.num_seqs);
+  const WsLayout wl(a.num_seqs, a.hv, a.hk, maxch);
+  float* mid = reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) + wl.state);
+  PrefillArgs sa = a, sb = a;
+  sa.part_hi = SPLIT_NUM;
+  sa.part_den = SPLIT_DEN;
+  sa.s1 = mid;
+  sb.part_lo = SPLIT_NUM;
+  sb.part_hi = sb.part_den = SPLIT_DEN;
+  sb.s0 = mid;
+  sb.stage = 1;
+  if ((e = launch_offsets(a, st)) != hipSuccess) return e;
+  if ((e = launch_prep<true>(sa, maxch, st, q->prepped_a)) != hipSuccess) return e;
+  if ((e = launch_scan<O_DT, true, true>(sa, maxch, st)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(q->s, q->prepped_a, 0)) != hipSuccess) return e;
+  if ((e = launch_prep<true>(sb, maxch, q->s, q->prepped_b)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(st, q->prepped_b, 0)) != hipSuccess) return e;
+  if ((e = launch_scan<O_DT, true, true>(sb, maxch, st)) != hipSuccess) return e;
+  return launch_history(a, st);
+}
+
 hipError_t launch_layer_prefill(const PrefillArgs& a, hipStream_t st) {
-  return a.o_dtype == DT_BF16 ? launch_o<DT_BF16, true, true>(a, st) : launch_o<DT_F32, true, true>(a, st);
+  return a.o_dtype == DT_BF16 ? launch_layer<DT_BF16>(a, st) : launch_layer<DT_F32>(a, st);
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st) {

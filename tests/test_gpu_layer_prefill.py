@@ -113,6 +113,32 @@ def test_layer_prefill_equals_two_calls():
     assert float(rel.max()) <= 1e-5
 
 
+def test_layer_prefill_in_two_stages():
+    """Long sequences on a grid that leaves a quarter of the chip free: the call runs as two stages
+    (the prep of the second beside the scan of the first, the state carried over in between).
+    Ragged lengths split at 3/5 of each sequence's chunks, empty and one-token sequences, conv
+    history and initial states; o, the final state and the conv history bit-equal to the two-call
+    path, y within a few fp32 ulps of it and within tolerance of the oracle."""
+    rng = np.random.default_rng(650)
+    lens = [700, 1, 0, 2000, 64, 1300]
+    d = _case(rng, lens, 2, 6)
+    y1, f1, cs1, o1 = _layer(d, want_o=True)
+    cs2 = dev(d["cs"])
+    o2, f2 = gdn.prefill_fused(dev(d["x"]), dev(d["w"]), dev(d["g"]), dev(d["beta"]), dev(d["cu"]), num_k_heads=2,
+                               conv_state=cs2, initial_state=dev(d["s0"]), o_dtype=torch.float32)
+    y2 = gdn.gated_rmsnorm(o2, dev(d["z"]), dev(d["nw"]))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(o1, host(o2))
+    np.testing.assert_array_equal(f1, host(f2))
+    np.testing.assert_array_equal(cs1, host(cs2))
+    y2 = host(y2)
+    rel = np.abs(y1 - y2) / np.maximum(np.abs(y2), 1e-30)
+    ry, _, _, rfin = _oracle(d)
+    ey = rel_l2(y1, ry)
+    print(f"layer prefill in two stages: max rel diff of y vs two calls {rel.max():.3e}, y vs oracle {ey:.3e}")
+    assert float(rel.max()) <= 1e-5 and ey <= TOL_Y and rel_l2(f1, rfin) <= 2e-3
+
+
 def test_layer_prefill_bf16_outputs_are_rne_of_fp32_outputs():
     rng = np.random.default_rng(620)
     d = _case(rng, [150, 37], 1, 3)
