@@ -281,6 +281,14 @@ size_t agnes_gdn_layer_prefill_workspace_size(int num_seqs, int64_t total_tokens
  * of squares through the workspace; they take their roles in the order they
  * start, so any batch size runs (no co-residency of the grid is assumed).
  * Errors as agnes_gdn_prefill_fused; the workspace is cleared by the call.
+ *
+ * Where the scan leaves a quarter of the device's compute units free and the
+ * sequences average at least 512 tokens, the call runs in two stages and
+ * enqueues part of its work on a side stream of the library's own (created
+ * with two events on first use, once per device, default priority), joined
+ * back into `stream` before the call's last launch: work enqueued on `stream`
+ * afterwards sees every result.  Calls enqueue under a lock; the side stream
+ * joins a graph capture of `stream` through its events.
  */
 int agnes_gdn_layer_prefill(const void* x, int64_t x_token_stride, agnes_dtype dtype,
                             const void* conv_weight, const void* conv_bias, void* conv_state,
