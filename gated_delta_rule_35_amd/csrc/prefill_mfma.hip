@@ -174,8 +174,8 @@ __device__ __forceinline__ void lds_barrier() {
 // ---------------------------------------------------------------- 1. chunk offsets
 __global__ __launch_bounds__(256) void chunk_offsets_kernel(const int32_t* cu, int num_seqs, int64_t total,
                                                             int32_t* off) {
-  __shared__ int32_t part[256];
-  const int t = threadIdx.x;
+  __shared__ int32_t wsum[4];
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int per = (num_seqs + 255) / 256;
   const int lo = t * per < num_seqs ? t * per : num_seqs;
   const int hi = lo + per < num_seqs ? lo + per : num_seqs;
@@ -184,18 +184,17 @@ __global__ __launch_bounds__(256) void chunk_offsets_kernel(const int32_t* cu, i
     const int64_t s = cu_at(cu, n, total), e = cu_at(cu, n + 1, total);
     sum += e > s ? (int32_t)((e - s + mp::C - 1) / mp::C) : 0;
   }
-  part[t] = sum;
-  __syncthreads();
-  if (t == 0) {
-    int32_t run = 0;
-    for (int i = 0; i < 256; ++i) {
-      const int32_t v = part[i];
-      part[i] = run;
-      run += v;
-    }
+  // exclusive prefix of the per-thread sums: within each wave by shuffles, then over the waves
+  int32_t incl = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int32_t u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
   }
+  if (lane == 63) wsum[wv] = incl;
   __syncthreads();
-  int32_t run = part[t];
+  int32_t run = incl - sum;
+  for (int i = 0; i < wv; ++i) run += wsum[i];
   for (int n = lo; n < hi; ++n) {
     off[n] = run;
     const int64_t s = cu_at(cu, n, total), e = cu_at(cu, n + 1, total);

@@ -228,6 +228,21 @@ def test_prefill_bf16_varlen_full_heads():
     np.testing.assert_array_equal(fin[3], s["initial_state"][3])
 
 
+def test_prefill_many_sequences():
+    """300 sequences (more than one per thread of the chunk-offset prefix sum), lengths 0..60:
+    every sequence's output and final state, including empty ones passing their state through."""
+    rng = np.random.default_rng(46)
+    lens = [int(x) for x in rng.integers(0, 61, size=300)]
+    lens[0], lens[1], lens[299] = 0, 64, 129
+    s = sequence_inputs(rng, lens, 1, 3, 128, dtype="bf16", init="normal")
+    o, fin = run_prefill(s)
+    ro, rf = oracle_prefill(s)
+    eo, ef = rel_l2(o, ro), rel_l2(fin, rf)
+    print(f"300 sequences rel-L2 o={eo:.3e} state={ef:.3e}")
+    assert eo <= 2e-3 and ef <= 2e-3
+    np.testing.assert_array_equal(fin[0], s["initial_state"][0])
+
+
 def test_prefill_bf16_output_is_rne_of_fp32_output():
     rng = np.random.default_rng(42)
     s = sequence_inputs(rng, [150, 70], 2, 6, 128, dtype="bf16", init="normal")
