@@ -1210,14 +1210,42 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
   unsigned lid = blockIdx.x;
   if ((nblk & 7u) == 0) lid = (blockIdx.x & 7u) * (nblk >> 3) + (blockIdx.x >> 3);
   if constexpr (NORM) {
-    // The NB workgroups of a value head wait for each other.  Their roles follow the order in
-    // which workgroups start (a ticket), not the block index: every workgroup with a smaller
-    // ticket has started, so at most one head has members still to start and all others run
-    // to the end and free their compute units.  No residency of the whole grid is assumed.
-    // (Dealing tickets over the XCDs like the block index above measured slower.)
-    if (threadIdx.x == 0)
-      sm.ticket = __hip_atomic_fetch_add(reinterpret_cast<unsigned*>(const_cast<unsigned char*>(ws) + wl.tick) + a.stage,
-                                         1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // The NB workgroups of a value head wait for each other, so their roles are claimed in the
+    // order workgroups start, not taken from the block index.  The roles are cut into 8 ranges
+    // of whole key groups, one per XCD; a workgroup claims the next role of its own XCD's range
+    // (from the XCC_ID register) with an atomic counter, or, once that range is used up, the
+    // next role of a range that is not.  Each range is claimed in order, so at most one head
+    // per range has members still to start: at most 24 workgroups wait on partners that have
+    // not started, and the others run to the end and free their compute units.  No residency of
+    // the whole grid is assumed, only room for more than 24 of these workgroups at a time.  The
+    // XCC_ID only steers the 12 workgroups of a key group to one L2 (a wrong value costs
+    // locality, not correctness).
+    if (threadIdx.x == 0) {
+      unsigned* cnt = reinterpret_cast<unsigned*>(const_cast<unsigned char*>(ws) + wl.tick) + 8 * a.stage;
+      const unsigned cap = nblk >> 3;
+      unsigned role = 0;
+      if ((nblk % (8u * NB * (unsigned)(a.hv / a.hk))) == 0) {
+        const unsigned x = __builtin_amdgcn_s_getreg(0xf814) & 7u;  // hwreg(HW_REG_XCC_ID)
+        unsigned t = __hip_atomic_fetch_add(&cnt[x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (t < cap) {
+          role = x * cap + t;
+        } else {  // this XCD's range is used up: another range still has a role for every such claim
+          bool got = false;
+          for (int it = 0; it < (1 << 16) && !got; ++it)
+            for (unsigned y = 0; y < 8 && !got; ++y) {
+              if (__hip_atomic_load(&cnt[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= cap) continue;
+              t = __hip_atomic_fetch_add(&cnt[y], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              if (t < cap) {
+                role = y * cap + t;
+                got = true;
+              }
+            }
+        }
+      } else {
+        role = __hip_atomic_fetch_add(&cnt[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // plain start order
+      }
+      sm.ticket = role;
+    }
     __syncthreads();
     lid = sm.ticket;
   }
