@@ -108,6 +108,22 @@ __device__ __forceinline__ void store8(void* base, int64_t idx, const float v[8]
   }
 }
 
+// store8 with non-temporal stores (outputs nothing in the same kernel reads back).
+template <int DT>
+__device__ __forceinline__ void store8_nt(void* base, int64_t idx, const float v[8]) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  if constexpr (DT == DT_BF16) {
+    const u32x4 u = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                     pack_bf16x2(v[6], v[7])};
+    __builtin_nontemporal_store(u, reinterpret_cast<u32x4*>(static_cast<uint16_t*>(base) + idx));
+  } else {
+    f32x4* p = reinterpret_cast<f32x4*>(static_cast<float*>(base) + idx);
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, p);
+    __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, p + 1);
+  }
+}
+
 // 4 consecutive values (8-byte aligned for bf16, 16 for f32).
 template <int DT>
 __device__ __forceinline__ void store4(void* base, int64_t idx, f4 v) {
