@@ -1013,9 +1013,11 @@ __device__ __forceinline__ void norm_issue(const NormCtx& nc_, const PrefillArgs
 #pragma unroll
   for (int q = 0; q < NG; ++q) {
     const int r = nc_.r0 + mp::TRPP * q + lane / mp::TLPR;
-    g.z[q] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.z) +
-                                             (G.start + (int64_t)c * mp::C + (r < L ? r : 0)) * a.z_stride +
-                                             (int64_t)G.h * mp::D + G.dv0 + col);
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 zz = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+        static_cast<const uint16_t*>(a.z) + (G.start + (int64_t)c * mp::C + (r < L ? r : 0)) * a.z_stride +
+        (int64_t)G.h * mp::D + G.dv0 + col));  // read once: streamed past the cache
+    g.z[q] = make_uint4(zz[0], zz[1], zz[2], zz[3]);
   }
 }
 
