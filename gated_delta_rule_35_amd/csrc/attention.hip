@@ -9,16 +9,15 @@
 //   2. attn_kprep_kernel: per (token, KV head) the normalised, rotated k in bf16 (the KV cache
 //      rows, written where the caller says), an optional copy of v, and per token the 32 (cos,
 //      sin) pairs of its rotary angles, computed in fp64 and rounded once to fp32.
-//   3. attn_fwd_kernel: one 4-wave workgroup per (128-query block, query head).  Each wave owns
-//      32 queries.  The q rows arrive by direct global -> LDS copies and are normalised and
+//   3. attn_fwd_kernel: one 8-wave workgroup per (128-query block, query head).  Each wave owns
+//      16 queries; two waves share a SIMD, so one's softmax overlaps the other's products.  The q rows arrive by direct global -> LDS copies and are normalised and
 //      rotated in place, scaled by log2(e)/16 and kept as bf16 matrix-core operands.  K and V
 //      blocks of 64 keys are double-buffered in LDS (direct copies, 16-byte chunks of a row
 //      XOR-swizzled by a permutation of the row's low four bits, so both the 16-byte fragment
 //      reads and the transposing reads are free of bank conflicts).  Per block: S^T = K Q^T
 //      (each lane then holds scores of one query), an online softmax in base 2, and
 //      O^T += V^T P^T with the V^T fragments from the transposing LDS read; every LDS operand
-//      is read one step ahead of its products (one wave per SIMD: nothing else hides the
-//      latency).  The running maximum moves only when a score exceeds it by more than 2^8
+//      is read one step ahead of its products.  The running maximum moves only when a score exceeds it by more than 2^8
 //      (the weights stay <= 256, the result is unchanged, and the accumulators are rescaled
 //      rarely).  The output is divided by the softmax sum, multiplied by sigmoid(gate) and
 //      stored straight from the result layout.
@@ -31,8 +30,9 @@ constexpr int D = 256;        // head dim
 constexpr int HROT = 32;      // rotary pairs (dims 0..31 with 32..63)
 constexpr int BQ = 128;       // queries per workgroup
 constexpr int BK = 64;        // keys per block
-constexpr int NW = 4;         // waves per workgroup
-constexpr int QT = 2;         // 16-query tiles per wave
+constexpr int NW = 4;         // waves per workgroup (decode)
+constexpr int NWF = 8;        // waves per workgroup (prefill): two per SIMD
+constexpr int QT = BQ / 16 / NWF;  // 16-query tiles per wave (prefill)
 constexpr int CH = D / 8;     // 16-byte chunks per row (32)
 }  // namespace at
 
@@ -176,31 +176,34 @@ __global__ __launch_bounds__(256) void attn_kprep_kernel(AttnArgs a) {
 // Direct copies of 64 rows (two per 1 KiB copy) of a [rows][256] bf16 source into a swizzled
 // LDS tile: lane i of copy u brings row 2u + i/32, chunk (i % 32) ^ rsw(row), so the LDS slot
 // of chunk c of a row is c ^ rsw(row).  Rows at or past `valid` re-read row valid - 1 (their
-// results are masked or dropped).  Copies u = q + NW j (j < 8) are this wave's: row
-// r = 2q + rr + 8j, whose swizzle rsw(r) = ((2q + rr) << 1) | (j & 1) depends on j only through
-// its parity, so the lane's element offset is o[j & 1] + 8 j stride.
+// results are masked or dropped).  With NWC copying waves, copies u = q + NWC j (j < 32 / NWC)
+// are wave q's: row r = 2q + rr + 2 NWC j, whose swizzle rsw(r) depends on j only through its
+// parity (2 NWC is 8 or 16: bit 3 of r flips with j or never), so the lane's element offset is
+// o[j & 1] + 2 NWC j stride.
 struct CopyOffs {
   int32_t o[2];
 };
+template <int NWC>
 __device__ __forceinline__ CopyOffs copy_offs(int64_t stride, int q, int lane) {
   CopyOffs c;
   const int rr = lane >> 5, ch = lane & 31, r0 = 2 * q + rr;
 #pragma unroll
-  for (int b = 0; b < 2; ++b) c.o[b] = (int32_t)(r0 * stride + 8 * (ch ^ ((r0 << 1) | b)));
+  for (int b = 0; b < 2; ++b) c.o[b] = (int32_t)(r0 * stride + 8 * (ch ^ rsw(r0 + 2 * NWC * b)));
   return c;
 }
+template <int NWC>
 __device__ __forceinline__ void copy_rows(uint16_t* tile, const uint16_t* src, int64_t stride, int row0, int valid,
                                           int q, int lane, const CopyOffs& off) {
   if (row0 + 64 <= valid) {
     const uint16_t* base = src + (int64_t)row0 * stride;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_global_load_lds((aglb_void*)(base + 8 * j * stride + off.o[j & 1]),
-                                       (alds_void*)(tile + 2 * (q + at::NW * j) * at::D), 16, 0, 0);
+    for (int j = 0; j < 32 / NWC; ++j)
+      __builtin_amdgcn_global_load_lds((aglb_void*)(base + 2 * NWC * j * stride + off.o[j & 1]),
+                                       (alds_void*)(tile + 2 * (q + NWC * j) * at::D), 16, 0, 0);
     return;
   }
   const int rr = lane >> 5, ch = lane & 31;
-  for (int u = q; u < 32; u += at::NW) {
+  for (int u = q; u < 32; u += NWC) {
     int r = 2 * u + rr;
     const int lr = r;
     if (row0 + r >= valid) r = valid - 1 - row0;
@@ -210,7 +213,7 @@ __device__ __forceinline__ void copy_rows(uint16_t* tile, const uint16_t* src, i
 }
 
 template <int O_DT>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a, int nblk_total) {
+__global__ __launch_bounds__(64 * at::NWF) void attn_fwd_kernel(AttnArgs a, int nblk_total) {
   using namespace at;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   AttnSmem& sm = *reinterpret_cast<AttnSmem*>(smem_raw);
@@ -249,16 +252,16 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a, int nblk_tota
   const uint16_t* vsrc = static_cast<const uint16_t*>(a.v) + start * a.v_stride + (int64_t)g * D;
 
   // q rows into tiles 2 and 3 (rows 0..63, 64..127 of the block), K/V block 0 into tiles 0, 1
-  const CopyOffs qoff = copy_offs(a.q_stride, w, lane), koff = copy_offs(a.k_out_stride, w, lane),
-                 voff = copy_offs(a.v_stride, w, lane);
-  copy_rows(&sm.t[2][0][0], qsrc, a.q_stride, q0, len, w, lane, qoff);
-  copy_rows(&sm.t[3][0][0], qsrc, a.q_stride, q0 + BK, len, w, lane, qoff);
-  copy_rows(&sm.t[0][0][0], ksrc, a.k_out_stride, 0, len, w, lane, koff);
-  copy_rows(&sm.t[1][0][0], vsrc, a.v_stride, 0, len, w, lane, voff);
+  const CopyOffs qoff = copy_offs<NWF>(a.q_stride, w, lane), koff = copy_offs<NWF>(a.k_out_stride, w, lane),
+                 voff = copy_offs<NWF>(a.v_stride, w, lane);
+  copy_rows<NWF>(&sm.t[2][0][0], qsrc, a.q_stride, q0, len, w, lane, qoff);
+  copy_rows<NWF>(&sm.t[3][0][0], qsrc, a.q_stride, q0 + BK, len, w, lane, qoff);
+  copy_rows<NWF>(&sm.t[0][0][0], ksrc, a.k_out_stride, 0, len, w, lane, koff);
+  copy_rows<NWF>(&sm.t[1][0][0], vsrc, a.v_stride, 0, len, w, lane, voff);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // RMS-norm, rotary and the base-2 softmax scale of this wave's 32 q rows, in place; lane l
+  // RMS-norm, rotary and the base-2 softmax scale of this wave's 16 q rows, in place; lane l
   // holds dims 4l..4l+3 of a row.
   {
     const uint2 wr = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(a.q_norm_w) + 4 * lane);
@@ -266,7 +269,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a, int nblk_tota
                          bf16_to_f32(wr.y >> 16)};
     const float qscale = (a.scale > 0.f ? a.scale : 0.0625f) * 1.4426950408889634f;
     for (int i = 0; i < QT * 16; ++i) {
-      const int row = 32 * w + i;  // row of the 128-query block
+      const int row = 16 * QT * w + i;  // row of the 128-query block
       uint16_t* tile = &sm.t[2 + (row >> 6)][0][0];
       uint16_t* p = tile + swz(row & 63, 4 * lane);
       const uint2 raw = *reinterpret_cast<const uint2*>(p);
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a, int nblk_tota
   abf8 qf[QT][8];
 #pragma unroll
   for (int qt = 0; qt < QT; ++qt) {
-    const int row = 32 * w + 16 * qt + ln;
+    const int row = 16 * QT * w + 16 * qt + ln;
     const uint16_t* tile = &sm.t[2 + (row >> 6)][0][0];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qf[qt][ks] = *reinterpret_cast<const abf8*>(tile + swz(row & 63, 32 * ks + 8 * lg));
@@ -329,8 +332,8 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a, int nblk_tota
     const uint16_t* kcp = ksrc + (int64_t)nrow * a.k_out_stride;
     const uint16_t* vcp = vsrc + (int64_t)nrow * a.v_stride;
     if (next && !spread) {
-      copy_rows(nK, ksrc, a.k_out_stride, nrow, len, w, lane, koff);
-      copy_rows(nV, vsrc, a.v_stride, nrow, len, w, lane, voff);
+      copy_rows<NWF>(nK, ksrc, a.k_out_stride, nrow, len, w, lane, koff);
+      copy_rows<NWF>(nV, vsrc, a.v_stride, nrow, len, w, lane, voff);
     }
     const uint16_t* Kt = &sm.t[(kb & 1) * 2][0][0];
     const uint16_t* Vt = &sm.t[(kb & 1) * 2 + 1][0][0];
@@ -345,11 +348,11 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a, int nblk_tota
     for (int kt = 0; kt < 4; ++kt) kf[0][kt] = *reinterpret_cast<const abf8*>(Kt + swz(16 * kt + ln, 8 * lg));
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      if (spread) {
-        __builtin_amdgcn_global_load_lds((aglb_void*)(kcp + 8 * ks * a.k_out_stride + koff.o[ks & 1]),
-                                         (alds_void*)(nK + 2 * (w + NW * ks) * D), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((aglb_void*)(vcp + 8 * ks * a.v_stride + voff.o[ks & 1]),
-                                         (alds_void*)(nV + 2 * (w + NW * ks) * D), 16, 0, 0);
+      if (spread && ks < 32 / NWF) {
+        __builtin_amdgcn_global_load_lds((aglb_void*)(kcp + 2 * NWF * ks * a.k_out_stride + koff.o[ks & 1]),
+                                         (alds_void*)(nK + 2 * (w + NWF * ks) * D), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((aglb_void*)(vcp + 2 * NWF * ks * a.v_stride + voff.o[ks & 1]),
+                                         (alds_void*)(nV + 2 * (w + NWF * ks) * D), 16, 0, 0);
       }
       if (ks < 7) {
 #pragma unroll
@@ -376,7 +379,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a, int nblk_tota
     abf8 pf[QT][2];
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) {
-      const int qi = q0 + 32 * w + 16 * qt + ln;
+      const int qi = q0 + 16 * QT * w + 16 * qt + ln;
       if (kbase + BK - 1 > qi || kbase + BK > len) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
@@ -452,7 +455,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnArgs a, int nblk_tota
     l += __shfl_xor(l, 16);
     l += __shfl_xor(l, 32);
     const float inv = 1.0f / l;
-    const int qi = q0 + 32 * w + 16 * qt + ln;
+    const int qi = q0 + 16 * QT * w + 16 * qt + ln;
     if (qi < len) {
       const int64_t t = start + qi;
       const uint16_t* gp = static_cast<const uint16_t*>(a.gate) + t * a.gate_stride + (int64_t)h * D + 4 * lg;
@@ -566,9 +569,9 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int ns, in
   const int64_t ts = (int64_t)a.hkv * D;  // cache token stride
   const uint16_t* ksrc = static_cast<const uint16_t*>(a.k_cache) + (((int64_t)b * a.max_len + k0) * a.hkv + g) * D;
   const uint16_t* vsrc = static_cast<const uint16_t*>(a.v_cache) + (((int64_t)b * a.max_len + k0) * a.hkv + g) * D;
-  const CopyOffs off = copy_offs(ts, w, lane);
-  copy_rows(&sm.t[0][0][0], ksrc, ts, 0, valid, w, lane, off);
-  copy_rows(&sm.t[1][0][0], vsrc, ts, 0, valid, w, lane, off);
+  const CopyOffs off = copy_offs<NW>(ts, w, lane);
+  copy_rows<NW>(&sm.t[0][0][0], ksrc, ts, 0, valid, w, lane, off);
+  copy_rows<NW>(&sm.t[1][0][0], vsrc, ts, 0, valid, w, lane, off);
   // Q^T operands: rows ln < G are the query heads g G + ln
   abf8 qf[8];
   {
@@ -591,8 +594,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(AttnArgs a, int ns, in
     __syncthreads();  // block kb has landed; every wave is done with the other buffer
     if (kb + 1 < nblk) {
       const int nb = ((kb + 1) & 1) * 2;
-      copy_rows(&sm.t[nb][0][0], ksrc, ts, (kb + 1) * BK, valid, w, lane, off);
-      copy_rows(&sm.t[nb + 1][0][0], vsrc, ts, (kb + 1) * BK, valid, w, lane, off);
+      copy_rows<NW>(&sm.t[nb][0][0], ksrc, ts, (kb + 1) * BK, valid, w, lane, off);
+      copy_rows<NW>(&sm.t[nb + 1][0][0], vsrc, ts, (kb + 1) * BK, valid, w, lane, off);
     }
     const uint16_t* Kt = &sm.t[(kb & 1) * 2][0][0];
     const uint16_t* Vt = &sm.t[(kb & 1) * 2 + 1][0][0];
@@ -788,7 +791,7 @@ hipError_t launch_attn_prefill(AttnArgs a, hipStream_t st) {
                                                    hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (a0 != hipSuccess) return a0;
   if (a1 != hipSuccess) return a1;
-  hipLaunchKernelGGL(k, dim3((unsigned)((int64_t)nblk * a.hq)), dim3(256), smem, st, a, nblk);
+  hipLaunchKernelGGL(k, dim3((unsigned)((int64_t)nblk * a.hq)), dim3(64 * at::NWF), smem, st, a, nblk);
   return hipGetLastError();
 }
 
