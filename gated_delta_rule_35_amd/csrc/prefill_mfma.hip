@@ -1426,7 +1426,9 @@ static hipError_t launch_prep(const PrefillArgs& a, int64_t maxch, hipStream_t s
   if (done) {
     hipExtLaunchKernelGGL((prep_kernel<FUSED>), grid, block, 0, st, nullptr, done, 0, a, maxch);
   } else {
-    if (a.total == 0) return hipSuccess;
+    // (the whole-layer call's first prep also clears the exchange words and role counters, so it
+    // runs even when every sequence is empty)
+    if (a.total == 0 && !(a.y && a.part_lo == 0)) return hipSuccess;
     hipLaunchKernelGGL((prep_kernel<FUSED>), grid, block, 0, st, a, maxch);
   }
   return hipGetLastError();

@@ -183,6 +183,28 @@ def test_layer_prefill_repeated_calls_reuse_the_workspace():
     assert rel_l2(outs[1], ry) <= TOL_Y
 
 
+def test_layer_prefill_all_sequences_empty_after_a_full_call():
+    """A batch of empty sequences right after a call that left its role counters and exchange
+    words in the same workspace: nothing is written to y, the final states are the initial
+    ones, and the conv history is unchanged."""
+    rng = np.random.default_rng(660)
+    d1 = _case(rng, [150, 40], 2, 6)
+    ws = torch.empty(gdn.layer_prefill_workspace_size(3, 190, 2, 6), dtype=torch.uint8, device="cuda")
+    gdn.layer_prefill(dev(d1["x"]), dev(d1["w"]), dev(d1["g"]), dev(d1["beta"]), dev(d1["cu"]), dev(d1["z"]),
+                      dev(d1["nw"]), num_k_heads=2, conv_state=dev(d1["cs"]), initial_state=dev(d1["s0"]),
+                      out_dtype=torch.float32, workspace=ws)
+    d0 = _case(rng, [0, 0, 0], 2, 6)
+    cs = dev(d0["cs"])
+    y = torch.full((0, 6, D), 7.0, dtype=torch.float32, device="cuda")
+    y0, fin = gdn.layer_prefill(dev(d0["x"]), dev(d0["w"]), dev(d0["g"]), dev(d0["beta"]), dev(d0["cu"]),
+                                dev(d0["z"]), dev(d0["nw"]), num_k_heads=2, conv_state=cs,
+                                initial_state=dev(d0["s0"]), y=y, workspace=ws)
+    torch.cuda.synchronize()
+    assert y0.shape == (0, 6, D)
+    np.testing.assert_array_equal(host(fin), d0["s0"])
+    np.testing.assert_array_equal(host(cs), d0["cs"])
+
+
 def test_layer_prefill_full_layer_t8192():
     """The layer's prefill workload (T = 8192, 16 key / 48 value heads, bf16 projection x, gate z
     and norm weight of the chain workload); the oracle follows value heads 0, 1, 2, 23, 46, 47."""
