@@ -1514,11 +1514,18 @@ static hipError_t launch_layer(const PrefillArgs& a, hipStream_t st) {
   sb.part_hi = sb.part_den = SPLIT_DEN;
   sb.s0 = mid;
   sb.stage = 1;
+  // Under stream capture the events are recorded as their own nodes (a kernel-completion event
+  // is not a capturable dependency); the side stream then joins the capture through them.
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if ((e = hipStreamIsCapturing(st, &cap)) != hipSuccess) return e;
+  const bool capturing = cap != hipStreamCaptureStatusNone;
   if ((e = launch_offsets(a, st)) != hipSuccess) return e;
-  if ((e = launch_prep<true>(sa, maxch, st, q->prepped_a)) != hipSuccess) return e;
+  if ((e = launch_prep<true>(sa, maxch, st, capturing ? nullptr : q->prepped_a)) != hipSuccess) return e;
+  if (capturing && (e = hipEventRecord(q->prepped_a, st)) != hipSuccess) return e;
   if ((e = launch_scan<O_DT, true, true>(sa, maxch, st)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(q->s, q->prepped_a, 0)) != hipSuccess) return e;
-  if ((e = launch_prep<true>(sb, maxch, q->s, q->prepped_b)) != hipSuccess) return e;
+  if ((e = launch_prep<true>(sb, maxch, q->s, capturing ? nullptr : q->prepped_b)) != hipSuccess) return e;
+  if (capturing && (e = hipEventRecord(q->prepped_b, q->s)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(st, q->prepped_b, 0)) != hipSuccess) return e;
   if ((e = launch_scan<O_DT, true, true>(sb, maxch, st)) != hipSuccess) return e;
   return launch_history(a, st);

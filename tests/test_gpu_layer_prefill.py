@@ -205,6 +205,39 @@ def test_layer_prefill_all_sequences_empty_after_a_full_call():
     np.testing.assert_array_equal(host(cs), d0["cs"])
 
 
+def test_layer_prefill_in_a_graph():
+    """The two-stage call (one 1024-token sequence on 2 key / 6 value heads) captured into a graph
+    with its side stream, replayed three times with eager work on the stream in between: every
+    replay equals the eager call bit for bit."""
+    rng = np.random.default_rng(670)
+    d = _case(rng, [1024], 2, 6, hist=False)
+    x, w, g, be, cu, z, nw, s0 = (dev(d[k]) for k in ("x", "w", "g", "beta", "cu", "z", "nw", "s0"))
+    ws = torch.empty(gdn.layer_prefill_workspace_size(1, 1024, 2, 6), dtype=torch.uint8, device="cuda")
+    y_ref, f_ref = gdn.layer_prefill(x, w, g, be, cu, z, nw, num_k_heads=2, initial_state=s0, out_dtype=torch.float32,
+                                     workspace=ws)
+    torch.cuda.synchronize()
+    y_ref, f_ref = host(y_ref), host(f_ref)
+    y = torch.empty((1024, 6, D), dtype=torch.float32, device="cuda")
+    fin = torch.empty((1, 6, D, D), dtype=torch.float32, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # capture on a non-default stream, as torch requires
+        with torch.cuda.graph(graph):
+            gdn.layer_prefill(x, w, g, be, cu, z, nw, num_k_heads=2, initial_state=s0, final_state=fin, y=y,
+                              workspace=ws)
+    torch.cuda.synchronize()
+    for r in range(3):
+        y.fill_(float("nan"))
+        fin.fill_(float("nan"))
+        junk = torch.randn(1 << 20, device="cuda") * 2.0  # eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(y), y_ref)
+        np.testing.assert_array_equal(host(fin), f_ref)
+        del junk
+
+
 def test_layer_prefill_full_layer_t8192():
     """The layer's prefill workload (T = 8192, 16 key / 48 value heads, bf16 projection x, gate z
     and norm weight of the chain workload); the oracle follows value heads 0, 1, 2, 23, 46, 47."""
