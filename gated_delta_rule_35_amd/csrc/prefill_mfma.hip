@@ -103,19 +103,19 @@ constexpr int QK_BYTES = sizeof(QKImage);
 // Workspace: [chunk offsets (N+1) int32, 256-aligned] [records: Hv x maxch] [q/k images: Hk x maxch]
 struct WsLayout {
   size_t rec, qk, bytes;
+  size_t mid;  // calls in two stages: the states between the stages
   // whole-layer call only: per (sequence, value head) RING chunk slots, each with one 64-bit
   // (chunk tag, partial sum of squares) word per output row and workgroup of the head; the
-  // workgroup ticket counters of the stages (both zeroed by the first stage's prep); the states
-  // between stages.
-  size_t ring, tick, state, layer_bytes;
+  // workgroup role counters of the stages (both zeroed by the first stage's prep)
+  size_t ring, tick, layer_bytes;
   __host__ __device__ WsLayout(int num_seqs, int hv, int hk, int64_t maxch) {
     rec = (4 * (size_t)(num_seqs + 1) + 255) & ~size_t(255);
     qk = rec + (size_t)hv * (size_t)maxch * mp::REC_BYTES;
-    bytes = qk + (size_t)hk * (size_t)maxch * mp::QK_BYTES;
+    mid = qk + (size_t)hk * (size_t)maxch * mp::QK_BYTES;
+    bytes = mid + (size_t)num_seqs * hv * mp::D * mp::D * 4;
     ring = (bytes + 255) & ~size_t(255);
     tick = ring + (size_t)num_seqs * hv * mp::RING * mp::NB * mp::C * 8;
-    state = tick + 256;
-    layer_bytes = state + (size_t)num_seqs * hv * mp::D * mp::D * 4;
+    layer_bytes = tick + 256;
   }
 };
 
@@ -302,7 +302,7 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
   if (a.y && a.part_lo == 0) {  // whole-layer call, first stage: no partial sum published yet
     // (tag 0 matches no chunk), no ticket taken
     uint4* r = reinterpret_cast<uint4*>(base + ws.ring);
-    const size_t n16 = (ws.state - ws.ring) / 16;
+    const size_t n16 = (ws.layer_bytes - ws.ring) / 16;
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)nblk * blockDim.x)
       r[i] = make_uint4(0u, 0u, 0u, 0u);
   }
@@ -1462,7 +1462,7 @@ static hipError_t launch_o(const PrefillArgs& a, hipStream_t st) {
   return e;
 }
 
-// ---- whole-layer call in two stages.  The scan of a single long sequence occupies 4 compute
+// ---- prefill calls in two stages.  The scan of a single long sequence occupies 4 compute
 // units per value head (192 of 256 for the layer) for its whole length, while prep uses the
 // whole chip for a short time before it.  So the call runs as prep(first part of every
 // sequence) -> scan(first part) on the caller's stream, with prep(rest) on a side stream beside
@@ -1493,8 +1493,8 @@ static hipError_t side_queue(SideQueue*& q) {
   return hipStreamCreateWithFlags(&q->s, hipStreamNonBlocking);  // default priority
 }
 
-template <int O_DT>
-static hipError_t launch_layer(const PrefillArgs& a, hipStream_t st) {
+template <int O_DT, bool FUSED, bool NORM>
+static hipError_t launch_staged(const PrefillArgs& a, hipStream_t st) {
   if (a.num_seqs == 0) return hipSuccess;
   std::lock_guard<std::mutex> lock(g_side_mu);
   SideQueue* q = nullptr;
@@ -1502,10 +1502,10 @@ static hipError_t launch_layer(const PrefillArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   const int64_t grid = (int64_t)a.num_seqs * a.hv * mp::NB;
   const bool split = 4 * grid <= 3 * (int64_t)q->cus && a.total >= (int64_t)a.num_seqs * 8 * mp::C;
-  if (!split) return launch_o<O_DT, true, true>(a, st);
+  if (!split) return launch_o<O_DT, FUSED, NORM>(a, st);
   const int64_t maxch = max_chunks(a.total, a.num_seqs);
   const WsLayout wl(a.num_seqs, a.hv, a.hk, maxch);
-  float* mid = reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) + wl.state);
+  float* mid = reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) + wl.mid);
   PrefillArgs sa = a, sb = a;
   sa.part_hi = SPLIT_NUM;
   sa.part_den = SPLIT_DEN;
@@ -1520,25 +1520,25 @@ static hipError_t launch_layer(const PrefillArgs& a, hipStream_t st) {
   if ((e = hipStreamIsCapturing(st, &cap)) != hipSuccess) return e;
   const bool capturing = cap != hipStreamCaptureStatusNone;
   if ((e = launch_offsets(a, st)) != hipSuccess) return e;
-  if ((e = launch_prep<true>(sa, maxch, st, capturing ? nullptr : q->prepped_a)) != hipSuccess) return e;
+  if ((e = launch_prep<FUSED>(sa, maxch, st, capturing ? nullptr : q->prepped_a)) != hipSuccess) return e;
   if (capturing && (e = hipEventRecord(q->prepped_a, st)) != hipSuccess) return e;
-  if ((e = launch_scan<O_DT, true, true>(sa, maxch, st)) != hipSuccess) return e;
+  if ((e = launch_scan<O_DT, FUSED, NORM>(sa, maxch, st)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(q->s, q->prepped_a, 0)) != hipSuccess) return e;
-  if ((e = launch_prep<true>(sb, maxch, q->s, capturing ? nullptr : q->prepped_b)) != hipSuccess) return e;
+  if ((e = launch_prep<FUSED>(sb, maxch, q->s, capturing ? nullptr : q->prepped_b)) != hipSuccess) return e;
   if (capturing && (e = hipEventRecord(q->prepped_b, q->s)) != hipSuccess) return e;
   if ((e = hipStreamWaitEvent(st, q->prepped_b, 0)) != hipSuccess) return e;
-  if ((e = launch_scan<O_DT, true, true>(sb, maxch, st)) != hipSuccess) return e;
-  return launch_history(a, st);
+  if ((e = launch_scan<O_DT, FUSED, NORM>(sb, maxch, st)) != hipSuccess) return e;
+  return FUSED ? launch_history(a, st) : hipSuccess;
 }
 
 hipError_t launch_layer_prefill(const PrefillArgs& a, hipStream_t st) {
-  return a.o_dtype == DT_BF16 ? launch_layer<DT_BF16>(a, st) : launch_layer<DT_F32>(a, st);
+  return a.o_dtype == DT_BF16 ? launch_staged<DT_BF16, true, true>(a, st) : launch_staged<DT_F32, true, true>(a, st);
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs& a, hipStream_t st) {
   if (a.conv_w)
-    return a.o_dtype == DT_BF16 ? launch_o<DT_BF16, true, false>(a, st) : launch_o<DT_F32, true, false>(a, st);
-  return a.o_dtype == DT_BF16 ? launch_o<DT_BF16, false, false>(a, st) : launch_o<DT_F32, false, false>(a, st);
+    return a.o_dtype == DT_BF16 ? launch_staged<DT_BF16, true, false>(a, st) : launch_staged<DT_F32, true, false>(a, st);
+  return a.o_dtype == DT_BF16 ? launch_staged<DT_BF16, false, false>(a, st) : launch_staged<DT_F32, false, false>(a, st);
 }
 
 }  // namespace agnes

@@ -130,6 +130,16 @@ size_t agnes_gdn_prefill_workspace_size(int num_seqs, int64_t total_tokens, int 
  * in_dtype BF16 computes the chunk products on fp16 matrix cores with fp32
  * accumulation and an fp32 state; in_dtype F32 computes everything in fp32.
  * Sequences of length 0 pass their initial state (or zeros) to final_state.
+ *
+ * With bf16 inputs, where the scan leaves a quarter of the device's compute
+ * units free and the sequences average at least 512 tokens, the call runs in
+ * two stages: the precomputation of the second part of every sequence runs
+ * on a side stream of the library's own (created with two events on first
+ * use, once per device, default priority) beside the scan of the first part,
+ * and is joined back into `stream` before the second scan; work enqueued on
+ * `stream` afterwards sees every result.  Calls enqueue under a lock; the side
+ * stream joins a graph capture of `stream`.  Results are bit-identical to the
+ * one-stage run.
  */
 int agnes_gdn_prefill_chunked(const void* q, const void* k, const void* v, agnes_dtype in_dtype,
                               int64_t qk_token_stride, int64_t v_token_stride,
@@ -159,7 +169,7 @@ int agnes_gdn_prefill_chunked(const void* q, const void* k, const void* v, agnes
  *                of the old contents.
  *   l2norm_eps   the q/k L2 norm divides by sqrt(sum of squares + l2norm_eps)
  *   the rest     as agnes_gdn_prefill_chunked (same workspace size query with
- *                in_dtype AGNES_BF16).
+ *                in_dtype AGNES_BF16; the same two-stage execution).
  * Supported: bf16 x (AGNES_ERR_UNSUPPORTED otherwise), head_dim 128, Hv a multiple of Hk.
  */
 int agnes_gdn_prefill_fused(const void* x, int64_t x_token_stride, agnes_dtype dtype,
@@ -282,13 +292,8 @@ size_t agnes_gdn_layer_prefill_workspace_size(int num_seqs, int64_t total_tokens
  * start, so any batch size runs (no co-residency of the grid is assumed).
  * Errors as agnes_gdn_prefill_fused; the workspace is cleared by the call.
  *
- * Where the scan leaves a quarter of the device's compute units free and the
- * sequences average at least 512 tokens, the call runs in two stages and
- * enqueues part of its work on a side stream of the library's own (created
- * with two events on first use, once per device, default priority), joined
- * back into `stream` before the call's last launch: work enqueued on `stream`
- * afterwards sees every result.  Calls enqueue under a lock; the side stream
- * joins a graph capture of `stream` through its events.
+ * Runs in two stages where agnes_gdn_prefill_chunked does (same side stream,
+ * same guarantees).
  */
 int agnes_gdn_layer_prefill(const void* x, int64_t x_token_stride, agnes_dtype dtype,
                             const void* conv_weight, const void* conv_bias, void* conv_state,

@@ -243,6 +243,19 @@ def test_prefill_many_sequences():
     np.testing.assert_array_equal(fin[0], s["initial_state"][0])
 
 
+def test_prefill_two_stages_equal_one():
+    """As for the fused call: one 2000-token sequence (two stages) against the same sequence
+    followed by 8 empty ones (one stage): o and the final state bit for bit."""
+    rng = np.random.default_rng(47)
+    s1 = sequence_inputs(rng, [2000], 2, 6, 128, dtype="bf16", init="normal")
+    s9 = dict(s1, cu_seqlens=np.concatenate([s1["cu_seqlens"], np.full(8, 2000)]).astype(np.int32),
+              initial_state=np.concatenate([s1["initial_state"], np.zeros((8, 6, 128, 128), np.float32)]))
+    o1, f1 = run_prefill(s1)
+    o9, f9 = run_prefill(s9)
+    np.testing.assert_array_equal(o1, o9)
+    np.testing.assert_array_equal(f1[0], f9[0])
+
+
 def test_prefill_bf16_output_is_rne_of_fp32_output():
     rng = np.random.default_rng(42)
     s = sequence_inputs(rng, [150, 70], 2, 6, 128, dtype="bf16", init="normal")

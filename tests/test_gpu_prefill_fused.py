@@ -76,6 +76,23 @@ def test_prefill_fused_varlen(hist, init, bias):
         np.testing.assert_array_equal(oracle.as_f64(cs), rcs)
 
 
+def test_prefill_fused_two_stages_equal_one():
+    """A long sequence on a grid that leaves a quarter of the chip free runs in two stages (the
+    second half's prep beside the first half's scan); the same sequence followed by 8 empty ones
+    fills the grid past that and runs in one.  o, the final state and the conv history agree
+    bit for bit."""
+    rng = np.random.default_rng(430)
+    d = _case(rng, [2000], 2, 6)
+    o1, f1, cs1 = _run(d)
+    d9 = dict(d, cu=np.concatenate([d["cu"], np.full(8, d["cu"][-1])]).astype(np.int32),
+              cs=np.concatenate([d["cs"], np.zeros((8,) + d["cs"].shape[1:], np.uint16)]),
+              s0=np.concatenate([d["s0"], np.zeros((8,) + d["s0"].shape[1:], np.float32)]))
+    o9, f9, cs9 = _run(d9)
+    np.testing.assert_array_equal(o1, o9)
+    np.testing.assert_array_equal(f1[0], f9[0])
+    np.testing.assert_array_equal(cs1[0], cs9[0])
+
+
 def test_prefill_fused_bf16_output_is_rne_of_fp32_output():
     rng = np.random.default_rng(410)
     d = _case(rng, [150, 37], 1, 3)
