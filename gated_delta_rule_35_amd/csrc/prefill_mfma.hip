@@ -72,7 +72,6 @@ constexpr int NPAIR = NVT / TPW;  // chain waves (and as many output waves) per 
 constexpr int NCP = 6;       // copy waves
 constexpr int NWAVES = 2 * NPAIR + NCP;  // chain waves, output waves, copy waves
 constexpr int DVB = 16 * NVT;
-constexpr int NRG = 2 * TPW;  // rows of the output tile one output-wave lane holds (one per pass)
 constexpr int RING = 8;      // whole-layer call: chunk slots of the partial-sum exchange
 static_assert(RING >= 4 && (RING & (RING - 1)) == 0, "exchange ring: no slot reused before it is read");
 constexpr int NB = D / DVB;  // scan workgroups per value head
@@ -611,9 +610,11 @@ __device__ __forceinline__ h8 kt_operand(const ScanBuf& B, int kt, int ks, int t
   return cat(lds_tr4(&B.QK.K[32 * ks + trow][16 * kt + tcol]), lds_tr4(&B.QK.K[32 * ks + 16 + trow][16 * kt + tcol]));
 }
 
-// Bounded wait for an LDS flag that another wave of the workgroup raises.  The flag only
-// orders work in time (every data hand-over goes through a barrier), so it is relaxed, and
-// the bound (never reached when the flag works) keeps a broken one from hanging the GPU.
+// Bounded wait for an LDS flag that another wave of the workgroup raises, with relaxed loads.
+// ks_done only orders work in time (its data hand-over goes through a barrier); os_ready hands
+// over the staged output tile, so its writer releases (workgroup scope, LDS) before raising it
+// and its readers acquire after the wait.  The bound (never reached when the flag works) keeps
+// a broken one from hanging the GPU.
 __device__ __forceinline__ void wait_flag(const int* f, int target) {
   for (int i = 0; i < (1 << 20); ++i) {
     if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return;
