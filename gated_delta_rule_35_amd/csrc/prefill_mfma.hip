@@ -1210,14 +1210,21 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
   const WsLayout wl(a.num_seqs, a.hv, a.hk, maxch);
 
   // Workgroups sharing a key group are consecutive in `lid`; the hardware deals block ids
-  // round-robin over the 8 XCDs, so give each XCD a contiguous run of lid (shared L2).
+  // round-robin over the 8 XCDs, so each key group's workgroups go to one XCD (shared L2), and
+  // the key groups are dealt to the XCDs in turn (kg mod 8), so that every XCD gets an even
+  // share of every sequence when the grid is larger than the chip.
   const unsigned nblk = gridDim.x;
+  const unsigned kgw = (unsigned)(NB * (a.hv / a.hk));  // workgroups per key group
   unsigned lid = blockIdx.x;
-  if ((nblk & 7u) == 0) lid = (blockIdx.x & 7u) * (nblk >> 3) + (blockIdx.x >> 3);
+  if ((nblk % (8u * kgw)) == 0) {
+    const unsigned i = blockIdx.x >> 3;
+    lid = ((i / kgw) * 8u + (blockIdx.x & 7u)) * kgw + i % kgw;
+  }
   if constexpr (NORM) {
     // The NB workgroups of a value head wait for each other, so their roles are claimed in the
     // order workgroups start, not taken from the block index.  The roles are cut into 8 ranges
-    // of whole key groups, one per XCD; a workgroup claims the next role of its own XCD's range
+    // of whole key groups, one per XCD (range y: key groups y, y + 8, y + 16, ..., dealt like the
+    // block index above, so every XCD gets its share of every sequence); a workgroup claims the next role of its own XCD's range
     // (from the XCC_ID register) with an atomic counter, or, once that range is used up, the
     // next role of a range that is not.  Each range is claimed in order, so at most one head
     // per range has members still to start: at most 24 workgroups wait on partners that have
@@ -1232,20 +1239,20 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
       if ((nblk % (8u * NB * (unsigned)(a.hv / a.hk))) == 0) {
         const unsigned x = __builtin_amdgcn_s_getreg(0xf814) & 7u;  // hwreg(HW_REG_XCC_ID)
         unsigned t = __hip_atomic_fetch_add(&cnt[x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (t < cap) {
-          role = x * cap + t;
-        } else {  // this XCD's range is used up: another range still has a role for every such claim
+        unsigned y = x;
+        if (t >= cap) {  // this XCD's range is used up: another range still has a role for every such claim
           bool got = false;
           for (int it = 0; it < (1 << 16) && !got; ++it)
-            for (unsigned y = 0; y < 8 && !got; ++y) {
+            for (y = 0; y < 8 && !got; ++y) {
               if (__hip_atomic_load(&cnt[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= cap) continue;
               t = __hip_atomic_fetch_add(&cnt[y], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              if (t < cap) {
-                role = y * cap + t;
-                got = true;
-              }
+              got = t < cap;
             }
+          if (got) --y;  // the loop advanced past the range it claimed from
         }
+        // claim t of range y: its key groups are y, y + 8, y + 16, ... (dealt as the block ids)
+        const unsigned kgw2 = (unsigned)(NB * (a.hv / a.hk));
+        role = ((t / kgw2) * 8u + y) * kgw2 + t % kgw2;
       } else {
         role = __hip_atomic_fetch_add(&cnt[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // plain start order
       }
