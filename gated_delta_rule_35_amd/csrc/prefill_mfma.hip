@@ -102,10 +102,10 @@ constexpr int QK_BYTES = sizeof(QKImage);
 // Workspace: [chunk offsets (N+1) int32, 256-aligned] [records: Hv x maxch] [q/k images: Hk x maxch]
 struct WsLayout {
   size_t rec, qk, bytes;
-  size_t mid;  // calls in two stages: the states between the stages
+  size_t mid;  // calls in stages: the states carried between the stages
   // whole-layer call only: per (sequence, value head) RING chunk slots, each with one 64-bit
   // (chunk tag, partial sum of squares) word per output row and workgroup of the head; the
-  // workgroup role counters of the stages (both zeroed by the first stage's prep)
+  // workgroup role counters of the stages (all zeroed by the first stage's prep)
   size_t ring, tick, layer_bytes;
   __host__ __device__ WsLayout(int num_seqs, int hv, int hk, int64_t maxch) {
     rec = (4 * (size_t)(num_seqs + 1) + 255) & ~size_t(255);
@@ -1470,18 +1470,27 @@ static hipError_t launch_o(const PrefillArgs& a, hipStream_t st) {
   return e;
 }
 
-// ---- prefill calls in two stages.  The scan of a single long sequence occupies 4 compute
-// units per value head (192 of 256 for the layer) for its whole length, while prep uses the
-// whole chip for a short time before it.  So the call runs as prep(first part of every
-// sequence) -> scan(first part) on the caller's stream, with prep(rest) on a side stream beside
-// that scan (on the compute units the scan leaves free), then scan(rest) carrying the state
-// over.  Used when the scan leaves a quarter of the chip free and sequences are long enough.
-constexpr int SPLIT_NUM = 3, SPLIT_DEN = 5;  // first stage: the first 3/5 of each sequence's chunks
+// ---- prefill calls in stages.  The scan of a single long sequence occupies 4 compute units per
+// value head (192 of 256 for the layer) for its whole length, while prep uses the whole chip for
+// a short time before it.  So the call runs as prep(first part of every sequence) -> scan(first
+// part) on the caller's stream, with prep(next part) on a side stream beside that scan (on the
+// compute units the scan leaves free), then scan(next part) carrying the state over.  Prep beside
+// a scan runs ~3x slower than alone, so the first part is the larger: 3/5 of the chunks.  More
+// stages shorten the exposed first prep but cost more at each hand-over than they save (at
+// T = 8192: two stages 356 us, three 373-380 us, four 398 us).  Used when the scan leaves a
+// quarter of the chip free and sequences are long enough.
+#ifndef GDN_SPLIT_CUTS
+#define GDN_SPLIT_CUTS 24
+#endif
+constexpr int SPLIT_DEN = 40;                          // stage boundaries in 1/40 of each sequence's chunks
+constexpr int SPLIT_CUT[] = {GDN_SPLIT_CUTS};          // stage k covers [cut[k-1], cut[k])
+constexpr int NSTAGE = (int)(sizeof(SPLIT_CUT) / sizeof(int)) + 1;
+static_assert(NSTAGE <= 8, "the workspace holds role counters for 8 stages");
 
 namespace {
 struct SideQueue {
   hipStream_t s = nullptr;
-  hipEvent_t prepped_a = nullptr, prepped_b = nullptr;
+  hipEvent_t prepped[NSTAGE] = {};
   int cus = 0;
 };
 std::mutex g_side_mu;  // held while a call enqueues: the side queue's events are shared
@@ -1496,8 +1505,8 @@ static hipError_t side_queue(SideQueue*& q) {
   q = &g_side[dev];
   if (q->s) return hipSuccess;
   if ((e = hipDeviceGetAttribute(&q->cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-  if ((e = hipEventCreate(&q->prepped_a)) != hipSuccess) return e;
-  if ((e = hipEventCreate(&q->prepped_b)) != hipSuccess) return e;
+  for (int k = 0; k < NSTAGE; ++k)
+    if ((e = hipEventCreate(&q->prepped[k])) != hipSuccess) return e;
   return hipStreamCreateWithFlags(&q->s, hipStreamNonBlocking);  // default priority
 }
 
@@ -1514,28 +1523,33 @@ static hipError_t launch_staged(const PrefillArgs& a, hipStream_t st) {
   const int64_t maxch = max_chunks(a.total, a.num_seqs);
   const WsLayout wl(a.num_seqs, a.hv, a.hk, maxch);
   float* mid = reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) + wl.mid);
-  PrefillArgs sa = a, sb = a;
-  sa.part_hi = SPLIT_NUM;
-  sa.part_den = SPLIT_DEN;
-  sa.s1 = mid;
-  sb.part_lo = SPLIT_NUM;
-  sb.part_hi = sb.part_den = SPLIT_DEN;
-  sb.s0 = mid;
-  sb.stage = 1;
+  PrefillArgs sp[NSTAGE];
+  for (int k = 0; k < NSTAGE; ++k) {
+    sp[k] = a;
+    sp[k].part_lo = k == 0 ? 0 : SPLIT_CUT[k - 1];
+    sp[k].part_hi = k == NSTAGE - 1 ? SPLIT_DEN : SPLIT_CUT[k];
+    sp[k].part_den = SPLIT_DEN;
+    sp[k].stage = k;
+    if (k > 0) sp[k].s0 = mid;           // a workgroup reads its state slice before it writes it,
+    if (k < NSTAGE - 1) sp[k].s1 = mid;  // so a middle stage updates the carried state in place
+  }
   // Under stream capture the events are recorded as their own nodes (a kernel-completion event
   // is not a capturable dependency); the side stream then joins the capture through them.
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   if ((e = hipStreamIsCapturing(st, &cap)) != hipSuccess) return e;
   const bool capturing = cap != hipStreamCaptureStatusNone;
   if ((e = launch_offsets(a, st)) != hipSuccess) return e;
-  if ((e = launch_prep<FUSED>(sa, maxch, st, capturing ? nullptr : q->prepped_a)) != hipSuccess) return e;
-  if (capturing && (e = hipEventRecord(q->prepped_a, st)) != hipSuccess) return e;
-  if ((e = launch_scan<O_DT, FUSED, NORM>(sa, maxch, st)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(q->s, q->prepped_a, 0)) != hipSuccess) return e;
-  if ((e = launch_prep<FUSED>(sb, maxch, q->s, capturing ? nullptr : q->prepped_b)) != hipSuccess) return e;
-  if (capturing && (e = hipEventRecord(q->prepped_b, q->s)) != hipSuccess) return e;
-  if ((e = hipStreamWaitEvent(st, q->prepped_b, 0)) != hipSuccess) return e;
-  if ((e = launch_scan<O_DT, FUSED, NORM>(sb, maxch, st)) != hipSuccess) return e;
+  if ((e = launch_prep<FUSED>(sp[0], maxch, st, capturing ? nullptr : q->prepped[0])) != hipSuccess) return e;
+  if (capturing && (e = hipEventRecord(q->prepped[0], st)) != hipSuccess) return e;
+  for (int k = 0; k < NSTAGE; ++k) {
+    if (k > 0 && (e = hipStreamWaitEvent(st, q->prepped[k], 0)) != hipSuccess) return e;
+    if ((e = launch_scan<O_DT, FUSED, NORM>(sp[k], maxch, st)) != hipSuccess) return e;
+    if (k + 1 == NSTAGE) break;
+    if (k == 0 && (e = hipStreamWaitEvent(q->s, q->prepped[0], 0)) != hipSuccess) return e;
+    hipEvent_t done = q->prepped[k + 1];
+    if ((e = launch_prep<FUSED>(sp[k + 1], maxch, q->s, capturing ? nullptr : done)) != hipSuccess) return e;
+    if (capturing && (e = hipEventRecord(done, q->s)) != hipSuccess) return e;
+  }
   return FUSED ? launch_history(a, st) : hipSuccess;
 }
 
