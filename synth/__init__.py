@@ -10,12 +10,13 @@ consumes.
 from .bf16 import f32_to_bf16_bits, bf16_bits_to_f32
 from .configs import (
     LAYER, make_config, decode_step_inputs, varlen_lengths, unit_vectors,
-    gate_draws,
+    gate_draws, layer_sequence_inputs, make_layer_config,
 )
 from .attention import ATTN, attn_prefill_inputs, attn_decode_inputs
 
 __all__ = [
     "f32_to_bf16_bits", "bf16_bits_to_f32", "LAYER", "make_config",
     "decode_step_inputs", "varlen_lengths", "unit_vectors", "gate_draws",
+    "layer_sequence_inputs", "make_layer_config",
     "ATTN", "attn_prefill_inputs", "attn_decode_inputs",
 ]

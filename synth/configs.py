@@ -126,6 +126,56 @@ def layer_prefill_inputs(rng, T, dtype="bf16"):
                 cu_seqlens=np.array([0, T], np.int32), dtype=dtype, **L)
 
 
+def layer_sequence_inputs(rng, lengths, init=None, init_std=0.01, g_scale=0.05):
+    """Whole-layer prefill inputs over a packed batch of ``lengths`` tokens, with the raw
+    projection output x drawn directly from its distribution N(0, PROJ_STD^2) (the projection
+    matmul of ``layer_prefill_inputs`` is too costly on the host at 65536 tokens and beyond).
+
+    Conv weights U(-1/2, 1/2), no bias, zero conv history; g, beta as every workload; z N(0,1);
+    norm weight 1 + 0.1 N(0,1); initial states per ``init`` as in ``sequence_inputs``.  x and z
+    are drawn in blocks of tokens, so host memory stays near the size of the stored arrays.
+    """
+    L = LAYER
+    lengths = [int(n) for n in lengths]
+    total = int(sum(lengths))
+    C, hv, D = L["conv_channels"], L["num_v_heads"], L["head_dim"]
+    cu = np.zeros(len(lengths) + 1, np.int32)
+    cu[1:] = np.cumsum(lengths)
+    conv_w = f32_to_bf16_bits(rng.uniform(-0.5, 0.5, size=(C, L["conv_kernel"])).astype(np.float32))
+    norm_w = f32_to_bf16_bits((1.0 + 0.1 * rng.standard_normal(D)).astype(np.float32))
+    x = np.empty((total, C), np.uint16)
+    z = np.empty((total, hv, D), np.uint16)
+    g = np.empty((total, hv), np.float32)
+    beta = np.empty((total, hv), np.float32)
+    for t0 in range(0, total, _BLOCK):
+        t1 = min(total, t0 + _BLOCK)
+        n = t1 - t0
+        x[t0:t1] = f32_to_bf16_bits(rng.standard_normal((n, C), dtype=np.float32) * np.float32(PROJ_STD))
+        z[t0:t1] = f32_to_bf16_bits(rng.standard_normal((n, hv, D), dtype=np.float32))
+        g[t0:t1], beta[t0:t1] = gate_draws(rng, (n, hv), g_scale)
+    s0 = None
+    if init is not None:
+        s0 = np.zeros((len(lengths), hv, D, D), np.float32)
+        for i in range(len(lengths)):
+            if init == "normal" or (init == "alternate" and i % 2 == 1):
+                s0[i] = rng.standard_normal((hv, D, D), dtype=np.float32) * np.float32(init_std)
+    return dict(x=x, conv_w=conv_w, g=g, beta=beta, z=z, norm_w=norm_w, cu_seqlens=cu,
+                initial_state=s0, dtype="bf16", **L)
+
+
+def make_layer_config(index):
+    """Whole-layer (conv -> recurrence -> gated norm) inputs for the long and the varlen
+    workloads, seeded with [1000 + index, 1]: 2 = one sequence of 65536 tokens with an initial
+    state N(0, 0.01^2); 4 = the 32 log-uniform lengths of workload 4 (the same lengths), initial
+    states zero for even and N(0, 0.01^2) for odd sequences."""
+    if index == 2:
+        return layer_sequence_inputs(np.random.default_rng([1002, 1]), [65536], init="normal")
+    if index == 4:
+        lengths = varlen_lengths(np.random.default_rng(1004))
+        return layer_sequence_inputs(np.random.default_rng([1004, 1]), lengths, init="alternate")
+    raise ValueError(f"no whole-layer variant of workload {index}")
+
+
 def decode_state_inputs(rng, batch):
     """Decode workload state: fp32 states N(0, 0.01^2), bf16 conv cache, conv weights."""
     L = LAYER

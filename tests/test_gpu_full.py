@@ -54,12 +54,13 @@ def test_full_layer_prefill_chain_t8192():
     # ---- prefill call on the oracle's conv output (rounded to bf16)
     yb = f32_to_bf16_bits(yr.astype(np.float32))
     q, k, v = _views(yb, T)
-    heads = [0, 1, 2, 23, 46, 47]
+    heads = list(range(HV))  # every key group and every value head of it
     o, fin = _prefill(q, k, v, cfg["g"], cfg["beta"], cu)
-    ro, rf = oracle.recurrence(q, k, v, cfg["g"], cfg["beta"], cu, heads=heads)
-    eo, ef = rel_l2(o[:, heads], ro[:, heads]), rel_l2(fin[:, heads], rf[:, heads])
-    print(f"prefill T=8192 rel-L2 o={eo:.3e} state={ef:.3e}")
-    assert eo <= 2e-3 and ef <= 2e-3
+    ro, rf = oracle.recurrence(q, k, v, cfg["g"], cfg["beta"], cu)
+    eo, ef = rel_l2(o, ro), rel_l2(fin, rf)
+    worst = max(rel_l2(o[:, h], ro[:, h]) for h in heads)
+    print(f"prefill T=8192 rel-L2 o={eo:.3e} state={ef:.3e} worst head o={worst:.3e}")
+    assert eo <= 2e-3 and ef <= 2e-3 and worst <= 2e-3
     # ---- gated RMSNorm call on the oracle's output (rounded to bf16)
     ob = f32_to_bf16_bits(ro[:, heads].astype(np.float32))
     zs = np.ascontiguousarray(cfg["z"][:, heads])
@@ -109,9 +110,10 @@ def test_varlen_prefill_32_sequences():
 
 def test_batched_decode_1000_steps():
     """256 sequences, 1000 consecutive seeded steps, fp32 states updated in place; the oracle
-    follows sequences 0, 85, 170, 255 (all 48 heads) through every step."""
+    follows 16 sequences (0, 17, .., 255: every workgroup position modulo 16) with all 48 heads
+    through every step."""
     d = make_config(3)
-    picks = [0, 85, 170, 255]
+    picks = list(range(0, 256, 17))
     state = dev(d["state"])
     ref_state = d["state"][picks].astype(np.float64)
     worst = 0.0

@@ -2,9 +2,10 @@
 gated RMS-norm in one call) against the fp64 oracle of the same composition, with nothing
 rounded between the steps.
 
-Tolerances: the recurrence output carries the chunked prefill's error (matrix-core operands in
-fp16, rel-L2 2e-3 on fp32 outputs); the norm divides each row by its own RMS, which the same
-relative error enters once more, so y is gated at rel-L2 3e-3.  Against the two-call path
+Tolerances: every output from bf16 inputs (y, o and the final state) is gated at rel-L2 2e-3 on
+fp32 outputs.  The norm divides each row by its own RMS: an error common to a row cancels, and
+independent errors move the row's RMS only by about e / sqrt(128), so y carries about the
+recurrence output's own error (measured: y 4e-4 where o is 3-4e-4).  Against the two-call path
 (agnes_gdn_prefill_fused then agnes_gdn_gated_rmsnorm) the recurrence output is the same
 arithmetic and must agree bit for bit; y then differs only by the order of the 128-term sum of
 squares and the reciprocal square root (a few fp32 ulps), gated at 1e-5 elementwise relative.
@@ -14,7 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
-from synth import f32_to_bf16_bits, make_config, LAYER
+from synth import f32_to_bf16_bits, make_config, make_layer_config, LAYER
 from tests.helpers import dev, host, rel_l2, as_f64
 
 torch = pytest.importorskip("torch")
@@ -23,7 +24,7 @@ import gated_delta_rule_35_amd as gdn  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 D = 128
-TOL_Y = 3e-3
+TOL_Y = 2e-3
 
 
 def _case(rng, lens, hk, hv, hist=True, init=True):
@@ -240,7 +241,9 @@ def test_layer_prefill_in_a_graph():
 
 def test_layer_prefill_full_layer_t8192():
     """The layer's prefill workload (T = 8192, 16 key / 48 value heads, bf16 projection x, gate z
-    and norm weight of the chain workload); the oracle follows value heads 0, 1, 2, 23, 46, 47."""
+    and norm weight of the chain workload) in the launch configuration the benchmark times (two
+    stages, roles claimed per XCD range); the oracle follows all 48 value heads, so every key
+    group and every one of the eight role ranges is checked."""
     cfg = make_config(1)
     T, HK, HV = 8192, LAYER["num_k_heads"], LAYER["num_v_heads"]
     cu = cfg["cu_seqlens"]
@@ -248,11 +251,93 @@ def test_layer_prefill_full_layer_t8192():
                                dev(cfg["z"]), dev(cfg["norm_w"]), num_k_heads=HK, out_dtype=torch.float32)
     torch.cuda.synchronize()
     y, fin = host(y), host(fin)
-    heads = [0, 1, 2, 23, 46, 47]
     u, _ = oracle.causal_conv(cfg["x"], cfg["conv_w"], cu, None, l2_heads=2 * HK)
     q, k, v = u[:, :HK * D].reshape(T, HK, D), u[:, HK * D:2 * HK * D].reshape(T, HK, D), u[:, 2 * HK * D:].reshape(T, HV, D)
-    ro, rf = oracle.recurrence(q, k, v, cfg["g"], cfg["beta"], cu, heads=heads)
-    ry = oracle.gated_rmsnorm(ro[:, heads], cfg["z"][:, heads], cfg["norm_w"])
-    ey, ef = rel_l2(y[:, heads], ry), rel_l2(fin[:, heads], rf[:, heads])
-    print(f"layer prefill T=8192 rel-L2 y={ey:.3e} state={ef:.3e}")
-    assert ey <= TOL_Y and ef <= 2e-3
+    del u
+    ro, rf = oracle.recurrence(q, k, v, cfg["g"], cfg["beta"], cu)
+    ry = oracle.gated_rmsnorm(ro, cfg["z"], cfg["norm_w"])
+    ey, ef = rel_l2(y, ry), rel_l2(fin, rf)
+    worst = max(rel_l2(y[:, h], ry[:, h]) for h in range(HV))
+    print(f"layer prefill T=8192 rel-L2 y={ey:.3e} state={ef:.3e} worst head y={worst:.3e}")
+    assert ey <= TOL_Y and ef <= 2e-3 and worst <= TOL_Y
+
+
+# value heads the oracle follows at the long and varlen sizes: stride 5 covers all three positions
+# of a key group (0, 5, 10 -> 0, 2, 1 mod 3) and 10 of the 16 key groups
+HEADS10 = list(range(0, 48, 5))
+
+
+def _sub_layer(d, heads, a, b, with_s0=True):
+    """The oracle of the whole layer on tokens [a, b) of one sequence (which starts at a), on the
+    value heads ``heads`` only: each head is taken with its key head's q and k channels as a
+    layer of len(heads) key and value heads (conv and L2 act per channel and per head)."""
+    kh = [h // 3 for h in heads]
+    ch = np.concatenate([np.arange(128 * j, 128 * j + 128) for j in kh]
+                        + [np.arange(2048 + 128 * j, 2048 + 128 * j + 128) for j in kh]
+                        + [np.arange(4096 + 128 * h, 4096 + 128 * h + 128) for h in heads])
+    x = np.ascontiguousarray(d["x"][a:b][:, ch])
+    w = np.ascontiguousarray(d["conv_w"][ch])
+    s0 = d["s0n"][:, heads] if with_s0 and d.get("s0n") is not None else None
+    n = len(heads)
+    ro, _, rf = oracle.prefill_conv_recurrence(x, w, np.array([0, b - a]), None, d["g"][a:b][:, heads],
+                                               d["beta"][a:b][:, heads], s0, n, n)
+    ry = oracle.gated_rmsnorm(ro, np.ascontiguousarray(d["z"][a:b][:, heads]), d["norm_w"])
+    return ry, rf[0]
+
+
+def _run_layer_big(d):
+    """The whole-layer call on a large workload; y stays on the device (fp32) for sampling."""
+    s0 = d["initial_state"]
+    y, fin = gdn.layer_prefill(dev(d["x"]), dev(d["conv_w"]), dev(d["g"]), dev(d["beta"]), dev(d["cu_seqlens"]),
+                               dev(d["z"]), dev(d["norm_w"]), num_k_heads=LAYER["num_k_heads"],
+                               initial_state=None if s0 is None else dev(s0), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    return y, host(fin)
+
+
+def test_layer_prefill_long_t65536():
+    """One sequence of 65536 tokens (1024 chunks, split at 3/5 between the two stages) with an
+    initial state, through the whole-layer call; the oracle follows value heads 0, 5, .., 45 over
+    the whole sequence, and the first 128 tokens (where the initial state still dominates) are
+    gated on their own."""
+    d = make_layer_config(2)
+    yd, fin = _run_layer_big(d)
+    y = host(yd[:, HEADS10])
+    del yd
+    d["s0n"] = d["initial_state"][0][None]
+    T = d["x"].shape[0]
+    ry, rf = _sub_layer(d, HEADS10, 0, T)
+    ey, ef, ew = rel_l2(y, ry), rel_l2(fin[0, HEADS10], rf), rel_l2(y[:128], ry[:128])
+    print(f"layer prefill T=65536 rel-L2 y={ey:.3e} state={ef:.3e} first-128 y={ew:.3e}")
+    assert ey <= TOL_Y and ef <= 2e-3 and ew <= TOL_Y
+
+
+def test_layer_prefill_varlen_32_sequences():
+    """The 32-sequence log-uniform batch (251,984 tokens, 1536 value-head chains, more workgroups
+    than the chip holds) through the whole-layer call: the first 128 tokens of every sequence on
+    value heads 0, 5, .., 45, and four whole sequences (the shortest, the longest, the first two)
+    with their final states."""
+    d = make_layer_config(4)
+    cu = d["cu_seqlens"]
+    lens = np.diff(cu)
+    yd, fin = _run_layer_big(d)
+    rows = np.concatenate([np.arange(a, min(b, a + 128)) for a, b in zip(cu[:-1], cu[1:])])
+    yw = host(yd[torch.from_numpy(rows).cuda()][:, HEADS10])
+    worst = 0.0
+    off = 0
+    for n in range(len(lens)):
+        a, m = int(cu[n]), int(min(lens[n], 128))
+        d["s0n"] = d["initial_state"][n][None]
+        ry, _ = _sub_layer(d, HEADS10, a, a + m)
+        worst = max(worst, rel_l2(yw[off:off + m], ry))
+        off += m
+    print(f"varlen layer prefill: worst first-128 window y rel-L2 {worst:.3e}")
+    assert worst <= TOL_Y
+    for n in sorted({0, 1, int(np.argmin(lens)), int(np.argmax(lens))}):
+        a, b = int(cu[n]), int(cu[n + 1])
+        d["s0n"] = d["initial_state"][n][None]
+        y = host(yd[a:b][:, HEADS10])
+        ry, rf = _sub_layer(d, HEADS10, a, b)
+        ey, ef = rel_l2(y, ry), rel_l2(fin[n, HEADS10], rf)
+        print(f"seq {n} len {b - a}: y rel-L2 {ey:.3e} state {ef:.3e}")
+        assert ey <= TOL_Y and ef <= 2e-3

@@ -121,7 +121,7 @@ def test_prefill_fused_close_to_separate_calls():
 
 def test_prefill_fused_full_layer_t8192():
     """The layer's prefill workload (T = 8192, 16 key / 48 value heads, x = the bf16 projection of
-    the chain workload); the oracle follows value heads 0, 1, 2, 23, 46, 47."""
+    the chain workload); the oracle follows all 48 value heads."""
     cfg = make_config(1)
     T, HK, HV = 8192, LAYER["num_k_heads"], LAYER["num_v_heads"]
     cu = cfg["cu_seqlens"]
@@ -129,10 +129,11 @@ def test_prefill_fused_full_layer_t8192():
                                num_k_heads=HK, o_dtype=torch.float32)
     torch.cuda.synchronize()
     o, fin = host(o), host(fin)
-    heads = [0, 1, 2, 23, 46, 47]
     u, _ = oracle.causal_conv(cfg["x"], cfg["conv_w"], cu, None, l2_heads=2 * HK)
     q, k, v = u[:, :HK * D].reshape(T, HK, D), u[:, HK * D:2 * HK * D].reshape(T, HK, D), u[:, 2 * HK * D:].reshape(T, HV, D)
-    ro, rf = oracle.recurrence(q, k, v, cfg["g"], cfg["beta"], cu, heads=heads)
-    eo, ef = rel_l2(o[:, heads], ro[:, heads]), rel_l2(fin[:, heads], rf[:, heads])
-    print(f"fused prefill T=8192 rel-L2 o={eo:.3e} state={ef:.3e}")
-    assert eo <= 2e-3 and ef <= 2e-3
+    del u
+    ro, rf = oracle.recurrence(q, k, v, cfg["g"], cfg["beta"], cu)
+    eo, ef = rel_l2(o, ro), rel_l2(fin, rf)
+    worst = max(rel_l2(o[:, h], ro[:, h]) for h in range(HV))
+    print(f"fused prefill T=8192 rel-L2 o={eo:.3e} state={ef:.3e} worst head o={worst:.3e}")
+    assert eo <= 2e-3 and ef <= 2e-3 and worst <= 2e-3
