@@ -23,7 +23,7 @@ from . import _lib
 
 __all__ = ["conv", "prefill_chunked", "prefill_fused", "decode_step", "gated_rmsnorm", "decode_fused",
            "prefill_workspace_size", "layer_prefill", "layer_prefill_workspace_size", "attn_prefill", "attn_prefill_workspace_size",
-           "attn_decode", "attn_decode_workspace_size",
+           "attn_decode", "attn_decode_workspace_size", "ceiling_rmw_stream", "ceiling_mfma",
            "AgnesError", "version", "LIB_PATH"]
 
 LIB_PATH = _lib.LIB_PATH
@@ -476,3 +476,21 @@ def attn_decode(q, k, v, gate, q_norm_weight, k_norm_weight, k_cache, v_cache, c
         _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(), _stream(q.device))
     _check("agnes_attn_decode", st)
     return o
+
+
+def ceiling_rmw_stream(buf):
+    """Measurement kernel: every 16-byte vector of the device tensor ``buf`` read and written back
+    once (contents unchanged); 2 * buf's bytes move through HBM."""
+    nbytes = buf.numel() * buf.element_size()
+    _check("agnes_gdn_ceiling_rmw_stream",
+           _lib.load().agnes_gdn_ceiling_rmw_stream(buf.data_ptr(), nbytes, _stream(buf.device)))
+
+
+def ceiling_mfma(sink, blocks, iters):
+    """Measurement kernel: ``blocks`` workgroups of four waves, each issuing ``iters`` rounds of 8
+    independent bf16 16x16x32 matrix-core products held in registers
+    (blocks * 4 * iters * 8 * 16384 FLOPs); ``sink`` is a float32 device tensor of blocks * 4."""
+    if sink.dtype != torch.float32 or sink.numel() < 4 * blocks:
+        raise ValueError("sink: float32 tensor of at least 4 * blocks elements")
+    _check("agnes_gdn_ceiling_mfma",
+           _lib.load().agnes_gdn_ceiling_mfma(sink.data_ptr(), blocks, iters, _stream(sink.device)))

@@ -45,6 +45,8 @@ SIGNATURES = {
                                   c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_int64, c_void_p,
                                   c_int, c_int, c_int, c_int, c_int, c_float, c_float, c_float, c_void_p, c_int,
                                   c_void_p, c_size_t, c_void_p]),
+    "agnes_gdn_ceiling_rmw_stream": (c_int, [c_void_p, c_size_t, c_void_p]),
+    "agnes_gdn_ceiling_mfma": (c_int, [c_void_p, c_int, c_int, c_void_p]),
     "agnes_gdn_status_string": (ctypes.c_char_p, [c_int]),
     "agnes_gdn_last_hip_error": (c_int, []),
     "agnes_gdn_version": (ctypes.c_char_p, []),

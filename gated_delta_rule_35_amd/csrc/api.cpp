@@ -471,3 +471,14 @@ AGNES_API int agnes_gdn_layer_prefill(const void* x, int64_t x_token_stride, agn
   a.y = y;
   return hip_status(agnes::launch_layer_prefill(a, static_cast<hipStream_t>(stream)));
 }
+
+AGNES_API int agnes_gdn_ceiling_rmw_stream(void* buf, size_t bytes, void* stream) {
+  if (!buf || !aligned(buf, 16) || bytes % 16) return AGNES_ERR_INVALID_ARG;
+  return hip_status(agnes::launch_rmw_stream(buf, bytes, static_cast<hipStream_t>(stream)));
+}
+
+AGNES_API int agnes_gdn_ceiling_mfma(float* sink, int blocks, int iters, void* stream) {
+  if (!sink || !aligned(sink, 4) || blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 20))
+    return AGNES_ERR_INVALID_ARG;
+  return hip_status(agnes::launch_mfma_peak(sink, blocks, iters, static_cast<hipStream_t>(stream)));
+}

@@ -396,6 +396,26 @@ int agnes_attn_decode(const void* q, int64_t q_stride, const void* k, int64_t k_
                       float rope_base, float norm_eps, float scale, void* o, agnes_dtype o_dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Measurement kernels: the two ceilings the benchmark reports its roofline fractions against,
+ * measured on the machine itself beside the vendor's peaks.
+ *
+ * agnes_gdn_ceiling_rmw_stream — every 16-byte vector of `buf` (device, `bytes` a multiple of
+ * 16, 16-byte aligned) read once and written back once (multiplied by 1.0, so the contents are
+ * unchanged): the access pattern of the decode step's in-place state update.  Bytes moved per
+ * call: 2 * bytes.
+ *
+ * agnes_gdn_ceiling_mfma — `blocks` workgroups of four waves, each wave issuing `iters` rounds of
+ * 8 independent bf16 16x16x32 matrix-core products on operands held in registers (each
+ * accumulator reused 8 products later).  FLOPs per call: blocks * 4 * iters * 8 * 16384.  One
+ * float per wave is written to `sink` (device, blocks * 4 floats).
+ *
+ * Both return AGNES_ERR_INVALID_ARG for a NULL or misaligned buffer, a size that is not a
+ * multiple of 16, or blocks / iters outside [1, 2^20]; AGNES_ERR_HIP if the launch fails.
+ */
+int agnes_gdn_ceiling_rmw_stream(void* buf, size_t bytes, void* stream);
+int agnes_gdn_ceiling_mfma(float* sink, int blocks, int iters, void* stream);
+
 const char* agnes_gdn_status_string(int status);
 
 /* hipError_t of the last AGNES_ERR_HIP returned on the calling thread (0 if none). */
