@@ -23,7 +23,8 @@ from . import _lib
 
 __all__ = ["conv", "prefill_chunked", "prefill_fused", "decode_step", "gated_rmsnorm", "decode_fused",
            "prefill_workspace_size", "layer_prefill", "layer_prefill_workspace_size", "attn_prefill", "attn_prefill_workspace_size",
-           "attn_decode", "attn_decode_workspace_size", "ceiling_rmw_stream", "ceiling_mfma",
+           "attn_decode", "attn_decode_workspace_size", "ceiling_rmw_stream", "ceiling_mfma", "workspace_status", "set_wait_limit",
+           "WS_WAIT_LDS", "WS_WAIT_EXCHANGE", "WS_WAIT_ROLE", "WS_RANGE",
            "AgnesError", "version", "LIB_PATH"]
 
 LIB_PATH = _lib.LIB_PATH
@@ -494,3 +495,26 @@ def ceiling_mfma(sink, blocks, iters):
         raise ValueError("sink: float32 tensor of at least 4 * blocks elements")
     _check("agnes_gdn_ceiling_mfma",
            _lib.load().agnes_gdn_ceiling_mfma(sink.data_ptr(), blocks, iters, _stream(sink.device)))
+
+
+WS_WAIT_LDS, WS_WAIT_EXCHANGE, WS_WAIT_ROLE, WS_RANGE = (_lib.WS_WAIT_LDS, _lib.WS_WAIT_EXCHANGE, _lib.WS_WAIT_ROLE,
+                                                         _lib.WS_RANGE)
+
+
+def workspace_status(workspace):
+    """Status bits (WS_WAIT_LDS, WS_WAIT_EXCHANGE, WS_WAIT_ROLE, WS_RANGE) that the last bf16 prefill
+    call on ``workspace`` (a device uint8 tensor passed as its workspace) left in it; 0 when all is
+    well.  Synchronises the current stream."""
+    import ctypes
+    flags = ctypes.c_uint32(0)
+    _check("agnes_gdn_workspace_status",
+           _lib.load().agnes_gdn_workspace_status(workspace.data_ptr(), ctypes.addressof(flags),
+                                                  _stream(workspace.device)))
+    return flags.value
+
+
+def set_wait_limit(polls):
+    """Process-wide bound on the polls of the bf16 prefill calls' bounded waits (0 restores each
+    wait's own bound).  For tests of the status bits only: with a small bound the waits give up
+    and the results are unreliable."""
+    _check("agnes_gdn_set_wait_limit", _lib.load().agnes_gdn_set_wait_limit(int(polls)))

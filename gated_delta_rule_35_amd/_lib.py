@@ -45,6 +45,8 @@ SIGNATURES = {
                                   c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p, c_int64, c_void_p,
                                   c_int, c_int, c_int, c_int, c_int, c_float, c_float, c_float, c_void_p, c_int,
                                   c_void_p, c_size_t, c_void_p]),
+    "agnes_gdn_workspace_status": (c_int, [c_void_p, c_void_p, c_void_p]),
+    "agnes_gdn_set_wait_limit": (c_int, [ctypes.c_uint32]),
     "agnes_gdn_ceiling_rmw_stream": (c_int, [c_void_p, c_size_t, c_void_p]),
     "agnes_gdn_ceiling_mfma": (c_int, [c_void_p, c_int, c_int, c_void_p]),
     "agnes_gdn_status_string": (ctypes.c_char_p, [c_int]),
@@ -53,6 +55,7 @@ SIGNATURES = {
 }
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+WS_WAIT_LDS, WS_WAIT_EXCHANGE, WS_WAIT_ROLE, WS_RANGE = 1, 2, 4, 8
 F32, BF16 = 0, 1
 
 _lib = None

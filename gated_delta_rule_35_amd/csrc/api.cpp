@@ -2,6 +2,7 @@
 // Every check runs before anything is enqueued; a failed check launches nothing.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -13,6 +14,7 @@
 namespace {
 
 thread_local int g_last_hip_error = 0;
+std::atomic<uint32_t> g_wait_limit{0};
 
 constexpr int kHeadDim = 128;
 
@@ -38,6 +40,10 @@ int hip_status(hipError_t e) {
 }
 
 }  // namespace
+
+namespace agnes {
+unsigned prefill_wait_limit() { return g_wait_limit.load(std::memory_order_relaxed); }
+}  // namespace agnes
 
 AGNES_API const char* agnes_gdn_status_string(int status) {
   switch (status) {
@@ -140,6 +146,7 @@ AGNES_API int agnes_gdn_prefill_chunked(const void* q, const void* k, const void
   agnes::PrefillArgs a{q, k, v, (int)in_dtype, qk_token_stride, v_token_stride, g, beta, cu_seqlens, num_seqs,
                        total_tokens, num_k_heads, num_v_heads, scale, initial_state, final_state, o, (int)o_dtype,
                        workspace, workspace_bytes};
+  a.wait_limit = agnes::prefill_wait_limit();
   hipStream_t st = static_cast<hipStream_t>(stream);
   return hip_status(in_dtype == AGNES_BF16 ? agnes::launch_prefill_mfma(a, st) : agnes::launch_prefill_f32(a, st));
 }
@@ -187,6 +194,7 @@ AGNES_API int agnes_gdn_prefill_fused(const void* x, int64_t x_token_stride, agn
                        (int)AGNES_BF16, x_token_stride, x_token_stride, g, beta, cu_seqlens, num_seqs, total_tokens,
                        num_k_heads, num_v_heads, scale, initial_state, final_state, o, (int)o_dtype, workspace,
                        workspace_bytes, conv_weight, conv_bias, conv_state, l2norm_eps};
+  a.wait_limit = agnes::prefill_wait_limit();
   return hip_status(agnes::launch_prefill_mfma(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -464,6 +472,7 @@ AGNES_API int agnes_gdn_layer_prefill(const void* x, int64_t x_token_stride, agn
                        (int)AGNES_BF16, x_token_stride, x_token_stride, g, beta, cu_seqlens, num_seqs, total_tokens,
                        num_k_heads, num_v_heads, scale, initial_state, final_state, o, (int)out_dtype, workspace,
                        workspace_bytes, conv_weight, conv_bias, conv_state, l2norm_eps};
+  a.wait_limit = agnes::prefill_wait_limit();
   a.z = z;
   a.z_stride = z_token_stride;
   a.norm_w = norm_weight;
@@ -481,4 +490,20 @@ AGNES_API int agnes_gdn_ceiling_mfma(float* sink, int blocks, int iters, void* s
   if (!sink || !aligned(sink, 4) || blocks < 1 || blocks > (1 << 20) || iters < 1 || iters > (1 << 20))
     return AGNES_ERR_INVALID_ARG;
   return hip_status(agnes::launch_mfma_peak(sink, blocks, iters, static_cast<hipStream_t>(stream)));
+}
+
+AGNES_API int agnes_gdn_workspace_status(const void* workspace, uint32_t* flags, void* stream) {
+  if (!workspace || !flags || !aligned(workspace, 4)) return AGNES_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint32_t word = 0;
+  hipError_t e = hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return hip_status(e);
+  *flags = word;
+  return AGNES_OK;
+}
+
+AGNES_API int agnes_gdn_set_wait_limit(uint32_t polls) {
+  g_wait_limit.store(polls, std::memory_order_relaxed);
+  return AGNES_OK;
 }

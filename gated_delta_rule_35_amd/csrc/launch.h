@@ -64,7 +64,11 @@ struct PrefillArgs {
   // n_c hi / den) of each sequence of n_c chunks; s0 / s1 are then the states at its ends.
   int part_lo = 0, part_hi = 1, part_den = 1;
   int stage = 0;          // whole-layer call: this stage's workgroup ticket counter
+  unsigned wait_limit = 0;  // bounded waits poll at most this often (0: each wait's own bound)
 };
+
+// Process-wide poll bound handed to every bf16 prefill launch (agnes_gdn_set_wait_limit).
+unsigned prefill_wait_limit();
 
 struct DecodeArgs {
   const void* q;

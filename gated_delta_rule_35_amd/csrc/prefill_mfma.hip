@@ -99,8 +99,10 @@ constexpr int REC_BYTES = sizeof(RecImage);
 constexpr int QK_BYTES = sizeof(QKImage);
 }  // namespace mp
 
-// Workspace: [chunk offsets (N+1) int32, 256-aligned] [records: Hv x maxch] [q/k images: Hk x maxch]
+// Workspace: [status word, 256 bytes] [chunk offsets (N+1) int32, 256-aligned] [records: Hv x maxch]
+// [q/k images: Hk x maxch] ...
 struct WsLayout {
+  static constexpr size_t OFF = 256;  // chunk offsets; the status word sits at byte 0
   size_t rec, qk, bytes;
   size_t mid;  // calls in stages: the states carried between the stages
   // whole-layer call only: per (sequence, value head) RING chunk slots, each with one 64-bit
@@ -108,7 +110,7 @@ struct WsLayout {
   // workgroup role counters of the stages (all zeroed by the first stage's prep)
   size_t ring, tick, layer_bytes;
   __host__ __device__ WsLayout(int num_seqs, int hv, int hk, int64_t maxch) {
-    rec = (4 * (size_t)(num_seqs + 1) + 255) & ~size_t(255);
+    rec = (OFF + 4 * (size_t)(num_seqs + 1) + 255) & ~size_t(255);
     qk = rec + (size_t)hv * (size_t)maxch * mp::REC_BYTES;
     mid = qk + (size_t)hk * (size_t)maxch * mp::QK_BYTES;
     bytes = mid + (size_t)num_seqs * hv * mp::D * mp::D * 4;
@@ -119,6 +121,30 @@ struct WsLayout {
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+__host__ __device__ inline const int32_t* ws_offsets(const void* ws) {
+  return reinterpret_cast<const int32_t*>(static_cast<const unsigned char*>(ws) + WsLayout::OFF);
+}
+
+// Status word of the workspace (byte 0): sticky bits, cleared by the first launch of every call
+// (the chunk offsets), set with an atomic OR where a bounded wait gives up or an operand leaves
+// the fp16 range of the matrix-core path.  The host reads it after the call
+// (agnes_gdn_workspace_status); the bit values are the AGNES_WS_* constants of the header.
+namespace wsbits {
+constexpr unsigned WAIT_LDS = 1u;       // a wait for another wave of the workgroup gave up
+constexpr unsigned WAIT_EXCHANGE = 2u;  // a wait for another workgroup's partial sums gave up
+constexpr unsigned WAIT_ROLE = 4u;      // a workgroup found no role to claim and did nothing
+constexpr unsigned RANGE = 8u;          // an fp16 operand or the final state left +-65504 / was not finite
+}  // namespace wsbits
+__device__ __forceinline__ void ws_report(void* ws, unsigned bits) {
+  __hip_atomic_fetch_or(static_cast<unsigned*>(ws), bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Poll bound of a wait: the caller's limit (tests force waits to give up with a small one), else
+// the wait's own default.
+__device__ __forceinline__ int wait_bound(unsigned limit, int def) {
+  return limit && limit < (unsigned)def ? (int)limit : def;
+}
+// fp16 range of a value about to become a matrix-core operand.
+__device__ __forceinline__ bool fp16_range(float v) { return __builtin_fabsf(v) <= 65504.f; }
 static inline int64_t max_chunks(int64_t total, int num_seqs) { return (total + mp::C - 1) / mp::C + num_seqs; }
 
 // ---------------------------------------------------------------- helpers
@@ -172,7 +198,8 @@ __device__ __forceinline__ void lds_barrier() {
 
 // ---------------------------------------------------------------- 1. chunk offsets
 __global__ __launch_bounds__(256) void chunk_offsets_kernel(const int32_t* cu, int num_seqs, int64_t total,
-                                                            int32_t* off) {
+                                                            int32_t* off, unsigned* status) {
+  if (threadIdx.x == 0) *status = 0u;
   __shared__ int32_t wsum[4];
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int per = (num_seqs + 255) / 256;
@@ -287,7 +314,7 @@ template <bool FUSED>
 __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6))) void prep_kernel(PrefillArgs a, int64_t maxch) {
   using namespace mp;
   __shared__ PrepSmem sm;
-  const int32_t* off = static_cast<const int32_t*>(a.workspace);
+  const int32_t* off = ws_offsets(a.workspace);
   const WsLayout ws(a.num_seqs, a.hv, a.hk, maxch);
   unsigned char* base = static_cast<unsigned char*>(a.workspace);
   const int grp = a.hv / a.hk;
@@ -318,6 +345,7 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
   const int slot = w >> 2, v = w & 3, ts = tid & 255;
   const int z = rd * PH + slot;
+  bool bad = false;  // a value that leaves the fp16 range on its way to the matrix cores
   const bool act = z < grp;
   const int h = kh * grp + (act ? z : 0);
   unsigned char* rec = base + ws.rec + ((size_t)h * maxch + j) * REC_BYTES;
@@ -467,6 +495,11 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
       const bool isk = i >= C * (D / 8);
       const int r = (i >> 4) & (C - 1), col = 8 * (i & 15);
       const uint4 u = *reinterpret_cast<const uint4*>(isk ? &sm.u.qk.K[r][col] : &sm.u.qk.Q[r][col]);
+      if (!FUSED && r < L) {  // bf16 magnitudes from 65536 up (0x4780) do not fit fp16
+        const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bad |= (wv[e] & 0x7fffu) >= 0x4780u || ((wv[e] >> 16) & 0x7fffu) >= 0x4780u;
+      }
       *reinterpret_cast<h8*>(isk ? &img->K[r][col] : &img->Q[r][col]) =
           FUSED ? __builtin_bit_cast(h8, u) : cvt8(r < L ? u : make_uint4(0, 0, 0, 0));
     }
@@ -492,7 +525,9 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
         const int r = r0 + e;
         const float d = s2 <= r ? __expf(gr[e] - gs) : 0.f;
         sm.u.hd[zz].A[w][4 * lg + e][ln] = s2 < r ? br[e] * d * gk[e] : 0.f;
-        pz[r * LDT + s2] = (_Float16)(s2 <= r ? d * gq[e] : 0.f);
+        const float pv = s2 <= r ? d * gq[e] : 0.f;
+        bad |= !fp16_range(pv);
+        pz[r * LDT + s2] = (_Float16)pv;
       }
     }
   } else {
@@ -554,10 +589,15 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
       const float* xr = &hd.X[bj <= bi ? tri(bi, bj) : 0][r & 15][s0 & 15];
       h8 xv;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xv[e] = (_Float16)(s0 + e <= r ? xr[e] : 0.f);
+      for (int e = 0; e < 8; ++e) {
+        const float xe = s0 + e <= r ? xr[e] : 0.f;
+        bad |= !fp16_range(xe);
+        xv[e] = (_Float16)xe;
+      }
       *reinterpret_cast<h8*>(rec + offsetof(RecImage, X) + (r * LDT + s0) * 2) = xv;
     }
   }
+  if (__any(bad) && lane == 0) ws_report(a.workspace, wsbits::RANGE);
 }
 
 // ---------------------------------------------------------------- 3. scan
@@ -615,11 +655,13 @@ __device__ __forceinline__ h8 kt_operand(const ScanBuf& B, int kt, int ks, int t
 // over the staged output tile, so its writer releases (workgroup scope, LDS) before raising it
 // and its readers acquire after the wait.  The bound (never reached when the flag works) keeps
 // a broken one from hanging the GPU.
-__device__ __forceinline__ void wait_flag(const int* f, int target) {
-  for (int i = 0; i < (1 << 20); ++i) {
+__device__ __forceinline__ void wait_flag(const int* f, int target, const PrefillArgs& a) {
+  const int n = wait_bound(a.wait_limit, 1 << 20);
+  for (int i = 0; i < n; ++i) {
     if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) >= target) return;
     __builtin_amdgcn_s_sleep(1);
   }
+  if ((threadIdx.x & 63) == 0) ws_report(a.workspace, wsbits::WAIT_LDS);
 }
 
 // Gates of the rows a lane holds in result layout (rows 16i + 4g + e of tile i, e = 0..3):
@@ -1027,14 +1069,20 @@ __device__ __forceinline__ void norm_issue(const NormCtx& nc_, const PrefillArgs
 template <int O_DT, int NG>
 __device__ __forceinline__ void norm_finish(const NormCtx& nc_, const PrefillArgs& a, const Geo& G, int c, int lane,
                                             NormIn<NG>& g, const float (&x)[NG][8], const float (&ss)[NG]) {
-  for (int it = 0; it < (1 << 24); ++it) {
+  const int bound = wait_bound(a.wait_limit, 1 << 24);
+  bool ready = false;
+  for (int it = 0; it < bound; ++it) {
     bool ok = true;
 #pragma unroll
     for (int i = 0; i < mp::NB - 1; ++i) ok = ok && (unsigned)g.w[i] == (unsigned)(c + nc_.cbase + 1);
-    if (__all(ok)) break;
+    if (__all(ok)) {
+      ready = true;
+      break;
+    }
     __builtin_amdgcn_s_sleep(1);
     norm_load_words(nc_, c, lane, g);
   }
+  if (!ready && lane == 0) ws_report(a.workspace, wsbits::WAIT_EXCHANGE);
   float oth = 0.f;
 #pragma unroll
   for (int i = 0; i < mp::NB - 1; ++i) oth += __uint_as_float((unsigned)(g.w[i] >> 32));
@@ -1081,7 +1129,7 @@ __device__ __forceinline__ void tile_wave(ScanSmem& sm, const PrefillArgs& a, co
       for (int e = 0; e < 8; ++e) xa[q][e] = xb[q][e];
     }
     if (c >= 1) {
-      wait_flag(&sm.os_ready, c);  // chunk c - 1 staged
+      wait_flag(&sm.os_ready, c, a);  // chunk c - 1 staged
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
       tile_take<NG>(sm.Os, r0, lane, xb);
       row_sums<NG>(xb, sb);
@@ -1205,7 +1253,7 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
   using namespace mp;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   ScanSmem& sm = *reinterpret_cast<ScanSmem*>(smem_raw);
-  const int32_t* off = static_cast<const int32_t*>(a.workspace);
+  const int32_t* off = ws_offsets(a.workspace);
   const unsigned char* ws = static_cast<const unsigned char*>(a.workspace);
   const WsLayout wl(a.num_seqs, a.hv, a.hk, maxch);
 
@@ -1236,19 +1284,25 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
       unsigned* cnt = reinterpret_cast<unsigned*>(const_cast<unsigned char*>(ws) + wl.tick) + 8 * a.stage;
       const unsigned cap = nblk >> 3;
       unsigned role = 0;
+      bool claimed = true;
       if ((nblk % (8u * NB * (unsigned)(a.hv / a.hk))) == 0) {
         const unsigned x = __builtin_amdgcn_s_getreg(0xf814) & 7u;  // hwreg(HW_REG_XCC_ID)
         unsigned t = __hip_atomic_fetch_add(&cnt[x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         unsigned y = x;
         if (t >= cap) {  // this XCD's range is used up: another range still has a role for every such claim
           bool got = false;
-          for (int it = 0; it < (1 << 16) && !got; ++it)
+          const int bound = wait_bound(a.wait_limit, 1 << 16);
+          for (int it = 0; it < bound && !got; ++it)
             for (y = 0; y < 8 && !got; ++y) {
               if (__hip_atomic_load(&cnt[y], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= cap) continue;
               t = __hip_atomic_fetch_add(&cnt[y], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
               got = t < cap;
             }
           if (got) --y;  // the loop advanced past the range it claimed from
+          if (!got) {  // (never when every workgroup claims once): no role, nothing is touched
+            ws_report(a.workspace, wsbits::WAIT_ROLE);
+            claimed = false;
+          }
         }
         // claim t of range y: its key groups are y, y + 8, y + 16, ... (dealt as the block ids)
         const unsigned kgw2 = (unsigned)(NB * (a.hv / a.hk));
@@ -1256,10 +1310,11 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
       } else {
         role = __hip_atomic_fetch_add(&cnt[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // plain start order
       }
-      sm.ticket = role;
+      sm.ticket = claimed ? role : ~0u;
     }
     __syncthreads();
     lid = sm.ticket;
+    if (lid == ~0u) return;
   }
   Geo G;
   const int blk = lid % NB;
@@ -1320,6 +1375,17 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
         chain_step<FUSED>(sm.B[c & 1], sm.X[c & 1], sm.X[(c + 1) & 1], t0, lane, ln, lg, sacc, sb, &sm.ks_done[pr], c);
       lds_barrier();
     }
+    // An fp16 operand out of range anywhere in the sequence leaves the state out of range or not
+    // finite (inf and NaN persist through the decay and the updates), so one check at the end
+    // covers the state and U operands of every chunk.
+    bool in_range = true;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) in_range = in_range && fp16_range(sacc[t][kt][e]);
+    if (!__all(in_range) && lane == 0) ws_report(a.workspace, wsbits::RANGE);
     if (a.s1) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t)
@@ -1340,7 +1406,7 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
     for (int c = 0; c < nc + 1; ++c) {
       // Start once the chain wave is past K S^T: run beside it, the output wave's LDS reads
       // slow the chain's operand reads (the serial path) by about a third.
-      if (c < nc) wait_flag(&sm.ks_done[pr], c + 1);
+      if (c < nc) wait_flag(&sm.ks_done[pr], c + 1, a);
       if (c >= 1) o_step<O_DT, NORM>(sm.X[(c - 1) & 1], sm.Os, &sm.os_ready, a, G, c - 1, t0, qs, pa, ge);
       if (c < nc) qs_step(sm.B[c & 1], sm.X[c & 1], t0, lane, ln, lg, qs, pa, ge);
       lds_barrier();
@@ -1422,7 +1488,7 @@ static hipError_t scan_attr() {
 
 static hipError_t launch_offsets(const PrefillArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(chunk_offsets_kernel, dim3(1), dim3(256), 0, st, a.cu, a.num_seqs, a.total,
-                     static_cast<int32_t*>(a.workspace));
+                     const_cast<int32_t*>(ws_offsets(a.workspace)), static_cast<unsigned*>(a.workspace));
   return hipGetLastError();
 }
 

@@ -20,9 +20,10 @@
  *     dimension contiguous.  Tensor base pointers must be 16-byte aligned and
  *     element strides multiples of 8 elements (vector loads of 16 bytes).
  *   - The caller owns every buffer, including the prefill workspace.  The
- *     library never allocates, frees or synchronises; every call is enqueued
- *     on `stream` (a hipStream_t; NULL = the default stream) and returns
- *     before the GPU work ends.
+ *     library never allocates, frees or synchronises (the status query
+ *     agnes_gdn_workspace_status aside); every call is enqueued on `stream` (a
+ *     hipStream_t; NULL = the default stream) and returns before the GPU work
+ *     ends.
  *   - All argument checks happen before anything is launched.  On a failed
  *     check the call returns a negative agnes_status, launches nothing and
  *     leaves every output untouched.  A launch failure returns AGNES_ERR_HIP and
@@ -395,6 +396,57 @@ int agnes_attn_decode(const void* q, int64_t q_stride, const void* k, int64_t k_
                       int num_q_heads, int num_kv_heads, int head_dim, int rot_dim,
                       float rope_base, float norm_eps, float scale, void* o, agnes_dtype o_dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Status of a bf16 prefill call (agnes_gdn_prefill_chunked with in_dtype BF16,
+ * agnes_gdn_prefill_fused, agnes_gdn_layer_prefill): the call clears a status word at the start
+ * of its workspace and its kernels set these sticky bits in it.
+ *
+ *   AGNES_WS_WAIT_LDS       a bounded wait for another wave of the same workgroup gave up
+ *   AGNES_WS_WAIT_EXCHANGE  (whole-layer call) a bounded wait for the partial sums of squares of
+ *                           another workgroup of the same value head gave up
+ *   AGNES_WS_WAIT_ROLE      (whole-layer call) a workgroup found no role to take and returned
+ *                           without touching any buffer
+ *   AGNES_WS_RANGE          a value on the fp16 matrix-core path was outside +-65504 or not
+ *                           finite: a bf16 q/k input of magnitude >= 65536 (plain call), an
+ *                           entry of the chunk-local factors P = exp(gamma_r - gamma_s) q_r.k_s
+ *                           or X = (I + A)^-1 (checked where they are formed: positive log-decays
+ *                           whose sum within a chunk exceeds ~11 overflow P), or the state of a
+ *                           sequence at its end (an fp16 state or U operand out of range anywhere
+ *                           in the sequence leaves the fp32 state non-finite there).  Inputs that
+ *                           are not finite also set it.
+ *
+ * A wait gives up only after its bound (about 10^6..10^7 polls of ~30 ns): with a correct
+ * workspace and grid it never does.  Any bit set means the outputs of that call are not
+ * reliable.  The fp16 domain in which every bit stays clear: |q|, |k| < 65504 (the layer's q
+ * and k are unit vectors), |v|, |state| and |U| (the delta-corrected values) < 65504, and
+ * log-decays g <= 0 or small enough that no chunk's in-chunk decay sum exceeds ~11.
+ */
+enum {
+  AGNES_WS_WAIT_LDS = 1,
+  AGNES_WS_WAIT_EXCHANGE = 2,
+  AGNES_WS_WAIT_ROLE = 4,
+  AGNES_WS_RANGE = 8
+};
+
+/*
+ * agnes_gdn_workspace_status — waits for the work enqueued on `stream` to finish (this call
+ * synchronises `stream`, unlike every other call), then stores the status word of a bf16
+ * prefill workspace (the first 4 bytes of `workspace`, device memory) in *flags (host).  Call it
+ * after the prefill call whose workspace it is; another call on the same workspace clears it.
+ * Returns AGNES_ERR_INVALID_ARG for a NULL or misaligned pointer, AGNES_ERR_HIP if the copy
+ * fails.
+ */
+int agnes_gdn_workspace_status(const void* workspace, uint32_t* flags, void* stream);
+
+/*
+ * agnes_gdn_set_wait_limit — process-wide bound on the polls of every bounded wait of the bf16
+ * prefill calls launched after it (0: each wait's own bound, the default).  For tests and
+ * debugging of the status bits: a small bound makes the waits give up, the kernels still end
+ * normally, and the results are then unreliable.  Not meant to change while calls are being
+ * launched from other threads.  Returns AGNES_OK.
+ */
+int agnes_gdn_set_wait_limit(uint32_t polls);
 
 /*
  * Measurement kernels: the two ceilings the benchmark reports its roofline fractions against,

@@ -314,3 +314,22 @@ def test_attn_decode_checks(lib):
     assert adec(lib) == WS
     assert adec(lib, ws=P[10], wsb=need - 1) == WS
     assert lib.agnes_gdn_last_hip_error() == 0
+
+
+def test_status_and_measurement_calls_check_their_arguments(lib):
+    """The status query, the wait-limit hook and the two measurement kernels reject bad
+    arguments before touching the device."""
+    import ctypes
+    flags = ctypes.c_uint32(7)
+    assert lib.agnes_gdn_workspace_status(None, ctypes.addressof(flags), None) == INV
+    assert lib.agnes_gdn_workspace_status(P[0], None, None) == INV
+    assert lib.agnes_gdn_workspace_status(P[0] + 2, ctypes.addressof(flags), None) == INV  # misaligned
+    assert flags.value == 7
+    assert lib.agnes_gdn_set_wait_limit(0) == 0
+    assert lib.agnes_gdn_ceiling_rmw_stream(None, 1024, None) == INV
+    assert lib.agnes_gdn_ceiling_rmw_stream(P[0], 1000, None) == INV                # not a multiple of 16
+    assert lib.agnes_gdn_ceiling_rmw_stream(P[0] + 8, 1024, None) == INV            # misaligned
+    assert lib.agnes_gdn_ceiling_mfma(None, 4, 4, None) == INV
+    assert lib.agnes_gdn_ceiling_mfma(P[0], 0, 4, None) == INV
+    assert lib.agnes_gdn_ceiling_mfma(P[0], 4, (1 << 20) + 1, None) == INV
+    assert lib.agnes_gdn_last_hip_error() == 0
