@@ -24,7 +24,7 @@ from . import _lib
 __all__ = ["conv", "prefill_chunked", "prefill_fused", "decode_step", "gated_rmsnorm", "decode_fused",
            "prefill_workspace_size", "layer_prefill", "layer_prefill_workspace_size", "attn_prefill", "attn_prefill_workspace_size",
            "attn_decode", "attn_decode_workspace_size", "ceiling_rmw_stream", "ceiling_mfma", "workspace_status", "set_wait_limit",
-           "WS_WAIT_LDS", "WS_WAIT_EXCHANGE", "WS_WAIT_ROLE", "WS_RANGE",
+           "WS_WAIT_LDS", "WS_WAIT_EXCHANGE", "WS_WAIT_ROLE", "WS_RANGE", "layer_prefill_noalloc",
            "AgnesError", "version", "LIB_PATH"]
 
 LIB_PATH = _lib.LIB_PATH
@@ -518,3 +518,35 @@ def set_wait_limit(polls):
     wait's own bound).  For tests of the status bits only: with a small bound the waits give up
     and the results are unreliable."""
     _check("agnes_gdn_set_wait_limit", _lib.load().agnes_gdn_set_wait_limit(int(polls)))
+
+
+def layer_prefill_noalloc(x, conv_weight, g, beta, cu_seqlens, z, norm_weight, y, *, num_k_heads, conv_bias=None,
+                          conv_state=None, initial_state=None, final_state=None, scale=1.0, l2norm_eps=1e-6,
+                          norm_eps=1e-6, o=None):
+    """``layer_prefill`` for callers that cannot allocate: the library's fixed per-device workspace
+    (64 MiB: one sequence of up to about 2400 tokens) replaces the workspace argument, and nothing is
+    allocated, here or in the library.  Every output (y, and final_state / o if wanted) is given by
+    the caller.  Calls that overlap in time on one device race.  Returns y."""
+    T, C = x.shape
+    Hk = num_k_heads
+    Hv = C // HEAD_DIM - 2 * Hk
+    if Hv <= 0 or C != (2 * Hk + Hv) * HEAD_DIM:
+        raise ValueError(f"x: {C} channels do not hold 2 x {Hk} key heads and whole value heads")
+    if y is None or tuple(y.shape) != (T, Hv, HEAD_DIM) or not y.is_contiguous():
+        raise ValueError(f"y: contiguous [{T}, {Hv}, 128] expected")
+    for t, name in ((o, "o"),):
+        if t is not None and (not t.is_contiguous() or t.dtype != y.dtype or tuple(t.shape) != (T, Hv, HEAD_DIM)):
+            raise ValueError(f"{name}: contiguous {y.dtype} [{T}, {Hv}, 128] expected")
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    n = cu_seqlens.numel() - 1
+    for s, name in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if s is not None and (s.dtype != torch.float32 or not s.is_contiguous()
+                              or tuple(s.shape) != (n, Hv, HEAD_DIM, HEAD_DIM)):
+            raise ValueError(f"{name}: expected contiguous fp32 [{n}, {Hv}, 128, 128]")
+    st = _lib.load().agnes_gdn_layer_prefill_noalloc(
+        _ptr(x), _rows(x, "x", C), _dt(x), _ptr(conv_weight), _ptr(conv_bias), _ptr(conv_state), _ptr(g), _ptr(beta),
+        _ptr(cu_seqlens), n, T, Hk, Hv, HEAD_DIM, scale, l2norm_eps, _ptr(initial_state), _ptr(final_state),
+        _ptr(z), _heads(z, "z", Hv), _ptr(norm_weight), norm_eps, _ptr(y), _ptr(o), _dt(y), _stream(x.device))
+    _check("agnes_gdn_layer_prefill_noalloc", st)
+    return y

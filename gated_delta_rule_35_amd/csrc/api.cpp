@@ -421,14 +421,18 @@ AGNES_API size_t agnes_gdn_layer_prefill_workspace_size(int num_seqs, int64_t to
   return agnes::layer_prefill_workspace(num_seqs, total_tokens, num_k_heads, num_v_heads);
 }
 
-AGNES_API int agnes_gdn_layer_prefill(const void* x, int64_t x_token_stride, agnes_dtype dtype,
-                                      const void* conv_weight, const void* conv_bias, void* conv_state,
-                                      const float* g, const float* beta, const int32_t* cu_seqlens, int num_seqs,
-                                      int64_t total_tokens, int num_k_heads, int num_v_heads, int head_dim,
-                                      float scale, float l2norm_eps, const float* initial_state, float* final_state,
-                                      const void* z, int64_t z_token_stride, const void* norm_weight, float norm_eps,
-                                      void* y, void* o, agnes_dtype out_dtype, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
+namespace agnes {
+int hip_report(hipError_t e) { return hip_status(e); }
+
+// agnes_gdn_layer_prefill's checks and launch; single_stage runs the call in one stage (no side
+// stream, nothing created on first use).
+int layer_prefill_checked(const void* x, int64_t x_token_stride, int dtype, const void* conv_weight,
+                          const void* conv_bias, void* conv_state, const float* g, const float* beta,
+                          const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens, int num_k_heads,
+                          int num_v_heads, int head_dim, float scale, float l2norm_eps, const float* initial_state,
+                          float* final_state, const void* z, int64_t z_token_stride, const void* norm_weight,
+                          float norm_eps, void* y, void* o, int out_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream, bool single_stage) {
   if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return AGNES_ERR_INVALID_ARG;
   if (num_seqs < 0 || total_tokens < 0 || num_k_heads <= 0 || num_v_heads <= 0) return AGNES_ERR_INVALID_ARG;
   if (head_dim != kHeadDim || num_v_heads % num_k_heads || dtype != AGNES_BF16) return AGNES_ERR_UNSUPPORTED;
@@ -478,7 +482,23 @@ AGNES_API int agnes_gdn_layer_prefill(const void* x, int64_t x_token_stride, agn
   a.norm_w = norm_weight;
   a.norm_eps = norm_eps;
   a.y = y;
+  a.single_stage = single_stage;
   return hip_status(agnes::launch_layer_prefill(a, static_cast<hipStream_t>(stream)));
+}
+}  // namespace agnes
+
+AGNES_API int agnes_gdn_layer_prefill(const void* x, int64_t x_token_stride, agnes_dtype dtype,
+                                      const void* conv_weight, const void* conv_bias, void* conv_state,
+                                      const float* g, const float* beta, const int32_t* cu_seqlens, int num_seqs,
+                                      int64_t total_tokens, int num_k_heads, int num_v_heads, int head_dim,
+                                      float scale, float l2norm_eps, const float* initial_state, float* final_state,
+                                      const void* z, int64_t z_token_stride, const void* norm_weight, float norm_eps,
+                                      void* y, void* o, agnes_dtype out_dtype, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  return agnes::layer_prefill_checked(x, x_token_stride, dtype, conv_weight, conv_bias, conv_state, g, beta,
+                                      cu_seqlens, num_seqs, total_tokens, num_k_heads, num_v_heads, head_dim, scale,
+                                      l2norm_eps, initial_state, final_state, z, z_token_stride, norm_weight, norm_eps,
+                                      y, o, out_dtype, workspace, workspace_bytes, stream, false);
 }
 
 AGNES_API int agnes_gdn_ceiling_rmw_stream(void* buf, size_t bytes, void* stream) {

@@ -65,10 +65,21 @@ struct PrefillArgs {
   int part_lo = 0, part_hi = 1, part_den = 1;
   int stage = 0;          // whole-layer call: this stage's workgroup ticket counter
   unsigned wait_limit = 0;  // bounded waits poll at most this often (0: each wait's own bound)
+  bool single_stage = false;  // run in one stage: no side stream, nothing created on first use
 };
 
 // Process-wide poll bound handed to every bf16 prefill launch (agnes_gdn_set_wait_limit).
 unsigned prefill_wait_limit();
+// The C-ABI status of a HIP error (recorded for agnes_gdn_last_hip_error on this thread).
+int hip_report(hipError_t e);
+// agnes_gdn_layer_prefill's argument checks and launch, on a given workspace.
+int layer_prefill_checked(const void* x, int64_t x_token_stride, int dtype, const void* conv_weight,
+                          const void* conv_bias, void* conv_state, const float* g, const float* beta,
+                          const int32_t* cu_seqlens, int num_seqs, int64_t total_tokens, int num_k_heads,
+                          int num_v_heads, int head_dim, float scale, float l2norm_eps, const float* initial_state,
+                          float* final_state, const void* z, int64_t z_token_stride, const void* norm_weight,
+                          float norm_eps, void* y, void* o, int out_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream, bool single_stage);
 
 struct DecodeArgs {
   const void* q;

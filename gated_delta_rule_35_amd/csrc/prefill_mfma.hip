@@ -1579,6 +1579,7 @@ static hipError_t side_queue(SideQueue*& q) {
 template <int O_DT, bool FUSED, bool NORM>
 static hipError_t launch_staged(const PrefillArgs& a, hipStream_t st) {
   if (a.num_seqs == 0) return hipSuccess;
+  if (a.single_stage) return launch_o<O_DT, FUSED, NORM>(a, st);
   std::lock_guard<std::mutex> lock(g_side_mu);
   SideQueue* q = nullptr;
   hipError_t e = side_queue(q);

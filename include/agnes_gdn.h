@@ -307,6 +307,30 @@ int agnes_gdn_layer_prefill(const void* x, int64_t x_token_stride, agnes_dtype d
                             size_t workspace_bytes, void* stream);
 
 /*
+ * agnes_gdn_layer_prefill_noalloc — agnes_gdn_layer_prefill for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same arguments and results without the workspace, which is instead a fixed
+ * 64 MiB array in device memory that the library's code object brings with it, one per device
+ * (held until the process ends).  The call allocates, frees and creates nothing: it always runs
+ * in one stage (no side stream) and looks the array's address up on its first call on a device.
+ *
+ *   Supported: problems whose agnes_gdn_layer_prefill_workspace_size is at most 64 MiB (one
+ *   sequence of up to about 2400 tokens of the 16 / 48-head layer); larger ones return
+ *   AGNES_ERR_UNSUPPORTED and launch nothing.
+ *   Every call on a device uses that device's one array: calls that may overlap in time on one
+ *   device (on different streams, or from several threads) race and give unspecified results.
+ *   Each call clears what it needs cleared; the array keeps the last call's contents.
+ */
+int agnes_gdn_layer_prefill_noalloc(const void* x, int64_t x_token_stride, agnes_dtype dtype,
+                                    const void* conv_weight, const void* conv_bias, void* conv_state,
+                                    const float* g, const float* beta, const int32_t* cu_seqlens,
+                                    int num_seqs, int64_t total_tokens, int num_k_heads,
+                                    int num_v_heads, int head_dim, float scale, float l2norm_eps,
+                                    const float* initial_state, float* final_state, const void* z,
+                                    int64_t z_token_stride, const void* norm_weight, float norm_eps,
+                                    void* y, void* o, agnes_dtype out_dtype, void* stream);
+
+/*
  * agnes_attn_prefill_workspace_size — bytes of device workspace agnes_attn_prefill
  * needs (0 for an empty batch).
  */

@@ -333,3 +333,14 @@ def test_status_and_measurement_calls_check_their_arguments(lib):
     assert lib.agnes_gdn_ceiling_mfma(P[0], 0, 4, None) == INV
     assert lib.agnes_gdn_ceiling_mfma(P[0], 4, (1 << 20) + 1, None) == INV
     assert lib.agnes_gdn_last_hip_error() == 0
+
+
+def test_noalloc_refuses_a_workspace_beyond_its_own_on_the_host(lib):
+    """The fixed-workspace call rejects a problem whose workspace exceeds its 64 MiB before any
+    device call (the size query is host arithmetic)."""
+    T = 8192
+    assert lib.agnes_gdn_layer_prefill_workspace_size(1, T, 16, 48, 128) > (64 << 20)
+    st = lib.agnes_gdn_layer_prefill_noalloc(P[0], 80 * 128, BF16, P[1], None, None, P[2], P[3], P[4], 1, T, 16, 48,
+                                             128, 1.0, 1e-6, None, None, P[5], 48 * 128, P[6], 1e-6, P[7], None, F32,
+                                             None)
+    assert st == UNS
