@@ -1,4 +1,5 @@
 """ctypes view of libagnes_gdn.so (the C ABI declared in include/agnes_gdn.h)."""
+import atexit
 import ctypes
 import os
 
@@ -53,6 +54,7 @@ SIGNATURES = {
     "agnes_gdn_set_wait_limit": (c_int, [ctypes.c_uint32]),
     "agnes_gdn_ceiling_rmw_stream": (c_int, [c_void_p, c_size_t, c_void_p]),
     "agnes_gdn_ceiling_mfma": (c_int, [c_void_p, c_int, c_int, c_void_p]),
+    "agnes_gdn_release": (c_int, []),
     "agnes_gdn_status_string": (ctypes.c_char_p, [c_int]),
     "agnes_gdn_last_hip_error": (c_int, []),
     "agnes_gdn_version": (ctypes.c_char_p, []),
@@ -79,4 +81,14 @@ def load():
             fn.restype = res
             fn.argtypes = args
         _lib = lib
+        # release the library's side streams and events while the HIP runtime (and any profiler
+        # attached to it) is still whole: interpreter exit handlers run before the C runtime's
+        atexit.register(_release_at_exit)
     return _lib
+
+
+def _release_at_exit():
+    try:
+        _lib.agnes_gdn_release()
+    except Exception:  # pragma: no cover - nothing to do at exit
+        pass

@@ -527,3 +527,5 @@ AGNES_API int agnes_gdn_set_wait_limit(uint32_t polls) {
   g_wait_limit.store(polls, std::memory_order_relaxed);
   return AGNES_OK;
 }
+
+AGNES_API int agnes_gdn_release(void) { return hip_status(agnes::release_side_queues()); }

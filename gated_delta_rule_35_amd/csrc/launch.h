@@ -189,6 +189,7 @@ hipError_t launch_layer_prefill(const PrefillArgs& a, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_gated_rmsnorm(const NormArgs& a, hipStream_t s);
 hipError_t launch_decode_fused(const FusedDecodeArgs& a, hipStream_t s);
+hipError_t release_side_queues();
 hipError_t launch_rmw_stream(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_mfma_peak(float* sink, int blocks, int iters, hipStream_t s);
 

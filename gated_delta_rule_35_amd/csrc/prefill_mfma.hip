@@ -1576,6 +1576,30 @@ static hipError_t side_queue(SideQueue*& q) {
   return hipStreamCreateWithFlags(&q->s, hipStreamNonBlocking);  // default priority
 }
 
+// Destroys the side queues (stream and events) the calls in stages created, after waiting for
+// their work; the next such call creates them again.  No HIP call at all when none exists.
+hipError_t release_side_queues() {
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  bool any = false;
+  for (const SideQueue& q : g_side) any = any || q.s != nullptr;
+  if (!any) return hipSuccess;
+  int cur = 0;
+  hipError_t first = hipGetDevice(&cur);
+  for (int d = 0; d < 64; ++d) {
+    SideQueue& q = g_side[d];
+    if (!q.s) continue;
+    hipError_t e = hipSetDevice(d);
+    if (e == hipSuccess) e = hipStreamSynchronize(q.s);
+    if (e == hipSuccess) e = hipStreamDestroy(q.s);
+    for (int k = 0; k < NSTAGE && e == hipSuccess; ++k)
+      if (q.prepped[k]) e = hipEventDestroy(q.prepped[k]);
+    if (first == hipSuccess) first = e;
+    q = SideQueue{};
+  }
+  const hipError_t e = hipSetDevice(cur);
+  return first != hipSuccess ? first : e;
+}
+
 template <int O_DT, bool FUSED, bool NORM>
 static hipError_t launch_staged(const PrefillArgs& a, hipStream_t st) {
   if (a.num_seqs == 0) return hipSuccess;

@@ -492,6 +492,16 @@ int agnes_gdn_set_wait_limit(uint32_t polls);
 int agnes_gdn_ceiling_rmw_stream(void* buf, size_t bytes, void* stream);
 int agnes_gdn_ceiling_mfma(float* sink, int blocks, int iters, void* stream);
 
+/*
+ * agnes_gdn_release — destroys the HIP objects the library keeps between calls: the side stream
+ * and the two events per device that the calls in two stages create on first use (after waiting
+ * for the work on that stream).  A later call in two stages creates them again.  Call it when no
+ * call of the library is in flight, e.g. before the process exits, so that no library handle is
+ * left for the runtime's own teardown; it makes no HIP call when nothing was created.  Returns
+ * AGNES_OK, or AGNES_ERR_HIP if a destroy fails.
+ */
+int agnes_gdn_release(void);
+
 const char* agnes_gdn_status_string(int status);
 
 /* hipError_t of the last AGNES_ERR_HIP returned on the calling thread (0 if none). */

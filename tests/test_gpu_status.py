@@ -128,3 +128,19 @@ def test_fp16_range_is_reported(what):
     flags = gdn.workspace_status(ws)
     print(f"{what}: status {flags:#x}")
     assert flags & gdn.WS_RANGE
+
+
+def test_release_then_calls_in_two_stages_again():
+    """agnes_gdn_release destroys the side stream and events of the calls in two stages; the next
+    such call creates them again and gives the same result bit for bit."""
+    rng = np.random.default_rng(904)
+    d = _layer_case(rng, [2000, 700], 2, 6)
+    ws = _ws(d)
+    y1, f1 = _layer(d, ws)
+    y1, f1 = host(y1), host(f1)
+    assert gdn._lib.load().agnes_gdn_release() == 0
+    assert gdn._lib.load().agnes_gdn_release() == 0  # nothing left: no HIP call
+    y2, f2 = _layer(d, ws)
+    np.testing.assert_array_equal(host(y2), y1)
+    np.testing.assert_array_equal(host(f2), f1)
+    assert gdn.workspace_status(ws) == 0
