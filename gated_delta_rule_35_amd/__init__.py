@@ -17,13 +17,15 @@ The global attention layer of the same model (model card, rows 全局注意力 a
   attn_prefill    q/k RMS-norm + partial three-axis rotary, causal GQA softmax attention, sigmoid gate
   attn_decode     one token per entry against a bf16 KV cache (the new k, v written at index len)
 """
+import ctypes
+
 import torch
 
 from . import _lib
 
 __all__ = ["conv", "prefill_chunked", "prefill_fused", "decode_step", "gated_rmsnorm", "decode_fused",
            "prefill_workspace_size", "layer_prefill", "layer_prefill_workspace_size", "attn_prefill", "attn_prefill_workspace_size",
-           "attn_decode", "attn_decode_workspace_size", "ceiling_rmw_stream", "ceiling_mfma", "workspace_status", "set_wait_limit",
+           "attn_decode", "attn_decode_workspace_size", "ceiling_rmw_stream", "ceiling_mfma", "workspace_status", "set_wait_limit", "set_prefill_stages",
            "WS_WAIT_LDS", "WS_WAIT_EXCHANGE", "WS_WAIT_ROLE", "WS_RANGE", "layer_prefill_noalloc",
            "AgnesError", "version", "LIB_PATH"]
 
@@ -505,7 +507,6 @@ def workspace_status(workspace):
     """Status bits (WS_WAIT_LDS, WS_WAIT_EXCHANGE, WS_WAIT_ROLE, WS_RANGE) that the last bf16 prefill
     call on ``workspace`` (a device uint8 tensor passed as its workspace) left in it; 0 when all is
     well.  Synchronises the current stream."""
-    import ctypes
     flags = ctypes.c_uint32(0)
     _check("agnes_gdn_workspace_status",
            _lib.load().agnes_gdn_workspace_status(workspace.data_ptr(), ctypes.addressof(flags),
@@ -519,6 +520,14 @@ def set_wait_limit(polls):
     and the results are unreliable."""
     _check("agnes_gdn_set_wait_limit", _lib.load().agnes_gdn_set_wait_limit(int(polls)))
 
+
+
+def set_prefill_stages(cuts=(24,)):
+    """Process-wide stage cuts of the bf16 prefill calls, in 1/40ths of each sequence's chunks
+    (strictly increasing inside (0, 40), at most 7; () runs every call in one stage).  The
+    default (24,) runs two stages.  The cuts change the schedule only, not the results."""
+    arr = (ctypes.c_int32 * max(len(cuts), 1))(*[int(c) for c in cuts])
+    _check("agnes_gdn_set_prefill_stages", _lib.load().agnes_gdn_set_prefill_stages(arr, len(cuts)))
 
 def layer_prefill_noalloc(x, conv_weight, g, beta, cu_seqlens, z, norm_weight, y, *, num_k_heads, conv_bias=None,
                           conv_state=None, initial_state=None, final_state=None, scale=1.0, l2norm_eps=1e-6,

@@ -52,6 +52,7 @@ SIGNATURES = {
                                   c_void_p, c_size_t, c_void_p]),
     "agnes_gdn_workspace_status": (c_int, [c_void_p, c_void_p, c_void_p]),
     "agnes_gdn_set_wait_limit": (c_int, [ctypes.c_uint32]),
+    "agnes_gdn_set_prefill_stages": (c_int, [c_void_p, c_int]),
     "agnes_gdn_ceiling_rmw_stream": (c_int, [c_void_p, c_size_t, c_void_p]),
     "agnes_gdn_ceiling_mfma": (c_int, [c_void_p, c_int, c_int, c_void_p]),
     "agnes_gdn_release": (c_int, []),

@@ -528,4 +528,8 @@ AGNES_API int agnes_gdn_set_wait_limit(uint32_t polls) {
   return AGNES_OK;
 }
 
+AGNES_API int agnes_gdn_set_prefill_stages(const int32_t* cuts, int n_cuts) {
+  return agnes::set_stage_cuts(cuts, n_cuts) ? AGNES_OK : AGNES_ERR_INVALID_ARG;
+}
+
 AGNES_API int agnes_gdn_release(void) { return hip_status(agnes::release_side_queues()); }

@@ -190,6 +190,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 hipError_t launch_gated_rmsnorm(const NormArgs& a, hipStream_t s);
 hipError_t launch_decode_fused(const FusedDecodeArgs& a, hipStream_t s);
 hipError_t release_side_queues();
+bool set_stage_cuts(const int* cuts, int n);
 hipError_t launch_rmw_stream(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_mfma_peak(float* sink, int blocks, int iters, hipStream_t s);
 

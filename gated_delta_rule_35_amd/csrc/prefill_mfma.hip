@@ -1544,23 +1544,24 @@ static hipError_t launch_o(const PrefillArgs& a, hipStream_t st) {
 // a scan runs ~3x slower than alone, so the first part is the larger: 3/5 of the chunks.  More
 // stages shorten the exposed first prep but cost more at each hand-over than they save (at
 // T = 8192: two stages 356 us, three 373-380 us, four 398 us).  Used when the scan leaves a
-// quarter of the chip free and sequences are long enough.
-#ifndef GDN_SPLIT_CUTS
-#define GDN_SPLIT_CUTS 24
-#endif
-constexpr int SPLIT_DEN = 40;                          // stage boundaries in 1/40 of each sequence's chunks
-constexpr int SPLIT_CUT[] = {GDN_SPLIT_CUTS};          // stage k covers [cut[k-1], cut[k])
-constexpr int NSTAGE = (int)(sizeof(SPLIT_CUT) / sizeof(int)) + 1;
-static_assert(NSTAGE <= 8, "the workspace holds role counters for 8 stages");
+// quarter of the chip free and sequences are long enough.  The cuts are a process-wide setting
+// (agnes_gdn_set_prefill_stages), read under the side-queue lock at each launch.
+constexpr int SPLIT_DEN = 40;    // stage boundaries in 1/40 of each sequence's chunks
+constexpr int MAX_STAGES = 8;    // the workspace holds role counters for 8 stages
+struct StageCuts {
+  int n = 1;                     // number of cuts: the call runs in n + 1 stages
+  int cut[MAX_STAGES - 1] = {24};  // stage k covers [cut[k-1], cut[k]) of SPLIT_DEN
+};
 
 namespace {
 struct SideQueue {
   hipStream_t s = nullptr;
-  hipEvent_t prepped[NSTAGE] = {};
+  hipEvent_t prepped[MAX_STAGES] = {};
   int cus = 0;
 };
 std::mutex g_side_mu;  // held while a call enqueues: the side queue's events are shared
 SideQueue g_side[64];
+StageCuts g_cuts;      // under g_side_mu
 }  // namespace
 
 static hipError_t side_queue(SideQueue*& q) {
@@ -1571,7 +1572,7 @@ static hipError_t side_queue(SideQueue*& q) {
   q = &g_side[dev];
   if (q->s) return hipSuccess;
   if ((e = hipDeviceGetAttribute(&q->cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-  for (int k = 0; k < NSTAGE; ++k)
+  for (int k = 0; k < MAX_STAGES; ++k)
     if ((e = hipEventCreate(&q->prepped[k])) != hipSuccess) return e;
   return hipStreamCreateWithFlags(&q->s, hipStreamNonBlocking);  // default priority
 }
@@ -1591,7 +1592,7 @@ hipError_t release_side_queues() {
     hipError_t e = hipSetDevice(d);
     if (e == hipSuccess) e = hipStreamSynchronize(q.s);
     if (e == hipSuccess) e = hipStreamDestroy(q.s);
-    for (int k = 0; k < NSTAGE && e == hipSuccess; ++k)
+    for (int k = 0; k < MAX_STAGES && e == hipSuccess; ++k)
       if (q.prepped[k]) e = hipEventDestroy(q.prepped[k]);
     if (first == hipSuccess) first = e;
     q = SideQueue{};
@@ -1600,29 +1601,45 @@ hipError_t release_side_queues() {
   return first != hipSuccess ? first : e;
 }
 
+// Sets the stage cuts of the later calls: n cuts strictly increasing inside (0, SPLIT_DEN),
+// n < MAX_STAGES (n = 0: one stage).  False, and nothing changed, for any other list.
+bool set_stage_cuts(const int* cuts, int n) {
+  if (n < 0 || n >= MAX_STAGES || (n > 0 && !cuts)) return false;
+  for (int i = 0; i < n; ++i)
+    if (cuts[i] <= (i ? cuts[i - 1] : 0) || cuts[i] >= SPLIT_DEN) return false;
+  std::lock_guard<std::mutex> lock(g_side_mu);
+  g_cuts = StageCuts{};
+  g_cuts.n = n;
+  for (int i = 0; i < n; ++i) g_cuts.cut[i] = cuts[i];
+  return true;
+}
+
 template <int O_DT, bool FUSED, bool NORM>
 static hipError_t launch_staged(const PrefillArgs& a, hipStream_t st) {
   if (a.num_seqs == 0) return hipSuccess;
   if (a.single_stage) return launch_o<O_DT, FUSED, NORM>(a, st);
   std::lock_guard<std::mutex> lock(g_side_mu);
+  const StageCuts cuts = g_cuts;
+  if (cuts.n == 0) return launch_o<O_DT, FUSED, NORM>(a, st);
   SideQueue* q = nullptr;
   hipError_t e = side_queue(q);
   if (e != hipSuccess) return e;
   const int64_t grid = (int64_t)a.num_seqs * a.hv * mp::NB;
   const bool split = 4 * grid <= 3 * (int64_t)q->cus && a.total >= (int64_t)a.num_seqs * 8 * mp::C;
   if (!split) return launch_o<O_DT, FUSED, NORM>(a, st);
+  const int nstage = cuts.n + 1;
   const int64_t maxch = max_chunks(a.total, a.num_seqs);
   const WsLayout wl(a.num_seqs, a.hv, a.hk, maxch);
   float* mid = reinterpret_cast<float*>(static_cast<unsigned char*>(a.workspace) + wl.mid);
-  PrefillArgs sp[NSTAGE];
-  for (int k = 0; k < NSTAGE; ++k) {
+  PrefillArgs sp[MAX_STAGES];
+  for (int k = 0; k < nstage; ++k) {
     sp[k] = a;
-    sp[k].part_lo = k == 0 ? 0 : SPLIT_CUT[k - 1];
-    sp[k].part_hi = k == NSTAGE - 1 ? SPLIT_DEN : SPLIT_CUT[k];
+    sp[k].part_lo = k == 0 ? 0 : cuts.cut[k - 1];
+    sp[k].part_hi = k == nstage - 1 ? SPLIT_DEN : cuts.cut[k];
     sp[k].part_den = SPLIT_DEN;
     sp[k].stage = k;
     if (k > 0) sp[k].s0 = mid;           // a workgroup reads its state slice before it writes it,
-    if (k < NSTAGE - 1) sp[k].s1 = mid;  // so a middle stage updates the carried state in place
+    if (k < nstage - 1) sp[k].s1 = mid;  // so a middle stage updates the carried state in place
   }
   // Under stream capture the events are recorded as their own nodes (a kernel-completion event
   // is not a capturable dependency); the side stream then joins the capture through them.
@@ -1632,10 +1649,10 @@ static hipError_t launch_staged(const PrefillArgs& a, hipStream_t st) {
   if ((e = launch_offsets(a, st)) != hipSuccess) return e;
   if ((e = launch_prep<FUSED>(sp[0], maxch, st, capturing ? nullptr : q->prepped[0])) != hipSuccess) return e;
   if (capturing && (e = hipEventRecord(q->prepped[0], st)) != hipSuccess) return e;
-  for (int k = 0; k < NSTAGE; ++k) {
+  for (int k = 0; k < nstage; ++k) {
     if (k > 0 && (e = hipStreamWaitEvent(st, q->prepped[k], 0)) != hipSuccess) return e;
     if ((e = launch_scan<O_DT, FUSED, NORM>(sp[k], maxch, st)) != hipSuccess) return e;
-    if (k + 1 == NSTAGE) break;
+    if (k + 1 == nstage) break;
     if (k == 0 && (e = hipStreamWaitEvent(q->s, q->prepped[0], 0)) != hipSuccess) return e;
     hipEvent_t done = q->prepped[k + 1];
     if ((e = launch_prep<FUSED>(sp[k + 1], maxch, q->s, capturing ? nullptr : done)) != hipSuccess) return e;

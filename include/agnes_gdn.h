@@ -473,6 +473,22 @@ int agnes_gdn_workspace_status(const void* workspace, uint32_t* flags, void* str
 int agnes_gdn_set_wait_limit(uint32_t polls);
 
 /*
+ * agnes_gdn_set_prefill_stages — process-wide stage cuts of the bf16 prefill calls launched
+ * after it (agnes_gdn_prefill_chunked, agnes_gdn_prefill_fused and the whole-layer calls).  When
+ * the scan of a call leaves a quarter of the compute units free and its sequences average at
+ * least 8 chunks, the call runs in n_cuts + 1 stages: stage k covers chunks
+ * [cuts[k-1], cuts[k]) in 1/40ths of each sequence's chunk count (cuts[-1] = 0, cuts[n_cuts] =
+ * 40), the preparation of stage k + 1 overlapping the scan of stage k on a side stream and the
+ * state carried between stages in the workspace.  The stages change the schedule only: the
+ * results are the same bit for bit.  `cuts` (host, n_cuts values) must increase strictly inside
+ * (0, 40), 0 <= n_cuts <= 7; n_cuts = 0 runs every call in one stage.  The default is one cut at
+ * 24 (two stages, the first 3/5 of the chunks).  Not meant to change while calls are being
+ * launched from other threads.  Returns AGNES_OK, or AGNES_ERR_INVALID_ARG (nothing changed)
+ * for any other list.
+ */
+int agnes_gdn_set_prefill_stages(const int32_t* cuts, int n_cuts);
+
+/*
  * Measurement kernels: the two ceilings the benchmark reports its roofline fractions against,
  * measured on the machine itself beside the vendor's peaks.
  *
@@ -494,8 +510,8 @@ int agnes_gdn_ceiling_mfma(float* sink, int blocks, int iters, void* stream);
 
 /*
  * agnes_gdn_release — destroys the HIP objects the library keeps between calls: the side stream
- * and the two events per device that the calls in two stages create on first use (after waiting
- * for the work on that stream).  A later call in two stages creates them again.  Call it when no
+ * and the events per device that the calls in stages create on first use (after waiting for the
+ * work on that stream).  A later call in stages creates them again.  Call it when no
  * call of the library is in flight, e.g. before the process exits, so that no library handle is
  * left for the runtime's own teardown; it makes no HIP call when nothing was created.  Returns
  * AGNES_OK, or AGNES_ERR_HIP if a destroy fails.

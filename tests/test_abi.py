@@ -335,6 +335,24 @@ def test_status_and_measurement_calls_check_their_arguments(lib):
     assert lib.agnes_gdn_last_hip_error() == 0
 
 
+
+def test_stage_cuts_are_checked_on_the_host(lib):
+    """The stage cuts must increase strictly inside (0, 40), at most 7 of them; any other list is
+    refused and leaves the setting as it was (host-only, no device call)."""
+    import ctypes
+
+    def cuts(*v):
+        return (ctypes.c_int32 * max(len(v), 1))(*v), len(v)
+
+    for bad in [(0,), (40,), (24, 24), (30, 20), (-1,), tuple(range(1, 9))]:
+        assert lib.agnes_gdn_set_prefill_stages(*cuts(*bad)) == INV, bad
+    assert lib.agnes_gdn_set_prefill_stages(None, 1) == INV
+    assert lib.agnes_gdn_set_prefill_stages(None, -1) == INV
+    assert lib.agnes_gdn_set_prefill_stages(None, 0) == 0
+    assert lib.agnes_gdn_set_prefill_stages(*cuts(1, 2, 3, 4, 5, 6, 39)) == 0
+    assert lib.agnes_gdn_set_prefill_stages(*cuts(24)) == 0
+    assert lib.agnes_gdn_last_hip_error() == 0
+
 def test_noalloc_refuses_a_workspace_beyond_its_own_on_the_host(lib):
     """The fixed-workspace call rejects a problem whose workspace exceeds its 64 MiB before any
     device call (the size query is host arithmetic)."""

@@ -140,6 +140,28 @@ def test_layer_prefill_in_two_stages():
     assert float(rel.max()) <= 1e-5 and ey <= TOL_Y and rel_l2(f1, rfin) <= 2e-3
 
 
+
+@pytest.mark.parametrize("cuts", [(), (18, 31), (10, 20, 30), (39,), (5, 10, 15, 20, 25, 30, 35)],
+                         ids=["one", "three", "four", "late", "eight"])
+def test_layer_prefill_stage_cuts_change_nothing(cuts):
+    """The stage cuts (agnes_gdn_set_prefill_stages) change the schedule only: one stage, three,
+    four, a late single cut and eight stages (middle stages that update the carried state in
+    place, and for the short sequences stages with no chunk at all) give y, o, the final state and
+    the conv history of the default two stages bit for bit."""
+    rng = np.random.default_rng(655)
+    d = _case(rng, [700, 1, 0, 2000, 64, 1300], 2, 6)
+    ref = _layer(d, want_o=True)
+    try:
+        gdn.set_prefill_stages(cuts)
+        got = _layer(d, want_o=True)
+    finally:
+        gdn.set_prefill_stages()
+    for a, b in zip(got, ref):
+        np.testing.assert_array_equal(a, b)
+    again = _layer(d, want_o=True)
+    for a, b in zip(again, ref):
+        np.testing.assert_array_equal(a, b)
+
 def test_layer_prefill_bf16_outputs_are_rne_of_fp32_outputs():
     rng = np.random.default_rng(620)
     d = _case(rng, [150, 37], 1, 3)
