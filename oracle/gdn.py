@@ -49,11 +49,12 @@ def recurrence(q, k, v, g, beta, cu_seqlens=None, initial_state=None, scale=1.0,
     kh = key_head_of(Hk, Hv)[hs]
     o = np.zeros((T, Hv, dv))
     final = np.zeros((N, Hv, dv, dk))
+    S0 = None if initial_state is None else as_f64(initial_state)
     for n in range(N):
-        if initial_state is None:
+        if S0 is None:
             S = np.zeros((len(hs), dv, dk))
         else:
-            S = as_f64(initial_state)[n][hs].copy()
+            S = S0[n][hs].copy()
         for t in range(int(cu[n]), int(cu[n + 1])):
             a = np.exp(g[t, hs])[:, None, None]        # alpha_t per head
             b = beta[t, hs][:, None, None]             # beta_t per head
