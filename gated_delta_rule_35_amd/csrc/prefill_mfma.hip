@@ -103,6 +103,7 @@ constexpr int QK_BYTES = sizeof(QKImage);
 // [q/k images: Hk x maxch] ...
 struct WsLayout {
   static constexpr size_t OFF = 256;  // chunk offsets; the status word sits at byte 0
+  static constexpr size_t SINK = 64;  // 64 bytes of the header that stores may hit and nothing reads
   size_t rec, qk, bytes;
   size_t mid;  // calls in stages: the states carried between the stages
   // whole-layer call only: per (sequence, value head) RING chunk slots, each with one 64-bit
@@ -949,8 +950,8 @@ __device__ __forceinline__ void o_step(const ExBuf& exU, float (*Os)[mp::DVB + 4
 // invalidation of a whole L2) is needed.  Chunk c (counted from the sequence start, so that
 // the stages of a call never take each other's words) uses slot c mod RING.  In step c a tile wave
 // (1) waits for the words of chunk c - 3 (loaded at the end of step c - 1, reloaded while a tag
-// is older) and writes y of chunk c - 3; (2) takes chunk c - 1 from Os and publishes its sums;
-// (3) loads the words and gates of chunk c - 2.  Chunk k is published in step k + 1 and read in
+// is older) and computes y of chunk c - 3; (2) takes chunk c - 1 from Os and publishes its sums;
+// (3) loads the words and gates of chunk c - 2; (4) stores y of chunk c - 3.  Chunk k is published in step k + 1 and read in
 // steps k + 2 .. k + 3; slot k is next written (chunk k + RING) in step k + RING + 1, after the
 // writer's wait for chunk k + RING - 2, which every reader publishes in step k + RING - 1 after
 // its own read of chunk k (step k + 3): RING >= 4 suffices.  Every wait ends (the workgroups
@@ -969,6 +970,7 @@ struct NormCtx {
   int r0;                    // first row of this tile wave
   int cbase;                 // the sequence's chunk index of local chunk 0: tags and slots use it
   float w[8];                // norm weights of the lane's 8 columns
+  void* sink;                // where the row stores of rows past the chunk end go (see tile_store_y)
 };
 
 // The lane's pieces of rows r0 + 16 g + lane / 4 (g < NG) of the staged tile, columns
@@ -1064,11 +1066,22 @@ __device__ __forceinline__ void norm_issue(const NormCtx& nc_, const PrefillArgs
   }
 }
 
-// Waits until every other block has published chunk c, then writes y of chunk c from the
+// An empty use of the exchange loads' registers: the compiler waits for those loads here.  At the
+// start of every step this tells it that no load is pending when the step issues the next ones;
+// without it, it waits for everything in flight before issuing them (vector memory counts retire
+// in order), the row stores of the same step included.
+template <int NG>
+__device__ __forceinline__ void consume(const NormIn<NG>& g) {
+  static_assert(mp::NB - 1 == 3 && NG == 2, "operand list below");
+  asm volatile("" ::"v"(g.w[0]), "v"(g.w[1]), "v"(g.w[2]), "v"(g.z[0].x), "v"(g.z[0].y), "v"(g.z[0].z),
+               "v"(g.z[0].w), "v"(g.z[1].x), "v"(g.z[1].y), "v"(g.z[1].z), "v"(g.z[1].w));
+}
+
+// Waits until every other block has published chunk c, then computes y of chunk c from the
 // lane's row pieces x, their own sums ss and the gates in g.
-template <int O_DT, int NG>
-__device__ __forceinline__ void norm_finish(const NormCtx& nc_, const PrefillArgs& a, const Geo& G, int c, int lane,
-                                            NormIn<NG>& g, const float (&x)[NG][8], const float (&ss)[NG]) {
+template <int NG>
+__device__ __forceinline__ void norm_compute(const NormCtx& nc_, const PrefillArgs& a, int c, int lane, NormIn<NG>& g,
+                                             const float (&x)[NG][8], const float (&ss)[NG], float (&y)[NG][8]) {
   const int bound = wait_bound(a.wait_limit, 1 << 24);
   bool ready = false;
   for (int it = 0; it < bound; ++it) {
@@ -1081,12 +1094,12 @@ __device__ __forceinline__ void norm_finish(const NormCtx& nc_, const PrefillArg
     }
     __builtin_amdgcn_s_sleep(1);
     norm_load_words(nc_, c, lane, g);
+    consume(g);  // a reload is waited for here, not where the next step's loads are issued
   }
   if (!ready && lane == 0) ws_report(a.workspace, wsbits::WAIT_EXCHANGE);
   float oth = 0.f;
 #pragma unroll
   for (int i = 0; i < mp::NB - 1; ++i) oth += __uint_as_float((unsigned)(g.w[i] >> 32));
-  float y[NG][8];
 #pragma unroll
   for (int q = 0; q < NG; ++q) {
     const float tot = ss[q] + __shfl(oth, mp::TRPP * q + lane / mp::TLPR);
@@ -1098,7 +1111,23 @@ __device__ __forceinline__ void norm_finish(const NormCtx& nc_, const PrefillArg
       y[q][e] = x[q][e] * rs * nc_.w[e] * silu(zv);
     }
   }
-  tile_store<O_DT, NG>(a.y, a, G, c, nc_.r0, lane, y);
+}
+
+// y rows of chunk c out (c < 0: none).  Every lane stores, the rows past the chunk end into the
+// sink (64 bytes of the workspace header that nothing reads), so that the number of stores after
+// a step's exchange loads is the same on every path and the wait for those loads at the start of
+// the next step (see consume) need not also wait for these stores.
+template <int O_DT, int NG>
+__device__ __forceinline__ void tile_store_y(const NormCtx& nc_, const PrefillArgs& a, const Geo& G, int c, int lane,
+                                             const float (&y)[NG][8]) {
+  const int L = c >= 0 ? G.len(c) : 0, col = 8 * (lane % mp::TLPR);
+  constexpr int ES = O_DT == DT_BF16 ? 2 : 4;
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    const int r = nc_.r0 + mp::TRPP * q + lane / mp::TLPR;
+    const int64_t idx = ((G.start + (int64_t)c * mp::C + r) * a.hv + G.h) * (int64_t)mp::D + G.dv0 + col;
+    store8_nt<O_DT>(r < L ? static_cast<void*>(static_cast<unsigned char*>(a.y) + idx * ES) : nc_.sink, 0, y[q]);
+  }
 }
 
 // A tile wave's steps (as many LDS barriers as every other wave).  qt: this tile wave.
@@ -1117,11 +1146,14 @@ __device__ __forceinline__ void tile_wave(ScanSmem& sm, const PrefillArgs& a, co
   nctx.blk = G.dv0 / DVB;
   nctx.r0 = r0;
   nctx.cbase = G.cbase;
+  nctx.sink = static_cast<unsigned char*>(a.workspace) + WsLayout::SINK;
   load8<DT_BF16>(a.norm_w, G.dv0 + 8 * (lane % TLPR), nctx.w);
   float xa[NG][8], xb[NG][8], sa[NG], sb[NG];  // chunks c - 3 and c - 2 at the start of step c
-  NormIn<NG> gin;
+  float y[NG][8] = {};                          // y of chunk c - 3, stored at the end of step c
+  NormIn<NG> gin = {};
   for (int c = 0; c < nc + 1; ++c) {
-    if (c >= 3) norm_finish<O_DT, NG>(nctx, a, G, c - 3, lane, gin, xa, sa);
+    consume(gin);
+    if (c >= 3) norm_compute<NG>(nctx, a, c - 3, lane, gin, xa, sa, y);
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
       sa[q] = sb[q];
@@ -1137,13 +1169,18 @@ __device__ __forceinline__ void tile_wave(ScanSmem& sm, const PrefillArgs& a, co
       if (a.o) tile_store<O_DT, NG>(a.o, a, G, c - 1, r0, lane, xb);
     }
     if (c >= 2) norm_issue<NG>(nctx, a, G, c - 2, lane, gin);
+    tile_store_y<O_DT, NG>(nctx, a, G, c - 3, lane, y);  // steps 0 .. 2: all into the sink
     lds_barrier();
   }
   // chunks nc - 2 (words and gates in flight) and nc - 1
-  if (nc >= 2) norm_finish<O_DT, NG>(nctx, a, G, nc - 2, lane, gin, xa, sa);
+  if (nc >= 2) {
+    norm_compute<NG>(nctx, a, nc - 2, lane, gin, xa, sa, y);
+    tile_store_y<O_DT, NG>(nctx, a, G, nc - 2, lane, y);
+  }
   if (nc >= 1) {
     norm_issue<NG>(nctx, a, G, nc - 1, lane, gin);
-    norm_finish<O_DT, NG>(nctx, a, G, nc - 1, lane, gin, xb, sb);
+    norm_compute<NG>(nctx, a, nc - 1, lane, gin, xb, sb, y);
+    tile_store_y<O_DT, NG>(nctx, a, G, nc - 1, lane, y);
   }
 }
 
