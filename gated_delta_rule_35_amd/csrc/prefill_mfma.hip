@@ -1246,6 +1246,37 @@ __device__ __forceinline__ void issue_chunk(ScanSmem& sm, const PrefillArgs& a, 
   }
 }
 
+// LDS reads and the write of the V-slice conv, written out so that the compiler does not wait
+// for the copy wave's direct copies in flight before them: it cannot tell the parity-indexed
+// rows apart from the copies' destinations and would wait for every copy to land (vector memory
+// counts) before the conv could start.  The conv reads Vr[cc & 1] (landed a step earlier) and
+// writes B[cc & 1].Vs, and the copies in flight write B[cc & 1].QK / .R and Vr[(cc + 1) & 1]:
+// disjoint bytes.  Each block waits for its own LDS operations.
+__device__ __forceinline__ void lds_read4_b128(const void* p0, const void* p1, const void* p2, const void* p3,
+                                               uint4 (&x)[4]) {
+  const unsigned a0 = (unsigned)(uintptr_t)(const lds_void*)p0, a1 = (unsigned)(uintptr_t)(const lds_void*)p1,
+                 a2 = (unsigned)(uintptr_t)(const lds_void*)p2, a3 = (unsigned)(uintptr_t)(const lds_void*)p3;
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 r0, r1, r2, r3;
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+  x[0] = make_uint4(r0[0], r0[1], r0[2], r0[3]);
+  x[1] = make_uint4(r1[0], r1[1], r1[2], r1[3]);
+  x[2] = make_uint4(r2[0], r2[1], r2[2], r2[3]);
+  x[3] = make_uint4(r3[0], r3[1], r3[2], r3[3]);
+}
+__device__ __forceinline__ void lds_write_b128(void* p, h8 v) {
+  const unsigned a = (unsigned)(uintptr_t)(lds_void*)p;
+  asm volatile("ds_write_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" ::"v"(a), "v"(v) : "memory");
+}
+
 // Copy waves, fused prologue: the V slice of chunk cc = SiLU(causal conv) of its raw x rows in
 // Vr[cc & 1] (row r of the chunk reads raw rows r .. r + 3), fp16 into B[cc & 1].Vs.  For the
 // sequence's first chunk the halo rows are the conv history (zeros without one).  Item
@@ -1258,19 +1289,21 @@ __device__ __forceinline__ void conv_vslice(ScanSmem& sm, const PrefillArgs& a, 
   if (item >= C * DVB / 8) return;
   const int r = item >> 2, cg = item & 3;
   uint4 xr[4];
+  lds_read4_b128(&sm.Vr[cc & 1][r][8 * cg], &sm.Vr[cc & 1][r + 1][8 * cg], &sm.Vr[cc & 1][r + 2][8 * cg],
+                 &sm.Vr[cc & 1][r + 3][8 * cg], xr);
+  if (cc == 0 && G.start == G.hstart) {  // staged rows 0 .. 2 lie before the sequence start
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
-    const int i = r + jt;
-    if (cc == 0 && i < 3 && G.start == G.hstart) {
-      const uint16_t* hist = static_cast<const uint16_t*>(a.conv_hist);
-      const int64_t ch = (int64_t)(2 * a.hk + G.h) * D + G.dv0 + 8 * cg;
-      const int64_t Ctot = (int64_t)(2 * a.hk + a.hv) * D;
-      const uint16_t* hp = hist + ((int64_t)n * Ctot + ch) * 3 + i;
-      xr[jt] = hist ? make_uint4(hp[0] | (uint32_t)hp[3] << 16, hp[6] | (uint32_t)hp[9] << 16,
-                                 hp[12] | (uint32_t)hp[15] << 16, hp[18] | (uint32_t)hp[21] << 16)
-                    : make_uint4(0, 0, 0, 0);
-    } else {
-      xr[jt] = *reinterpret_cast<const uint4*>(&sm.Vr[cc & 1][i][8 * cg]);
+    for (int jt = 0; jt < 3; ++jt) {
+      const int i = r + jt;
+      if (i < 3) {
+        const uint16_t* hist = static_cast<const uint16_t*>(a.conv_hist);
+        const int64_t ch = (int64_t)(2 * a.hk + G.h) * D + G.dv0 + 8 * cg;
+        const int64_t Ctot = (int64_t)(2 * a.hk + a.hv) * D;
+        const uint16_t* hp = hist + ((int64_t)n * Ctot + ch) * 3 + i;
+        xr[jt] = hist ? make_uint4(hp[0] | (uint32_t)hp[3] << 16, hp[6] | (uint32_t)hp[9] << 16,
+                                   hp[12] | (uint32_t)hp[15] << 16, hp[18] | (uint32_t)hp[21] << 16)
+                      : make_uint4(0, 0, 0, 0);
+      }
     }
   }
   float acc[8];
@@ -1278,7 +1311,7 @@ __device__ __forceinline__ void conv_vslice(ScanSmem& sm, const PrefillArgs& a, 
   h8 o;
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = (_Float16)silu(acc[e]);
-  *reinterpret_cast<h8*>(&sm.B[cc & 1].Vs[r][8 * cg]) = o;
+  lds_write_b128(&sm.B[cc & 1].Vs[r][8 * cg], o);
 }
 
 // Waves: NPAIR chain waves, NPAIR output waves (pair p for value tiles TPW p .. TPW p + TPW - 1),
