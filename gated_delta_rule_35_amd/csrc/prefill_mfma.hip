@@ -950,8 +950,9 @@ __device__ __forceinline__ void o_step(const ExBuf& exU, float (*Os)[mp::DVB + 4
 // invalidation of a whole L2) is needed.  Chunk c (counted from the sequence start, so that
 // the stages of a call never take each other's words) uses slot c mod RING.  In step c a tile wave
 // (1) waits for the words of chunk c - 3 (loaded at the end of step c - 1, reloaded while a tag
-// is older) and computes y of chunk c - 3; (2) takes chunk c - 1 from Os and publishes its sums;
-// (3) loads the words and gates of chunk c - 2; (4) stores y of chunk c - 3.  Chunk k is published in step k + 1 and read in
+// is older) and computes y of chunk c - 3; (2) loads the gates of chunk c - 2 and stores y of
+// chunk c - 3; (3) takes chunk c - 1 from Os and publishes its sums; (4) loads the words of chunk
+// c - 2.  Chunk k is published in step k + 1 and read in
 // steps k + 2 .. k + 3; slot k is next written (chunk k + RING) in step k + RING + 1, after the
 // writer's wait for chunk k + RING - 2, which every reader publishes in step k + RING - 1 after
 // its own read of chunk k (step k + 3): RING >= 4 suffices.  Every wait ends (the workgroups
@@ -1051,9 +1052,8 @@ __device__ __forceinline__ void norm_load_words(const NormCtx& nc_, int c, int l
 }
 
 template <int NG>
-__device__ __forceinline__ void norm_issue(const NormCtx& nc_, const PrefillArgs& a, const Geo& G, int c, int lane,
-                                           NormIn<NG>& g) {
-  norm_load_words(nc_, c, lane, g);
+__device__ __forceinline__ void norm_load_z(const NormCtx& nc_, const PrefillArgs& a, const Geo& G, int c, int lane,
+                                            NormIn<NG>& g) {
   const int L = G.len(c), col = 8 * (lane % mp::TLPR);
 #pragma unroll
   for (int q = 0; q < NG; ++q) {
@@ -1113,10 +1113,10 @@ __device__ __forceinline__ void norm_compute(const NormCtx& nc_, const PrefillAr
   }
 }
 
-// y rows of chunk c out (c < 0: none).  Every lane stores, the rows past the chunk end into the
-// sink (64 bytes of the workspace header that nothing reads), so that the number of stores after
-// a step's exchange loads is the same on every path and the wait for those loads at the start of
-// the next step (see consume) need not also wait for these stores.
+// y rows of chunk c out (c < 0: none).  Every lane stores, the rows past the chunk end (and all
+// rows for c < 0) into the sink, 64 bytes of the workspace header that nothing reads: the store
+// sequence has no branch, so the compiler's count of the memory operations in flight is exact on
+// every path through the step.
 template <int O_DT, int NG>
 __device__ __forceinline__ void tile_store_y(const NormCtx& nc_, const PrefillArgs& a, const Geo& G, int c, int lane,
                                              const float (&y)[NG][8]) {
@@ -1154,6 +1154,10 @@ __device__ __forceinline__ void tile_wave(ScanSmem& sm, const PrefillArgs& a, co
   for (int c = 0; c < nc + 1; ++c) {
     consume(gin);
     if (c >= 3) norm_compute<NG>(nctx, a, c - 3, lane, gin, xa, sa, y);
+    // the gates of chunk c - 2 (from HBM) a whole step before their use, and y of chunk c - 3
+    // out, before the wait for the staged tile: neither lies on the way to the barrier
+    if (c >= 2) norm_load_z<NG>(nctx, a, G, c - 2, lane, gin);
+    tile_store_y<O_DT, NG>(nctx, a, G, c - 3, lane, y);  // steps 0 .. 2: all into the sink
 #pragma unroll
     for (int q = 0; q < NG; ++q) {
       sa[q] = sb[q];
@@ -1168,8 +1172,7 @@ __device__ __forceinline__ void tile_wave(ScanSmem& sm, const PrefillArgs& a, co
       norm_publish<NG>(nctx, c - 1, lane, sb);
       if (a.o) tile_store<O_DT, NG>(a.o, a, G, c - 1, r0, lane, xb);
     }
-    if (c >= 2) norm_issue<NG>(nctx, a, G, c - 2, lane, gin);
-    tile_store_y<O_DT, NG>(nctx, a, G, c - 3, lane, y);  // steps 0 .. 2: all into the sink
+    if (c >= 2) norm_load_words<NG>(nctx, c - 2, lane, gin);
     lds_barrier();
   }
   // chunks nc - 2 (words and gates in flight) and nc - 1
@@ -1178,7 +1181,8 @@ __device__ __forceinline__ void tile_wave(ScanSmem& sm, const PrefillArgs& a, co
     tile_store_y<O_DT, NG>(nctx, a, G, nc - 2, lane, y);
   }
   if (nc >= 1) {
-    norm_issue<NG>(nctx, a, G, nc - 1, lane, gin);
+    norm_load_z<NG>(nctx, a, G, nc - 1, lane, gin);
+    norm_load_words<NG>(nctx, nc - 1, lane, gin);
     norm_compute<NG>(nctx, a, nc - 1, lane, gin, xb, sb, y);
     tile_store_y<O_DT, NG>(nctx, a, G, nc - 1, lane, y);
   }
