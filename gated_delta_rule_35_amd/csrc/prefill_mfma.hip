@@ -197,6 +197,12 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Barrier of the copy waves of the fused scan, which order their own LDS traffic with explicit
+// waits (the direct copies that must land before the barrier, and the conv's LDS accesses, which
+// wait for themselves): a workgroup release fence here would make the compiler wait for every
+// direct copy in flight, the raw rows of the chunk after next included.
+__device__ __forceinline__ void copy_barrier() { __builtin_amdgcn_s_barrier(); }
+
 // ---------------------------------------------------------------- 1. chunk offsets
 __global__ __launch_bounds__(256) void chunk_offsets_kernel(const int32_t* cu, int num_seqs, int64_t total,
                                                             int32_t* off, unsigned* status) {
@@ -1205,6 +1211,39 @@ __device__ __forceinline__ int first_copy(int base, int q) {
   return base + (r < 0 ? r + NCOPY : r);
 }
 
+// Number of direct copies copy wave q issues for one chunk (issue_chunk with c >= 0 and cv >= 0).
+template <bool FUSED, int NCOPY>
+__device__ __forceinline__ int copies_of_wave(int q) {
+  using namespace mp;
+  constexpr int NQK = QK_BYTES / 1024, NREC = REC_BYTES / 1024, NV = C * (LDV / 8) / 64;
+  const int nqk = (NQK - q + NCOPY - 1) / NCOPY;
+  const int f = first_copy<NCOPY>(NQK, q);
+  const int nrec = f < NQK + NREC ? (NQK + NREC - f + NCOPY - 1) / NCOPY : 0;
+  if constexpr (FUSED) return nqk + nrec + (q < 4 ? 2 : 0);
+  const int fv = first_copy<NCOPY>(NQK + NREC, q);
+  return nqk + nrec + (fv < NQK + NREC + NV ? (NQK + NREC + NV - fv + NCOPY - 1) / NCOPY : 0);
+}
+
+// s_waitcnt on the vector memory count only (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// The same for a wave-uniform count n in [0, 24) (larger counts wait for everything).
+__device__ __forceinline__ void wait_vm_n(int n) {
+  switch (n) {
+#define AGNES_WAIT_CASE(k) case k: wait_vm<k>(); break;
+    AGNES_WAIT_CASE(1) AGNES_WAIT_CASE(2) AGNES_WAIT_CASE(3) AGNES_WAIT_CASE(4) AGNES_WAIT_CASE(5)
+    AGNES_WAIT_CASE(6) AGNES_WAIT_CASE(7) AGNES_WAIT_CASE(8) AGNES_WAIT_CASE(9) AGNES_WAIT_CASE(10)
+    AGNES_WAIT_CASE(11) AGNES_WAIT_CASE(12) AGNES_WAIT_CASE(13) AGNES_WAIT_CASE(14) AGNES_WAIT_CASE(15)
+    AGNES_WAIT_CASE(16) AGNES_WAIT_CASE(17) AGNES_WAIT_CASE(18) AGNES_WAIT_CASE(19) AGNES_WAIT_CASE(20)
+    AGNES_WAIT_CASE(21) AGNES_WAIT_CASE(22) AGNES_WAIT_CASE(23)
+#undef AGNES_WAIT_CASE
+    default: wait_vm<0>(); break;
+  }
+}
+
 template <bool FUSED, int NCOPY>
 __device__ __forceinline__ void issue_chunk(ScanSmem& sm, const PrefillArgs& a, const Geo& G,
                                             const unsigned char* ws, int c, int cv, int q) {
@@ -1236,9 +1275,13 @@ __device__ __forceinline__ void issue_chunk(ScanSmem& sm, const PrefillArgs& a, 
     }
   }
   if constexpr (FUSED) {
-    if (cv >= 0) {
+    // raw rows: conv wave q (< 4) copies pieces q and q + 1 (raw rows 16 q .. 16 q + 31), all
+    // that its own conv items (chunk rows 16 q .. 16 q + 15) read, so that the conv waits only
+    // for its own copies
+    if (cv >= 0 && q < 4) {
+      static_assert(NV == 5, "four conv waves, two overlapping 16-row pieces each");
       const int64_t c0 = G.start + (int64_t)cv * C;
-      for (int u = first_copy<NCOPY>(NQK + NREC, q); u < NQK + NREC + NV; u += NCOPY) {
+      for (int u = NQK + NREC + q; u < NQK + NREC + q + 2; ++u) {
         const int jv = 64 * (u - NQK - NREC) + lane, i = jv >> 2, pc = jv & 3;
         const int64_t pos = c0 - 3 + i;
         const bool in = pos >= G.hstart && i < 3 + G.len(cv);
@@ -1517,13 +1560,24 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
       lds_barrier();  // raw rows of chunk 0 visible to every copy wave
       if (nc > 0 && qv >= 0 && qv < 4) conv_vslice(sm, a, G, n, 0, qv, wt, bs);
       lds_barrier();
+      // A conv wave's raw rows of chunk c + 2 (its last two copies of step c) may still be in
+      // flight at the end of step c: only its own conv of step c + 1 reads them, after a wait
+      // for everything but that step's own copies.  Every other copy lands before the barrier.
+      const bool conv_wave = qv >= 0 && qv < 4;
       for (int c = 0; c < nc + 1; ++c) {
         if (c + 1 < nc) {
-          issue_chunk<true, NCOPY>(sm, a, G, ws, c + 1, c + 2 < nc ? c + 2 : -1, qc);
-          if (qv >= 0 && qv < 4) conv_vslice(sm, a, G, n, c + 1, qv, wt, bs);
-          __builtin_amdgcn_s_waitcnt(0);
+          const bool raw = c + 2 < nc;
+          issue_chunk<true, NCOPY>(sm, a, G, ws, c + 1, raw ? c + 2 : -1, qc);
+          if (conv_wave) {
+            wait_vm_n(copies_of_wave<true, NCOPY>(qc) - (raw ? 0 : 2));  // raw rows of chunk c + 1
+            conv_vslice(sm, a, G, n, c + 1, qv, wt, bs);
+            if (raw) wait_vm<2>();
+            else wait_vm<0>();
+          } else {
+            __builtin_amdgcn_s_waitcnt(0);
+          }
         }
-        lds_barrier();
+        copy_barrier();
       }
     } else {
       if (nc > 0) {
