@@ -179,6 +179,22 @@ __device__ __forceinline__ float sum16(float v) {
   v += __shfl_xor(v, 8, 16);
   return v;
 }
+// The same sum through DPP lane moves within each 16-lane row (one VALU operation per step
+// instead of an LDS permute and its index arithmetic): swap neighbours, swap pairs, then add the
+// mirrored half-row and the mirrored row.  Each step adds lane values from the other half of the
+// current group, so after four steps every lane holds its row's sum (in another summation order
+// than sum16).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float sum16_dpp(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1, 0, 3, 2]: lane ^ 1
+  v += dpp_f<0x4E>(v);   // quad_perm [2, 3, 0, 1]: lane ^ 2
+  v += dpp_f<0x141>(v);  // row_half_mirror: lane 7 - i of each 8
+  v += dpp_f<0x140>(v);  // row_mirror: lane 15 - i of each 16
+  return v;
+}
 
 // x * sigmoid(x) with the hardware exp2 and reciprocal (each within about 1 ulp).
 __device__ __forceinline__ float silu(float u) { return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u)); }

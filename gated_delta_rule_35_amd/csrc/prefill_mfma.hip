@@ -436,21 +436,24 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
     }
     const uint16_t (*X)[D] = hs ? sm.u.qk.Xk : sm.u.qk.Xq;
     const uint16_t* hist = static_cast<const uint16_t*>(a.conv_hist);
+    const bool head = c0 - 3 < start;  // the sequence's first chunk: the halo is the history
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       const int r = rr + 24 * k;
       if (r >= C) break;
       uint4 xr[4];
 #pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        const int i = r + jt;  // staged row i = x row c0 - 3 + i
-        if (c0 - 3 + i < start) {  // before the sequence start: history entry i (oldest first)
-          const uint16_t* hp = hist + ((int64_t)n * Ctot + ch) * 3 + i;
-          xr[jt] = hist ? make_uint4(hp[0] | (uint32_t)hp[3] << 16, hp[6] | (uint32_t)hp[9] << 16,
-                                          hp[12] | (uint32_t)hp[15] << 16, hp[18] | (uint32_t)hp[21] << 16)
-                             : make_uint4(0, 0, 0, 0);
-        } else {
-          xr[jt] = *reinterpret_cast<const uint4*>(&X[i][8 * col]);
+      for (int jt = 0; jt < 4; ++jt) xr[jt] = *reinterpret_cast<const uint4*>(&X[r + jt][8 * col]);
+      if (head) {
+#pragma unroll
+        for (int jt = 0; jt < 3; ++jt) {
+          const int i = r + jt;  // staged row i = x row c0 - 3 + i
+          if (c0 - 3 + i < start) {  // before the sequence start: history entry i (oldest first)
+            const uint16_t* hp = hist + ((int64_t)n * Ctot + ch) * 3 + i;
+            xr[jt] = hist ? make_uint4(hp[0] | (uint32_t)hp[3] << 16, hp[6] | (uint32_t)hp[9] << 16,
+                                       hp[12] | (uint32_t)hp[15] << 16, hp[18] | (uint32_t)hp[21] << 16)
+                          : make_uint4(0, 0, 0, 0);
+          }
         }
       }
       float y[8], ss = 0.f;
@@ -460,7 +463,7 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
         y[e] = silu(y[e]);
         ss = fmaf(y[e], y[e], ss);
       }
-      ss = sum16(ss);
+      ss = sum16_dpp(ss);
       const float rs = rsqrt_fast(ss + a.l2_eps);
       h8 hv;
 #pragma unroll
