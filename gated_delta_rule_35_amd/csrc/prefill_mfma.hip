@@ -1672,7 +1672,7 @@ static hipError_t launch_o(const PrefillArgs& a, hipStream_t st) {
 // a short time before it.  So the call runs as prep(first part of every sequence) -> scan(first
 // part) on the caller's stream, with prep(next part) on a side stream beside that scan (on the
 // compute units the scan leaves free), then scan(next part) carrying the state over.  Prep beside
-// a scan runs ~3x slower than alone, so the first part is the larger: 3/5 of the chunks.  More
+// a scan runs ~3x slower than alone, so the first part is the larger: 13/20 of the chunks.  More
 // stages shorten the exposed first prep but cost more at each hand-over than they save (at
 // T = 8192: two stages 356 us, three 373-380 us, four 398 us).  Used when the scan leaves a
 // quarter of the chip free and sequences are long enough.  The cuts are a process-wide setting
@@ -1681,7 +1681,7 @@ constexpr int SPLIT_DEN = 40;    // stage boundaries in 1/40 of each sequence's 
 constexpr int MAX_STAGES = 8;    // the workspace holds role counters for 8 stages
 struct StageCuts {
   int n = 1;                     // number of cuts: the call runs in n + 1 stages
-  int cut[MAX_STAGES - 1] = {24};  // stage k covers [cut[k-1], cut[k]) of SPLIT_DEN
+  int cut[MAX_STAGES - 1] = {26};  // stage k covers [cut[k-1], cut[k]) of SPLIT_DEN
 };
 
 namespace {

@@ -482,7 +482,7 @@ int agnes_gdn_set_wait_limit(uint32_t polls);
  * state carried between stages in the workspace.  The stages change the schedule only: the
  * results are the same bit for bit.  `cuts` (host, n_cuts values) must increase strictly inside
  * (0, 40), 0 <= n_cuts <= 7; n_cuts = 0 runs every call in one stage.  The default is one cut at
- * 24 (two stages, the first 3/5 of the chunks).  Not meant to change while calls are being
+ * 26 (two stages, the first 13/20 of the chunks).  Not meant to change while calls are being
  * launched from other threads.  Returns AGNES_OK, or AGNES_ERR_INVALID_ARG (nothing changed)
  * for any other list.
  */

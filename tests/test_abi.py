@@ -350,7 +350,7 @@ def test_stage_cuts_are_checked_on_the_host(lib):
     assert lib.agnes_gdn_set_prefill_stages(None, -1) == INV
     assert lib.agnes_gdn_set_prefill_stages(None, 0) == 0
     assert lib.agnes_gdn_set_prefill_stages(*cuts(1, 2, 3, 4, 5, 6, 39)) == 0
-    assert lib.agnes_gdn_set_prefill_stages(*cuts(24)) == 0
+    assert lib.agnes_gdn_set_prefill_stages(*cuts(26)) == 0  # the default again
     assert lib.agnes_gdn_last_hip_error() == 0
 
 def test_noalloc_refuses_a_workspace_beyond_its_own_on_the_host(lib):

@@ -117,7 +117,7 @@ def test_layer_prefill_equals_two_calls():
 def test_layer_prefill_in_two_stages():
     """Long sequences on a grid that leaves a quarter of the chip free: the call runs as two stages
     (the prep of the second beside the scan of the first, the state carried over in between).
-    Ragged lengths split at 3/5 of each sequence's chunks, empty and one-token sequences, conv
+    Ragged lengths split at 13/20 of each sequence's chunks, empty and one-token sequences, conv
     history and initial states; o, the final state and the conv history bit-equal to the two-call
     path, y within a few fp32 ulps of it and within tolerance of the oracle."""
     rng = np.random.default_rng(650)
@@ -318,7 +318,7 @@ def _run_layer_big(d):
 
 
 def test_layer_prefill_long_t65536():
-    """One sequence of 65536 tokens (1024 chunks, split at 3/5 between the two stages) with an
+    """One sequence of 65536 tokens (1024 chunks, split at 13/20 between the two stages) with an
     initial state, through the whole-layer call; the oracle follows value heads 0, 5, .., 45 over
     the whole sequence, and the first 128 tokens (where the initial state still dominates) are
     gated on their own."""
