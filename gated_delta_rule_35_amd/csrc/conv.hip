@@ -42,7 +42,7 @@ __device__ __forceinline__ void conv_token(const ConvArgs& a, const float w[8][4
     y[e] = active ? silu(acc) : 0.f;
     ss = fmaf(y[e], y[e], ss);
   }
-  ss = sum16(ss);
+  ss = sum16_dpp(ss);
   if (l2) {
     const float r = rsqrt_fast(ss + a.eps);
 #pragma unroll

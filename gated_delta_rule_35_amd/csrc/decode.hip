@@ -58,7 +58,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   float kq = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) kq = fmaf(kv[e], qv[e], kq);
-  kq = sum16(kq);
+  kq = sum16_dpp(kq);
 
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
@@ -71,8 +71,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
       sk = fmaf(x[e], kv[e], sk);
       sq = fmaf(x[e], qv[e], sq);
     }
-    sk = sum16(sk);
-    sq = sum16(sq);
+    sk = sum16_dpp(sk);
+    sq = sum16_dpp(sq);
     const float d = beta * (vrow[p] - alpha * sk);
     float y[8];
 #pragma unroll

@@ -52,7 +52,7 @@ __device__ __forceinline__ void fd_conv_item(const FusedDecodeArgs& a, int b, in
     y[e] = silu(acc);
     ss = fmaf(y[e], y[e], ss);
   }
-  ss = sum16(ss);  // the 16 items of one head are 16 consecutive lanes
+  ss = sum16_dpp(ss);  // the 16 items of one head are 16 consecutive lanes
   const float r = l2 ? rsqrt_fast(ss + a.l2_eps) : 1.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) dst[e] = y[e] * r;
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(FusedDecodeArgs a) {
   float kq = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) kq = fmaf(kv[e], qv[e], kq);
-  kq = sum16(kq);
+  kq = sum16_dpp(kq);
 
   for (int j = 0; j < G; ++j) {
     if (j > 0 || DT != DT_BF16) load_state(j);
@@ -146,8 +146,8 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(FusedDecodeArgs a) {
         sk = fmaf(x[e], kv[e], sk);
         sq = fmaf(x[e], qv[e], sq);
       }
-      sk = sum16(sk);
-      sq = sum16(sq);
+      sk = sum16_dpp(sk);
+      sq = sum16_dpp(sq);
       const float d = beta * (v_s[j * 128 + row] - alpha * sk);
       float y[8];
 #pragma unroll
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(FusedDecodeArgs a) {
       const int64_t rb = bh * 128;
       const float o0 = oj[2 * l], o1 = oj[2 * l + 1];
       float ss = fmaf(o0, o0, o1 * o1);
-      ss = sum16(ss);
+      ss = sum16_dpp(ss);
       ss += __shfl_xor(ss, 16);
       ss += __shfl_xor(ss, 32);
       const float r = rsqrt_fast(ss * (1.0f / 128.0f) + a.norm_eps);
