@@ -436,6 +436,8 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
     }
     const uint16_t (*X)[D] = hs ? sm.u.qk.Xk : sm.u.qk.Xq;
     const uint16_t* hist = static_cast<const uint16_t*>(a.conv_hist);
+    // the first round of a key group also writes the fp16 q/k image, straight from the conv
+    QKImage* img = reinterpret_cast<QKImage*>(base + ws.qk + ((size_t)kh * maxch + j) * QK_BYTES);
     const bool head = c0 - 3 < start;  // the sequence's first chunk: the halo is the history
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
@@ -469,6 +471,7 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
 #pragma unroll
       for (int e = 0; e < 8; ++e) hv[e] = r < L ? (_Float16)(y[e] * rs) : (_Float16)0.f;
       *reinterpret_cast<h8*>(hs ? &sm.u.qk.K[r][8 * col] : &sm.u.qk.Q[r][8 * col]) = hv;
+      if (rd == 0) *reinterpret_cast<h8*>(hs ? &img->K[r][8 * col] : &img->Q[r][8 * col]) = hv;
     }
     lds_barrier();
   }
@@ -480,7 +483,7 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
   }
 
   // ---- Gram blocks K K^T and Q K^T (bf16 matrix cores): wave w < 10 takes lower block pair w.
-  // The first round of a key group also writes the fp16 q/k image (rows >= L zero).
+  // The first round of a key group of the plain call also writes the fp16 q/k image (rows >= L zero).
   f4 gk = {0.f, 0.f, 0.f, 0.f}, gq = gk;
   int bi = 0, bj = 0;
   if (w < 10) {
@@ -488,30 +491,31 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int col = 32 * ks + 8 * lg;
+      // gq is the transpose, K_bj Q_bi^T, so that a lane holds four consecutive columns of a row
+      // of P (one 8-byte store per head below)
       if constexpr (FUSED) {  // fp16 rows
         const h8 kbv = *reinterpret_cast<const h8*>(&sm.u.qk.K[16 * bj + ln][col]);
         gk = mfma_16x16x32(*reinterpret_cast<const h8*>(&sm.u.qk.K[16 * bi + ln][col]), kbv, gk);
-        gq = mfma_16x16x32(*reinterpret_cast<const h8*>(&sm.u.qk.Q[16 * bi + ln][col]), kbv, gq);
+        gq = mfma_16x16x32(kbv, *reinterpret_cast<const h8*>(&sm.u.qk.Q[16 * bi + ln][col]), gq);
       } else {
         const bf8 kbv = *reinterpret_cast<const bf8*>(&sm.u.qk.K[16 * bj + ln][col]);
         gk = mfma_bf(*reinterpret_cast<const bf8*>(&sm.u.qk.K[16 * bi + ln][col]), kbv, gk);
-        gq = mfma_bf(*reinterpret_cast<const bf8*>(&sm.u.qk.Q[16 * bi + ln][col]), kbv, gq);
+        gq = mfma_bf(kbv, *reinterpret_cast<const bf8*>(&sm.u.qk.Q[16 * bi + ln][col]), gq);
       }
     }
   }
-  if (rd == 0) {
+  if (!FUSED && rd == 0) {  // the fp16 q/k image of the plain call (the fused one wrote it in the conv)
     QKImage* img = reinterpret_cast<QKImage*>(base + ws.qk + ((size_t)kh * maxch + j) * QK_BYTES);
     for (int i = tid; i < 2 * C * (D / 8); i += 256 * PH) {
       const bool isk = i >= C * (D / 8);
       const int r = (i >> 4) & (C - 1), col = 8 * (i & 15);
       const uint4 u = *reinterpret_cast<const uint4*>(isk ? &sm.u.qk.K[r][col] : &sm.u.qk.Q[r][col]);
-      if (!FUSED && r < L) {  // bf16 magnitudes from 65536 up (0x4780) do not fit fp16
+      if (r < L) {  // bf16 magnitudes from 65536 up (0x4780) do not fit fp16
         const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) bad |= (wv[e] & 0x7fffu) >= 0x4780u || ((wv[e] >> 16) & 0x7fffu) >= 0x4780u;
       }
-      *reinterpret_cast<h8*>(isk ? &img->K[r][col] : &img->Q[r][col]) =
-          FUSED ? __builtin_bit_cast(h8, u) : cvt8(r < L ? u : make_uint4(0, 0, 0, 0));
+      *reinterpret_cast<h8*>(isk ? &img->K[r][col] : &img->Q[r][col]) = cvt8(r < L ? u : make_uint4(0, 0, 0, 0));
     }
   }
   lds_barrier();  // q/k rows are dead from here
@@ -520,7 +524,8 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
   // A (fp32, LDS) and P (fp16, record, zero above the diagonal).  Waves 10, 11 write the two
   // blocks of P above the diagonal that the scan reads, (0,1) and (2,3), as zeros.
   if (w < 10) {
-    const int s2 = 16 * bj + ln, r0 = 16 * bi + 4 * lg;
+    const int s2 = 16 * bj + ln, r0 = 16 * bi + 4 * lg;  // gk: rows r0 + e, column s2
+    const int pr = 16 * bi + ln, ps = 16 * bj + 4 * lg;  // gq: row pr, columns ps + e
 #pragma unroll
     for (int zz = 0; zz < PH; ++zz) {
       if (rd * PH + zz >= grp) break;
@@ -529,16 +534,19 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
       const f4 gr = *reinterpret_cast<const f4*>(&sm.gam[zz][r0]);
       const f4 br = *reinterpret_cast<const f4*>(&sm.bet[zz][r0]);
       const float gs = sm.gam[zz][s2];
-      _Float16* pz = reinterpret_cast<_Float16*>(rz + offsetof(RecImage, P));
+      const float gpr = sm.gam[zz][pr];
+      const f4 gps = *reinterpret_cast<const f4*>(&sm.gam[zz][ps]);
+      h4 pv4;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = r0 + e;
-        const float d = s2 <= r ? __expf(gr[e] - gs) : 0.f;
-        sm.u.hd[zz].A[w][4 * lg + e][ln] = s2 < r ? br[e] * d * gk[e] : 0.f;
-        const float pv = s2 <= r ? d * gq[e] : 0.f;
+        const float d = s2 < r ? __expf(gr[e] - gs) : 0.f;
+        sm.u.hd[zz].A[w][4 * lg + e][ln] = br[e] * d * gk[e];
+        const float pv = ps + e <= pr ? __expf(gpr - gps[e]) * gq[e] : 0.f;
         bad |= !fp16_range(pv);
-        pz[r * LDT + s2] = (_Float16)pv;
+        pv4[e] = (_Float16)pv;
       }
+      *reinterpret_cast<h4*>(rz + offsetof(RecImage, P) + (pr * LDT + ps) * 2) = pv4;
     }
   } else {
     for (int i = tid - 640; i < PH * 2 * 16 * 2; i += 128) {  // (head, block, row, half row)
