@@ -2,6 +2,7 @@
 // Every check runs before anything is enqueued; a failed check launches nothing.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdint>
@@ -22,16 +23,29 @@ bool aligned(const void* p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 bool valid_dtype(int d) { return d == AGNES_F32 || d == AGNES_BF16; }
 size_t esize(int d) { return d == AGNES_BF16 ? 2 : 4; }
 
-// Byte span [lo, hi) touched by `rows` rows of `width` elements at `stride` elements.
+// Tokens of one call: cu_seqlens are int32.
+constexpr int64_t kMaxTokens = INT32_MAX;
+
+// Byte span [lo, hi) touched by `rows` rows of `width` elements at `stride` elements (a NULL
+// buffer touches nothing).  The extent is computed exactly in 128 bits; `wraps` marks one that
+// runs past the end of the address space, which no buffer can: such a span overlaps every
+// non-empty span, so the overlap checks reject it.
 struct Span {
   uintptr_t lo, hi;
+  bool wraps;
 };
 Span span(const void* p, int64_t rows, int64_t stride, int64_t width, size_t es) {
   const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
-  if (rows <= 0 || width <= 0) return {lo, lo};
-  return {lo, lo + (uintptr_t)(((rows - 1) * stride + width) * (int64_t)es)};
+  if (!p || rows <= 0 || width <= 0) return {lo, lo, false};
+  using u128 = unsigned __int128;
+  const u128 end = (u128)lo + ((u128)(uint64_t)(rows - 1) * (uint64_t)stride + (uint64_t)width) * es;
+  if (stride < 0 || end > UINTPTR_MAX) return {lo, UINTPTR_MAX, true};
+  return {lo, (uintptr_t)end, false};
 }
-bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+bool overlap(Span a, Span b) {
+  if (a.lo == a.hi || b.lo == b.hi) return false;
+  return a.wraps || b.wraps || (a.lo < b.hi && b.lo < a.hi);
+}
 
 int hip_status(hipError_t e) {
   if (e == hipSuccess) return AGNES_OK;
@@ -70,7 +84,8 @@ AGNES_API int agnes_gdn_conv(const void* x, int64_t x_token_stride, void* y, int
   if (!aligned(x, 16) || !aligned(y, 16) || !aligned(weight, 4) || (bias && !aligned(bias, 4)) ||
       (conv_state && !aligned(conv_state, 4)))
     return AGNES_ERR_INVALID_ARG;
-  if (num_seqs < 0 || total_tokens < 0 || channels <= 0 || channels % 8) return AGNES_ERR_INVALID_ARG;
+  if (num_seqs < 0 || total_tokens < 0 || total_tokens > kMaxTokens || channels <= 0 || channels % 8)
+    return AGNES_ERR_INVALID_ARG;
   if (x_token_stride < channels || y_token_stride < channels || x_token_stride % 8 || y_token_stride % 8)
     return AGNES_ERR_INVALID_ARG;
   if (l2norm_heads < 0 || !(l2norm_eps >= 0.f) || !std::isfinite(l2norm_eps)) return AGNES_ERR_INVALID_ARG;
@@ -99,13 +114,26 @@ AGNES_API int agnes_gdn_conv(const void* x, int64_t x_token_stride, void* y, int
   return hip_status(agnes::launch_conv(a, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+// Status of a prefill problem's counts: invalid counts, then shapes outside the supported set
+// (head_dim, Hv % Hk, 32-bit (sequence, head) indexing, launches that do not fit the grid limit).
+int prefill_shape(int num_seqs, int64_t total_tokens, int num_k_heads, int num_v_heads, int head_dim, bool mfma) {
+  if (num_seqs < 0 || total_tokens < 0 || total_tokens > kMaxTokens || num_k_heads <= 0 || num_v_heads <= 0)
+    return AGNES_ERR_INVALID_ARG;
+  if (head_dim != kHeadDim || num_v_heads % num_k_heads) return AGNES_ERR_UNSUPPORTED;
+  if (num_seqs == 0 && total_tokens != 0) return AGNES_ERR_INVALID_ARG;
+  if ((int64_t)num_seqs * num_v_heads > INT32_MAX / 8) return AGNES_ERR_UNSUPPORTED;
+  const bool fits = mfma ? agnes::prefill_mfma_fits(num_seqs, total_tokens, num_k_heads, num_v_heads)
+                         : agnes::prefill_f32_fits(num_seqs, num_v_heads);
+  return fits ? AGNES_OK : AGNES_ERR_UNSUPPORTED;
+}
+}  // namespace
+
 AGNES_API size_t agnes_gdn_prefill_workspace_size(int num_seqs, int64_t total_tokens, int num_k_heads,
                                                   int num_v_heads, int head_dim, agnes_dtype in_dtype) {
-  if (num_seqs < 0 || total_tokens < 0 || num_k_heads <= 0 || num_v_heads <= 0 || head_dim != kHeadDim ||
-      num_v_heads % num_k_heads || !valid_dtype(in_dtype))
+  if (in_dtype != AGNES_BF16 || prefill_shape(num_seqs, total_tokens, num_k_heads, num_v_heads, head_dim, true))
     return 0;
-  if (in_dtype == AGNES_BF16) return agnes::prefill_mfma_workspace(num_seqs, total_tokens, num_k_heads, num_v_heads);
-  return 0;
+  return agnes::prefill_mfma_workspace(num_seqs, total_tokens, num_k_heads, num_v_heads);
 }
 
 AGNES_API int agnes_gdn_prefill_chunked(const void* q, const void* k, const void* v, agnes_dtype in_dtype,
@@ -116,9 +144,8 @@ AGNES_API int agnes_gdn_prefill_chunked(const void* q, const void* k, const void
                                         agnes_dtype o_dtype, void* workspace, size_t workspace_bytes,
                                         void* stream) {
   if (!valid_dtype(in_dtype) || !valid_dtype(o_dtype)) return AGNES_ERR_INVALID_ARG;
-  if (num_seqs < 0 || total_tokens < 0 || num_k_heads <= 0 || num_v_heads <= 0) return AGNES_ERR_INVALID_ARG;
-  if (head_dim != kHeadDim || num_v_heads % num_k_heads) return AGNES_ERR_UNSUPPORTED;
-  if (num_seqs == 0 && total_tokens != 0) return AGNES_ERR_INVALID_ARG;
+  if (const int st = prefill_shape(num_seqs, total_tokens, num_k_heads, num_v_heads, head_dim, in_dtype == AGNES_BF16))
+    return st;
   if (num_seqs > 0 && !cu_seqlens) return AGNES_ERR_INVALID_ARG;
   if (total_tokens > 0 && (!q || !k || !v || !g || !beta || !o)) return AGNES_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(g, 4) ||
@@ -128,7 +155,6 @@ AGNES_API int agnes_gdn_prefill_chunked(const void* q, const void* k, const void
       qk_token_stride % 8 || v_token_stride % 8)
     return AGNES_ERR_INVALID_ARG;
   if (!std::isfinite(scale)) return AGNES_ERR_INVALID_ARG;
-  if ((int64_t)num_seqs * num_v_heads * 8 > INT32_MAX) return AGNES_ERR_UNSUPPORTED;
   const int64_t sbytes = (int64_t)num_seqs * num_v_heads * head_dim * head_dim;
   const Span s0 = span(initial_state, 1, 0, sbytes, 4), s1 = span(final_state, 1, 0, sbytes, 4);
   if (initial_state && final_state && initial_state != final_state && overlap(s0, s1)) return AGNES_ERR_INVALID_ARG;
@@ -159,19 +185,17 @@ AGNES_API int agnes_gdn_prefill_fused(const void* x, int64_t x_token_stride, agn
                                       void* o, agnes_dtype o_dtype, void* workspace, size_t workspace_bytes,
                                       void* stream) {
   if (!valid_dtype(dtype) || !valid_dtype(o_dtype)) return AGNES_ERR_INVALID_ARG;
-  if (num_seqs < 0 || total_tokens < 0 || num_k_heads <= 0 || num_v_heads <= 0) return AGNES_ERR_INVALID_ARG;
-  if (head_dim != kHeadDim || num_v_heads % num_k_heads || dtype != AGNES_BF16) return AGNES_ERR_UNSUPPORTED;
-  if (num_seqs == 0 && total_tokens != 0) return AGNES_ERR_INVALID_ARG;
+  if (const int st = prefill_shape(num_seqs, total_tokens, num_k_heads, num_v_heads, head_dim, true)) return st;
+  if (dtype != AGNES_BF16 || num_seqs > 65535) return AGNES_ERR_UNSUPPORTED;
   if (num_seqs > 0 && (!cu_seqlens || !conv_weight)) return AGNES_ERR_INVALID_ARG;
   if (total_tokens > 0 && (!x || !g || !beta || !o)) return AGNES_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(conv_weight, 16) || !aligned(conv_bias, 16) || !aligned(conv_state, 4) ||
       !aligned(o, 16) || !aligned(g, 4) || !aligned(beta, 4) || !aligned(initial_state, 16) ||
       !aligned(final_state, 16) || !aligned(cu_seqlens, 4))
     return AGNES_ERR_INVALID_ARG;
-  const int64_t C = (int64_t)(2 * num_k_heads + num_v_heads) * head_dim;
+  const int64_t C = (2 * (int64_t)num_k_heads + num_v_heads) * head_dim;
   if (x_token_stride < C || x_token_stride % 8) return AGNES_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !(l2norm_eps >= 0.f) || !std::isfinite(l2norm_eps)) return AGNES_ERR_INVALID_ARG;
-  if ((int64_t)num_seqs * num_v_heads * 8 > INT32_MAX || (int64_t)num_seqs > 65535) return AGNES_ERR_UNSUPPORTED;
   const int64_t sbytes = (int64_t)num_seqs * num_v_heads * head_dim * head_dim;
   const Span s0 = span(initial_state, 1, 0, sbytes, 4), s1 = span(final_state, 1, 0, sbytes, 4);
   if (initial_state && final_state && initial_state != final_state && overlap(s0, s1)) return AGNES_ERR_INVALID_ARG;
@@ -179,7 +203,7 @@ AGNES_API int agnes_gdn_prefill_fused(const void* x, int64_t x_token_stride, agn
   const Span os = span(o, total_tokens, rowo, rowo, esize(o_dtype));
   const Span xs = span(x, total_tokens, x_token_stride, C, 2);
   const Span cs = span(conv_state, conv_state ? 1 : 0, 0, (int64_t)num_seqs * C * 3, 2);
-  const Span ws_span = span(workspace, workspace ? 1 : 0, 0, (int64_t)workspace_bytes, 1);
+  const Span ws_span = span(workspace, 1, 0, (int64_t)std::min<size_t>(workspace_bytes, INT64_MAX), 1);
   // outputs and in-place buffers must be disjoint from each other and from every input
   if (overlap(os, xs) || overlap(os, s1) || overlap(os, s0) || overlap(os, cs) || overlap(cs, xs) || overlap(cs, s1) ||
       overlap(cs, s0) || overlap(s1, xs) || overlap(ws_span, os) || overlap(ws_span, xs) || overlap(ws_span, cs) ||
@@ -189,8 +213,11 @@ AGNES_API int agnes_gdn_prefill_fused(const void* x, int64_t x_token_stride, agn
                                                        AGNES_BF16);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return AGNES_ERR_WORKSPACE;
 
+  // the q | k | v channel ranges of x (an empty batch may pass no x at all)
   const uint16_t* xb = static_cast<const uint16_t*>(x);
-  agnes::PrefillArgs a{xb, xb + (int64_t)num_k_heads * head_dim, xb + (int64_t)2 * num_k_heads * head_dim,
+  const uint16_t* xk = xb ? xb + (int64_t)num_k_heads * head_dim : nullptr;
+  const uint16_t* xv = xb ? xb + 2 * (int64_t)num_k_heads * head_dim : nullptr;
+  agnes::PrefillArgs a{xb, xk, xv,
                        (int)AGNES_BF16, x_token_stride, x_token_stride, g, beta, cu_seqlens, num_seqs, total_tokens,
                        num_k_heads, num_v_heads, scale, initial_state, final_state, o, (int)o_dtype, workspace,
                        workspace_bytes, conv_weight, conv_bias, conv_state, l2norm_eps};
@@ -216,6 +243,7 @@ AGNES_API int agnes_gdn_decode_step(const void* q, const void* k, const void* v,
   const Span ss = span(state, 1, 0, (int64_t)batch * num_v_heads * head_dim * head_dim, 4);
   const Span os = span(o, batch, (int64_t)num_v_heads * head_dim, (int64_t)num_v_heads * head_dim, esize(o_dtype));
   if (overlap(ss, os)) return AGNES_ERR_INVALID_ARG;
+  if (!agnes::decode_fits(batch, num_v_heads)) return AGNES_ERR_UNSUPPORTED;
 
   agnes::DecodeArgs a{q, k, v, (int)in_dtype, qk_token_stride, v_token_stride, g, beta, batch, num_k_heads,
                       num_v_heads, scale, state, o, (int)o_dtype};
@@ -235,6 +263,7 @@ AGNES_API int agnes_gdn_gated_rmsnorm(const void* o, agnes_dtype o_dtype, const 
   const bool exact_alias = (o == y) && (o_dtype == y_dtype);
   if (!exact_alias && overlap(ys, osp)) return AGNES_ERR_INVALID_ARG;
   if (overlap(ys, span(z, rows, dim, dim, esize(zw_dtype)))) return AGNES_ERR_INVALID_ARG;
+  if (!agnes::norm_fits(rows)) return AGNES_ERR_UNSUPPORTED;
 
   agnes::NormArgs a{o, (int)o_dtype, z, weight, (int)zw_dtype, eps, rows, y, (int)y_dtype};
   return hip_status(agnes::launch_gated_rmsnorm(a, static_cast<hipStream_t>(stream)));
@@ -257,7 +286,7 @@ AGNES_API int agnes_gdn_decode_fused(const void* x, int64_t x_token_stride, agne
   if (!x || !conv_weight || !conv_state || !g || !beta || !z || !norm_weight || !state || !y)
     return AGNES_ERR_INVALID_ARG;
   if (!slots && num_slots < batch) return AGNES_ERR_INVALID_ARG;
-  const int64_t C = (int64_t)(2 * num_k_heads + num_v_heads) * head_dim;
+  const int64_t C = (2 * (int64_t)num_k_heads + num_v_heads) * head_dim;
   if (x_token_stride < C || x_token_stride % 8) return AGNES_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(conv_weight, 16) || !aligned(conv_bias, 16) || !aligned(conv_state, 16) ||
       !aligned(g, 4) || !aligned(beta, 4) || !aligned(z, 4) || !aligned(norm_weight, 4) || !aligned(state, 16) ||
@@ -283,6 +312,7 @@ AGNES_API int agnes_gdn_decode_fused(const void* x, int64_t x_token_stride, agne
     for (const Span& in : ins)
       if (overlap(outs[i], in)) return AGNES_ERR_INVALID_ARG;
   }
+  if (!agnes::decode_fused_fits(batch, num_k_heads)) return AGNES_ERR_UNSUPPORTED;
 
   agnes::FusedDecodeArgs a{x, x_token_stride, (int)dtype, conv_weight, conv_bias, conv_state, g, beta, z,
                            norm_weight, state, slots, num_slots, batch, num_k_heads, num_v_heads, scale,
@@ -291,7 +321,7 @@ AGNES_API int agnes_gdn_decode_fused(const void* x, int64_t x_token_stride, agne
 }
 
 AGNES_API size_t agnes_attn_prefill_workspace_size(int num_seqs, int64_t total_tokens) {
-  if (num_seqs < 0 || total_tokens < 0) return 0;
+  if (num_seqs < 0 || total_tokens < 0 || total_tokens > kMaxTokens) return 0;
   return agnes::attn_prefill_workspace(num_seqs, total_tokens);
 }
 
@@ -305,7 +335,8 @@ AGNES_API int agnes_attn_prefill(const void* q, int64_t q_token_stride, const vo
                                  agnes_dtype o_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   constexpr int kAttnDim = 256;
   if (!valid_dtype(o_dtype)) return AGNES_ERR_INVALID_ARG;
-  if (num_seqs < 0 || total_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0) return AGNES_ERR_INVALID_ARG;
+  if (num_seqs < 0 || total_tokens < 0 || total_tokens > kMaxTokens || num_q_heads <= 0 || num_kv_heads <= 0)
+    return AGNES_ERR_INVALID_ARG;
   if (head_dim != kAttnDim || rot_dim != 64 || num_q_heads % num_kv_heads) return AGNES_ERR_UNSUPPORTED;
   if (num_seqs == 0 && total_tokens != 0) return AGNES_ERR_INVALID_ARG;
   if (num_seqs > 0 && !cu_seqlens) return AGNES_ERR_INVALID_ARG;
@@ -328,7 +359,7 @@ AGNES_API int agnes_attn_prefill(const void* q, int64_t q_token_stride, const vo
   if (!std::isfinite(rope_base) || rope_base <= 0.f || !std::isfinite(norm_eps) || norm_eps < 0.f ||
       !std::isfinite(scale))
     return AGNES_ERR_INVALID_ARG;
-  if (((total_tokens + 127) / 128 + num_seqs) * (int64_t)num_q_heads >= INT32_MAX) return AGNES_ERR_UNSUPPORTED;
+  if (!agnes::attn_prefill_fits(num_seqs, total_tokens, num_q_heads, num_kv_heads)) return AGNES_ERR_UNSUPPORTED;
   const Span os = span(o, total_tokens, qw, qw, esize(o_dtype));
   const Span ks = span(k_out, total_tokens, k_out_token_stride, kw, 2);
   const Span vs = span(v_out, total_tokens, v_out_token_stride, kw, 2);
@@ -357,8 +388,14 @@ AGNES_API int agnes_attn_prefill(const void* q, int64_t q_token_stride, const vo
   return hip_status(agnes::launch_attn_prefill(a, static_cast<hipStream_t>(stream)));
 }
 
+namespace {
+constexpr int64_t kMaxCacheLen = (int64_t)1 << 30;
+}  // namespace
+
 AGNES_API size_t agnes_attn_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads, int64_t max_len) {
-  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_len <= 0) return 0;
+  if (batch <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_len <= 0 || max_len > kMaxCacheLen ||
+      num_q_heads % num_kv_heads || !agnes::attn_decode_fits(batch, num_q_heads, num_kv_heads, max_len))
+    return 0;
   return agnes::attn_decode_workspace(batch, num_q_heads, num_kv_heads, max_len);
 }
 
@@ -373,7 +410,7 @@ AGNES_API int agnes_attn_decode(const void* q, int64_t q_stride, const void* k, 
   if (!valid_dtype(o_dtype)) return AGNES_ERR_INVALID_ARG;
   if (batch < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || max_len <= 0) return AGNES_ERR_INVALID_ARG;
   if (head_dim != kAttnDim || rot_dim != 64 || num_q_heads % num_kv_heads) return AGNES_ERR_UNSUPPORTED;
-  if (max_len > (int64_t)1 << 30) return AGNES_ERR_UNSUPPORTED;
+  if (max_len > kMaxCacheLen) return AGNES_ERR_UNSUPPORTED;
   if (batch == 0) return AGNES_OK;
   if (!q || !k || !v || !gate || !q_norm_weight || !k_norm_weight || !k_cache || !v_cache || !cache_lens || !o)
     return AGNES_ERR_INVALID_ARG;
@@ -389,14 +426,15 @@ AGNES_API int agnes_attn_decode(const void* q, int64_t q_stride, const void* k, 
   if (!std::isfinite(rope_base) || rope_base <= 0.f || !std::isfinite(norm_eps) || norm_eps < 0.f ||
       !std::isfinite(scale))
     return AGNES_ERR_INVALID_ARG;
-  const int64_t cache_elems = (int64_t)batch * max_len * kw;
+  const int64_t cache_rows = (int64_t)batch * max_len;  // of kw elements each
   const Span os = span(o, batch, qw, qw, esize(o_dtype));
-  const Span kc = span(k_cache, 1, 0, cache_elems, 2), vc = span(v_cache, 1, 0, cache_elems, 2);
+  const Span kc = span(k_cache, cache_rows, kw, kw, 2), vc = span(v_cache, cache_rows, kw, kw, 2);
   const Span ins[5] = {span(q, batch, q_stride, qw, 2), span(k, batch, k_stride, kw, 2), span(v, batch, v_stride, kw, 2),
                        span(gate, batch, gate_stride, qw, 2), span(cache_lens, 1, 0, batch, 4)};
   for (const Span& in : ins)
     if (overlap(os, in) || overlap(kc, in) || overlap(vc, in)) return AGNES_ERR_INVALID_ARG;
   if (overlap(os, kc) || overlap(os, vc) || overlap(kc, vc)) return AGNES_ERR_INVALID_ARG;
+  if (!agnes::attn_decode_fits(batch, num_q_heads, num_kv_heads, max_len)) return AGNES_ERR_UNSUPPORTED;
   const size_t need = agnes::attn_decode_workspace(batch, num_q_heads, num_kv_heads, max_len);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return AGNES_ERR_WORKSPACE;
 
@@ -415,9 +453,7 @@ AGNES_API int agnes_attn_decode(const void* q, int64_t q_stride, const void* k, 
 
 AGNES_API size_t agnes_gdn_layer_prefill_workspace_size(int num_seqs, int64_t total_tokens, int num_k_heads,
                                                        int num_v_heads, int head_dim) {
-  if (num_seqs < 0 || total_tokens < 0 || num_k_heads <= 0 || num_v_heads <= 0 || head_dim != kHeadDim ||
-      num_v_heads % num_k_heads)
-    return 0;
+  if (prefill_shape(num_seqs, total_tokens, num_k_heads, num_v_heads, head_dim, true) || num_seqs > 65535) return 0;
   return agnes::layer_prefill_workspace(num_seqs, total_tokens, num_k_heads, num_v_heads);
 }
 
@@ -434,23 +470,21 @@ int layer_prefill_checked(const void* x, int64_t x_token_stride, int dtype, cons
                           float norm_eps, void* y, void* o, int out_dtype, void* workspace, size_t workspace_bytes,
                           void* stream, bool single_stage) {
   if (!valid_dtype(dtype) || !valid_dtype(out_dtype)) return AGNES_ERR_INVALID_ARG;
-  if (num_seqs < 0 || total_tokens < 0 || num_k_heads <= 0 || num_v_heads <= 0) return AGNES_ERR_INVALID_ARG;
-  if (head_dim != kHeadDim || num_v_heads % num_k_heads || dtype != AGNES_BF16) return AGNES_ERR_UNSUPPORTED;
-  if (num_seqs == 0 && total_tokens != 0) return AGNES_ERR_INVALID_ARG;
+  if (const int st = prefill_shape(num_seqs, total_tokens, num_k_heads, num_v_heads, head_dim, true)) return st;
+  if (dtype != AGNES_BF16 || num_seqs > 65535) return AGNES_ERR_UNSUPPORTED;
   if (num_seqs > 0 && (!cu_seqlens || !conv_weight || !norm_weight)) return AGNES_ERR_INVALID_ARG;
   if (total_tokens > 0 && (!x || !g || !beta || !z || !y)) return AGNES_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(conv_weight, 16) || !aligned(conv_bias, 16) || !aligned(conv_state, 4) ||
       !aligned(o, 16) || !aligned(y, 16) || !aligned(z, 16) || !aligned(norm_weight, 16) || !aligned(g, 4) ||
       !aligned(beta, 4) || !aligned(initial_state, 16) || !aligned(final_state, 16) || !aligned(cu_seqlens, 4))
     return AGNES_ERR_INVALID_ARG;
-  const int64_t C = (int64_t)(2 * num_k_heads + num_v_heads) * head_dim;
+  const int64_t C = (2 * (int64_t)num_k_heads + num_v_heads) * head_dim;
   const int64_t rowo = (int64_t)num_v_heads * head_dim;
   if (x_token_stride < C || x_token_stride % 8 || z_token_stride < rowo || z_token_stride % 8)
     return AGNES_ERR_INVALID_ARG;
   if (!std::isfinite(scale) || !(l2norm_eps >= 0.f) || !std::isfinite(l2norm_eps) || !(norm_eps >= 0.f) ||
       !std::isfinite(norm_eps))
     return AGNES_ERR_INVALID_ARG;
-  if ((int64_t)num_seqs * num_v_heads * 8 > INT32_MAX || (int64_t)num_seqs > 65535) return AGNES_ERR_UNSUPPORTED;
   const int64_t sbytes = (int64_t)num_seqs * num_v_heads * head_dim * head_dim;
   const Span s0 = span(initial_state, 1, 0, sbytes, 4), s1 = span(final_state, 1, 0, sbytes, 4);
   if (initial_state && final_state && initial_state != final_state && overlap(s0, s1)) return AGNES_ERR_INVALID_ARG;
@@ -459,7 +493,7 @@ int layer_prefill_checked(const void* x, int64_t x_token_stride, int dtype, cons
   const Span xs = span(x, total_tokens, x_token_stride, C, 2);
   const Span zs = span(z, total_tokens, z_token_stride, rowo, 2);
   const Span cs = span(conv_state, conv_state ? 1 : 0, 0, (int64_t)num_seqs * C * 3, 2);
-  const Span ws_span = span(workspace, workspace ? 1 : 0, 0, (int64_t)workspace_bytes, 1);
+  const Span ws_span = span(workspace, 1, 0, (int64_t)std::min<size_t>(workspace_bytes, INT64_MAX), 1);
   const Span outs[5] = {os, ys, cs, s1, ws_span};
   const Span ins[4] = {xs, zs, s0, span(norm_weight, 1, 0, head_dim, 2)};
   for (int i = 0; i < 5; ++i) {
@@ -471,8 +505,11 @@ int layer_prefill_checked(const void* x, int64_t x_token_stride, int dtype, cons
   const size_t need = agnes::layer_prefill_workspace(num_seqs, total_tokens, num_k_heads, num_v_heads);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 256))) return AGNES_ERR_WORKSPACE;
 
+  // the q | k | v channel ranges of x (an empty batch may pass no x at all)
   const uint16_t* xb = static_cast<const uint16_t*>(x);
-  agnes::PrefillArgs a{xb, xb + (int64_t)num_k_heads * head_dim, xb + (int64_t)2 * num_k_heads * head_dim,
+  const uint16_t* xk = xb ? xb + (int64_t)num_k_heads * head_dim : nullptr;
+  const uint16_t* xv = xb ? xb + 2 * (int64_t)num_k_heads * head_dim : nullptr;
+  agnes::PrefillArgs a{xb, xk, xv,
                        (int)AGNES_BF16, x_token_stride, x_token_stride, g, beta, cu_seqlens, num_seqs, total_tokens,
                        num_k_heads, num_v_heads, scale, initial_state, final_state, o, (int)out_dtype, workspace,
                        workspace_bytes, conv_weight, conv_bias, conv_state, l2norm_eps};

@@ -730,6 +730,16 @@ static void decode_split(int64_t batch, int hkv, int64_t max_len, int& ns, int& 
   ns = (int)((max_len + k - 1) / k);
 }
 
+// prep over (entry, query or KV head), attention over (entry, KV head, key split), combine over
+// (entry, query head); max_len is at most 2^30.
+bool attn_decode_fits(int batch, int hq, int hkv, int64_t max_len) {
+  using u128 = unsigned __int128;
+  int ns, sk;
+  decode_split(batch, hkv, max_len, ns, sk);
+  return grid_fits(((u128)batch * ((u128)hq + (u128)hkv) + 3) / 4, 256) &&
+         grid_fits((u128)batch * (u128)hkv * (u128)ns, 256) && grid_fits(((u128)batch * (u128)hq + 3) / 4, 256);
+}
+
 size_t attn_decode_workspace(int64_t batch, int hq, int hkv, int64_t max_len) {
   if (batch <= 0 || hkv <= 0) return 0;
   int ns, sk;
@@ -764,6 +774,14 @@ hipError_t launch_attn_decode(AttnArgs a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------- host side
+// offsets in one block, key preparation over (token, KV head), attention over (query block,
+// query head) with at most total / BQ + num_seqs query blocks.
+bool attn_prefill_fits(int num_seqs, int64_t total, int hq, int hkv) {
+  using u128 = unsigned __int128;
+  const u128 nblk = (u128)((total + at::BQ - 1) / at::BQ) + (u128)num_seqs;
+  return grid_fits(((u128)total * (u128)hkv + 3) / 4, 256) && grid_fits(nblk * (u128)hq, 64 * at::NWF);
+}
+
 size_t attn_prefill_workspace(int num_seqs, int64_t total) {
   if (num_seqs <= 0) return 0;
   const size_t off = ((size_t)(num_seqs + 1) * 4 + 255) & ~size_t(255);

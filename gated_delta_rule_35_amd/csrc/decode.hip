@@ -83,6 +83,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   }
 }
 
+bool decode_fits(int batch, int hv) { return grid_fits((unsigned __int128)batch * (unsigned)hv, 256); }
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   if (a.batch == 0) return hipSuccess;
   dim3 grid((unsigned)a.batch * (unsigned)a.hv), block(256);

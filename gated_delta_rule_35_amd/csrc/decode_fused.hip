@@ -185,6 +185,8 @@ static void launch_fd_o(const FusedDecodeArgs& a, dim3 grid, dim3 block, size_t 
   else hipLaunchKernelGGL((decode_fused_kernel<DT, DT_F32>), grid, block, smem, st, a);
 }
 
+bool decode_fused_fits(int batch, int hk) { return grid_fits((unsigned __int128)batch * (unsigned)hk, 256); }
+
 hipError_t launch_decode_fused(const FusedDecodeArgs& a, hipStream_t st) {
   if (a.batch == 0) return hipSuccess;
   const int G = a.hv / a.hk;

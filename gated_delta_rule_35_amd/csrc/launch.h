@@ -172,6 +172,19 @@ struct AttnArgs {
   const int32_t* cache_lens;
 };
 
+// The work-items of a launch (blocks x threads per block) are counted in 32 bits.  Each *_fits
+// below says whether every launch of a call keeps to that for the given counts; the host layer
+// reports AGNES_ERR_UNSUPPORTED, and launches nothing, when one does not.  Token counts reach
+// them at most INT32_MAX.
+inline bool grid_fits(unsigned __int128 blocks, unsigned threads) { return blocks * threads <= 0xffffffffu; }
+bool prefill_mfma_fits(int num_seqs, int64_t total, int hk, int hv);
+bool prefill_f32_fits(int num_seqs, int hv);
+bool decode_fits(int batch, int hv);
+bool decode_fused_fits(int batch, int hk);
+bool norm_fits(int64_t rows);
+bool attn_prefill_fits(int num_seqs, int64_t total, int hq, int hkv);
+bool attn_decode_fits(int batch, int hq, int hkv, int64_t max_len);
+
 hipError_t launch_attn_prefill(AttnArgs a, hipStream_t s);
 size_t attn_prefill_workspace(int num_seqs, int64_t total);
 hipError_t launch_attn_decode(AttnArgs a, hipStream_t s);

@@ -53,6 +53,8 @@ static void launch_y(const NormArgs& a, dim3 g, hipStream_t st) {
   else hipLaunchKernelGGL((gated_rmsnorm_kernel<ODT, ZDT, DT_F32>), g, dim3(256), 0, st, a);
 }
 
+bool norm_fits(int64_t rows) { return grid_fits((unsigned __int128)(rows / NORM_ROWS + (rows % NORM_ROWS != 0)), 256); }
+
 hipError_t launch_gated_rmsnorm(const NormArgs& a, hipStream_t st) {
   if (a.rows == 0) return hipSuccess;
   dim3 g((unsigned)((a.rows + NORM_ROWS - 1) / NORM_ROWS));

@@ -193,6 +193,10 @@ __global__ __launch_bounds__(256) void prefill_f32_kernel(PrefillArgs a) {
   }
 }
 
+bool prefill_f32_fits(int num_seqs, int hv) {
+  return grid_fits((unsigned __int128)num_seqs * (unsigned)hv * f32p::NB, 256);
+}
+
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st) {
   const int64_t nblk = (int64_t)a.num_seqs * a.hv * f32p::NB;
   if (nblk == 0) return hipSuccess;

@@ -1618,6 +1618,15 @@ size_t layer_prefill_workspace(int num_seqs, int64_t total, int hk, int hv) {
   return WsLayout(num_seqs, hv, hk, max_chunks(total, num_seqs)).layer_bytes;
 }
 
+// prep over (chunk, key group, round of value heads), scan over (sequence, value head, row block);
+// the whole-layer call's conv history launch is bounded by its 65535 sequences.
+bool prefill_mfma_fits(int num_seqs, int64_t total, int hk, int hv) {
+  using u128 = unsigned __int128;
+  const int64_t rounds = (hv / hk + mp::PH - 1) / mp::PH;
+  return grid_fits((u128)max_chunks(total, num_seqs) * (u128)hk * (u128)rounds, 256 * mp::PH) &&
+         grid_fits((u128)num_seqs * (u128)hv * mp::NB, 64 * mp::NWAVES);
+}
+
 template <int O_DT, bool FUSED, bool NORM>
 static hipError_t scan_attr() {
   static const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan_kernel<O_DT, FUSED, NORM>),

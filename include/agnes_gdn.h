@@ -37,7 +37,18 @@
  *   - Functions keep no state between calls and may be called concurrently
  *     from several threads on disjoint buffers.
  *   - Supported set: head_dim 128, conv kernel_size 4, Hv a multiple of Hk.
- *     Anything else returns AGNES_ERR_UNSUPPORTED.
+ *     Anything else returns AGNES_ERR_UNSUPPORTED.  So does a problem so large
+ *     that one of its launches would exceed the device's grid (a launch counts
+ *     its work-items in 32 bits).  In round numbers: a prefill of 2^21 or more
+ *     (sequence, value head) pairs or of more than about 2^28.4 / Hk tokens (22M
+ *     at Hk = 16); from 2^24 (entry, value head) pairs of a decode step, 2^24
+ *     (entry, key head) pairs of a fused decode step, 2^31 rows of a gated
+ *     RMS-norm or 2^26 / Hkv tokens of an attention prefill on.
+ *   - Sizes: a call takes at most INT32_MAX tokens (cu_seqlens are int32); more
+ *     is AGNES_ERR_INVALID_ARG.  A buffer whose extent, from its size and
+ *     stride, runs past the end of the address space is AGNES_ERR_INVALID_ARG
+ *     too (it overlaps everything).  The workspace size queries return 0 for
+ *     every problem the matching call rejects.
  */
 #ifndef AGNES_GDN_H
 #define AGNES_GDN_H
@@ -59,7 +70,11 @@ typedef enum agnes_status {
 
 typedef enum agnes_dtype {
   AGNES_F32 = 0,  /* IEEE binary32 */
-  AGNES_BF16 = 1  /* bfloat16 (top half of binary32); stores round to nearest even */
+  AGNES_BF16 = 1, /* bfloat16 (top half of binary32); stores round to nearest even */
+  /* Not a type.  It widens the enum to every value from 0 to INT32_MAX, so that any such
+   * value a caller passes is a valid object of this type (C++ leaves values beyond an enum's
+   * range undefined); the calls reject everything but the two types above. */
+  AGNES_DTYPE_MAX_ENUM = 0x7fffffff
 } agnes_dtype;
 
 /*
@@ -332,7 +347,7 @@ int agnes_gdn_layer_prefill_noalloc(const void* x, int64_t x_token_stride, agnes
 
 /*
  * agnes_attn_prefill_workspace_size — bytes of device workspace agnes_attn_prefill
- * needs (0 for an empty batch).
+ * needs (0 for an empty batch or more than INT32_MAX tokens).
  */
 size_t agnes_attn_prefill_workspace_size(int num_seqs, int64_t total_tokens);
 
@@ -383,7 +398,8 @@ int agnes_attn_prefill(const void* q, int64_t q_token_stride, const void* k, int
 
 /*
  * agnes_attn_decode_workspace_size — bytes of device workspace agnes_attn_decode
- * needs for this batch, head count and cache length (0 for an empty batch).
+ * needs for this batch, head count and cache length (0 for an empty batch and
+ * for counts outside the supported set).
  */
 size_t agnes_attn_decode_workspace_size(int batch, int num_q_heads, int num_kv_heads,
                                         int64_t max_len);
