@@ -7,15 +7,14 @@
 
 namespace agnes {
 
-// p[i] *= a over n4 16-byte vectors, grid-stride.  Each vector is read once and written once.
-__global__ __launch_bounds__(256) void rmw_stream_kernel(float4* __restrict__ p, size_t n4, float a) {
+// p[i] *= a over n4 16-byte vectors, grid-stride.  Each vector is read once and written once,
+// with the non-temporal hint on both (the decode step's own access, and the faster of the two
+// forms on gfx950).
+typedef float f4v __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void rmw_stream_kernel(f4v* __restrict__ p, size_t n4, float a) {
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
-    float4 v = p[i];
-    v.x *= a;
-    v.y *= a;
-    v.z *= a;
-    v.w *= a;
-    p[i] = v;
+    const f4v v = __builtin_nontemporal_load(p + i);
+    __builtin_nontemporal_store(v * a, p + i);
   }
 }
 
@@ -25,7 +24,6 @@ __global__ __launch_bounds__(256) void rmw_stream_kernel(float4* __restrict__ p,
 // products are written as inline assembly so that the accumulators stay in the vector
 // registers the products read (no copies between register files inside the loop).
 typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
-typedef float f4v __attribute__((ext_vector_type(4)));
 #define AGNES_MFMA_BF16(acc) asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b))
 __global__ __launch_bounds__(256) void mfma_peak_kernel(float* sink, int iters) {
   bf8v a, b;
@@ -56,7 +54,7 @@ __global__ __launch_bounds__(256) void mfma_peak_kernel(float* sink, int iters) 
 hipError_t launch_rmw_stream(void* p, size_t bytes, hipStream_t s) {
   const size_t n4 = bytes / 16;
   if (n4 == 0) return hipSuccess;
-  hipLaunchKernelGGL(rmw_stream_kernel, dim3(1024), dim3(256), 0, s, static_cast<float4*>(p), n4, 1.0f);
+  hipLaunchKernelGGL(rmw_stream_kernel, dim3(1024), dim3(256), 0, s, static_cast<f4v*>(p), n4, 1.0f);
   return hipGetLastError();
 }
 

@@ -8,8 +8,9 @@
 // with xh taken from the sequence's conv history before its first token.  HBM-bound
 // streaming kernels: each thread owns 8 consecutive channels (one 16-byte bf16 vector)
 // and walks a block of tokens, keeping the three previous inputs in registers, so x is
-// read once (plus a 3-token halo per block) and y written once.  Sixteen lanes cover one
-// 128-channel head, so the L2 norm is a 16-lane reduction at each token.
+// read once (plus a 3-token halo per block) and y written once, with non-temporal stores.
+// Sixteen lanes cover one 128-channel head, so the L2 norm is a 16-lane reduction at each
+// token.
 #include "common.h"
 #include "launch.h"
 
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_prefill_kernel(ConvArgs a) 
         float xc[8], y[8];
         widen8<DT>(xb[b & 1][i], xc);
         conv_token<DT>(a, w, bias, h[0], h[1], h[2], xc, l2, active, y);
-        if (active) store8<DT>(a.y, (t0 + b * CONV_BATCH + i) * a.y_stride + c0, y);
+        if (active) store8_nt<DT>(a.y, (t0 + b * CONV_BATCH + i) * a.y_stride + c0, y);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           h[0][e] = h[1][e];
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_prefill_kernel(ConvArgs a) 
       for (int e = 0; e < 8; ++e) xc[e] = 0.f;
     }
     conv_token<DT>(a, w, bias, h[0], h[1], h[2], xc, l2, active, y);
-    if (active) store8<DT>(a.y, t * a.y_stride + c0, y);
+    if (active) store8_nt<DT>(a.y, t * a.y_stride + c0, y);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       h[0][e] = h[1][e];
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_decode_kernel(ConvArgs a) {
   }
   conv_token<DT>(a, w, bias, h[0], h[1], h[2], xc, l2, active, y);
   if (!active) return;
-  store8<DT>(a.y, (int64_t)n * a.y_stride + c0, y);
+  store8_nt<DT>(a.y, (int64_t)n * a.y_stride + c0, y);
   const int64_t base = ((int64_t)n * a.channels + c0) * 3;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {

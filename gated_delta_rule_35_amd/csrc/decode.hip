@@ -30,12 +30,12 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   const int c = (l & 15) * 4;
 
   float* S = a.state + (int64_t)bh * (128 * 128);
-  float4 s[8][2];
+  f4 s[8][2];  // streaming loads and stores: the state is read once and written once
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int row = p * 16 + w * 4 + sub;
-    s[p][0] = *reinterpret_cast<const float4*>(S + row * 128 + c);
-    s[p][1] = *reinterpret_cast<const float4*>(S + row * 128 + 64 + c);
+    s[p][0] = load_f4_stream(S + row * 128 + c);
+    s[p][1] = load_f4_stream(S + row * 128 + 64 + c);
   }
 
   const int64_t qk_base = (int64_t)b * a.qk_stride + (int64_t)kh * 128;
@@ -77,8 +77,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
     float y[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = fmaf(alpha, x[e], d * kv[e]);
-    *reinterpret_cast<float4*>(S + row * 128 + c) = make_float4(y[0], y[1], y[2], y[3]);
-    *reinterpret_cast<float4*>(S + row * 128 + 64 + c) = make_float4(y[4], y[5], y[6], y[7]);
+    store_f4_stream(S + row * 128 + c, f4{y[0], y[1], y[2], y[3]});
+    store_f4_stream(S + row * 128 + 64 + c, f4{y[4], y[5], y[6], y[7]});
     if ((l & 15) == 0) store1<O_DT>(a.o, (int64_t)bh * 128 + row, a.scale * fmaf(alpha, sq, d * kq));
   }
 }

@@ -92,14 +92,14 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(FusedDecodeArgs a) {
   float* v_s = fd_smem + 256;  // [G][128]
   float* o_s = v_s + G * 128;  // [4][128]: o of head j in slot j % 4, normalised by wave j % 4
 
-  float4 s[8][2];
+  f4 s[8][2];  // streaming loads and stores: each state is read once and written once
   auto load_state = [&](int j) {
     const float* S = a.state + ((int64_t)slot * a.hv + (int64_t)kh * G + j) * (128 * 128);
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const int row = p * 16 + w * 4 + sub;
-      s[p][0] = *reinterpret_cast<const float4*>(S + row * 128 + c);
-      s[p][1] = *reinterpret_cast<const float4*>(S + row * 128 + 64 + c);
+      s[p][0] = load_f4_stream(S + row * 128 + c);
+      s[p][1] = load_f4_stream(S + row * 128 + 64 + c);
     }
   };
   if (DT == DT_BF16) load_state(0);  // (f32 inputs: after the conv, fewer live registers)
@@ -152,8 +152,8 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(FusedDecodeArgs a) {
       float y[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) y[e] = fmaf(alpha, x[e], d * kv[e]);
-      *reinterpret_cast<float4*>(S + row * 128 + c) = make_float4(y[0], y[1], y[2], y[3]);
-      *reinterpret_cast<float4*>(S + row * 128 + 64 + c) = make_float4(y[4], y[5], y[6], y[7]);
+      store_f4_stream(S + row * 128 + c, f4{y[0], y[1], y[2], y[3]});
+      store_f4_stream(S + row * 128 + 64 + c, f4{y[4], y[5], y[6], y[7]});
       if ((l & 15) == 0) oj[row] = a.scale * fmaf(alpha, sq, d * kq);
     }
     // Slot j % 4 is rewritten at head j + 4, after three more barriers that wave j % 4 reaches
