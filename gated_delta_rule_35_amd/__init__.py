@@ -12,7 +12,7 @@ discosf article "Agnes 3.0 Flash 刚上线就刷屏…", section 二.1):
   prefill_fused   conv + SiLU + L2 and the chunked prefill in one call, from the raw q|k|v projection
   decode_step     stepwise gated delta rule, state updated in place
   gated_rmsnorm   y = rmsnorm(o) * w * silu(z)
-  decode_fused    one decode token through conv, recurrence and norm in one launch
+  decode_fused    one decode token through conv, recurrence and norm in one call
 The global attention layer of the same model (model card, rows 全局注意力 and 位置编码):
   attn_prefill    q/k RMS-norm + partial three-axis rotary, causal GQA softmax attention, sigmoid gate
   attn_decode     one token per entry against a bf16 KV cache (the new k, v written at index len)

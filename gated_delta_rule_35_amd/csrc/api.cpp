@@ -277,8 +277,7 @@ AGNES_API int agnes_gdn_decode_fused(const void* x, int64_t x_token_stride, agne
                                      agnes_dtype o_dtype, void* stream) {
   if (!valid_dtype(dtype) || !valid_dtype(o_dtype)) return AGNES_ERR_INVALID_ARG;
   if (batch < 0 || num_slots < 0 || num_k_heads <= 0 || num_v_heads <= 0) return AGNES_ERR_INVALID_ARG;
-  if (head_dim != kHeadDim || num_v_heads % num_k_heads || num_v_heads / num_k_heads > 120)
-    return AGNES_ERR_UNSUPPORTED;
+  if (head_dim != kHeadDim || num_v_heads % num_k_heads) return AGNES_ERR_UNSUPPORTED;
   if (!std::isfinite(scale) || !(l2norm_eps >= 0.f) || !std::isfinite(l2norm_eps) || !(norm_eps >= 0.f) ||
       !std::isfinite(norm_eps))
     return AGNES_ERR_INVALID_ARG;
@@ -312,7 +311,7 @@ AGNES_API int agnes_gdn_decode_fused(const void* x, int64_t x_token_stride, agne
     for (const Span& in : ins)
       if (overlap(outs[i], in)) return AGNES_ERR_INVALID_ARG;
   }
-  if (!agnes::decode_fused_fits(batch, num_k_heads)) return AGNES_ERR_UNSUPPORTED;
+  if (!agnes::decode_fused_fits(batch, num_v_heads)) return AGNES_ERR_UNSUPPORTED;
 
   agnes::FusedDecodeArgs a{x, x_token_stride, (int)dtype, conv_weight, conv_bias, conv_state, g, beta, z,
                            norm_weight, state, slots, num_slots, batch, num_k_heads, num_v_heads, scale,

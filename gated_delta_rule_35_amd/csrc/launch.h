@@ -180,7 +180,7 @@ inline bool grid_fits(unsigned __int128 blocks, unsigned threads) { return block
 bool prefill_mfma_fits(int num_seqs, int64_t total, int hk, int hv);
 bool prefill_f32_fits(int num_seqs, int hv);
 bool decode_fits(int batch, int hv);
-bool decode_fused_fits(int batch, int hk);
+bool decode_fused_fits(int batch, int hv);
 bool norm_fits(int64_t rows);
 bool attn_prefill_fits(int num_seqs, int64_t total, int hq, int hkv);
 bool attn_decode_fits(int batch, int hq, int hkv, int64_t max_len);

@@ -41,8 +41,8 @@
  *     that one of its launches would exceed the device's grid (a launch counts
  *     its work-items in 32 bits).  In round numbers: a prefill of 2^21 or more
  *     (sequence, value head) pairs or of more than about 2^28.4 / Hk tokens (22M
- *     at Hk = 16); from 2^24 (entry, value head) pairs of a decode step, 2^24
- *     (entry, key head) pairs of a fused decode step, 2^31 rows of a gated
+ *     at Hk = 16); from 2^24 (entry, value head) pairs of a decode step or a
+ *     fused decode step, 2^31 rows of a gated
  *     RMS-norm or 2^26 / Hkv tokens of an attention prefill on.
  *   - Sizes: a call takes at most INT32_MAX tokens (cu_seqlens are int32); more
  *     is AGNES_ERR_INVALID_ARG.  A buffer whose extent, from its size and
@@ -235,7 +235,7 @@ int agnes_gdn_gated_rmsnorm(const void* o, agnes_dtype o_dtype, const void* z,
 
 /*
  * agnes_gdn_decode_fused — one decode token per batch entry through the whole
- * delta layer in a single launch (discosf article, section 二.1: stepwise
+ * delta layer in two launches (discosf article, section 二.1: stepwise
  * decode; model card 架构 table, delta-rule row: kernel-4 causal conv in front,
  * gated RMS-norm behind, fp32 state).  For each entry b with slot s:
  *
@@ -266,7 +266,7 @@ int agnes_gdn_gated_rmsnorm(const void* o, agnes_dtype o_dtype, const void* z,
  *   y            [batch, Hv, head_dim] contiguous, `o_dtype`
  *   o            [batch, Hv, head_dim] contiguous, `o_dtype`, or NULL: the
  *                recurrence output before the norm
- * Supported: head_dim 128, Hv a multiple of Hk with Hv / Hk <= 120.
+ * Supported: head_dim 128, Hv a multiple of Hk.
  * Slots exist for a serving pool in which a sequence keeps its caches at a
  * fixed slot while the batch composition changes from step to step.
  */

@@ -251,7 +251,6 @@ void dfused_cases() {
   EXPECT(dfused(WITH(DFused, (a.B = 0, a.x = nullptr, a.y = nullptr))), OK);
   EXPECT(dfused(WITH(DFused, a.hd = 64)), UNS);
   EXPECT(dfused(WITH(DFused, a.hv = 7)), UNS);
-  EXPECT(dfused(WITH(DFused, (a.hk = 1, a.hv = 121, a.xs = 123 * 128))), UNS);
   EXPECT(dfused(WITH(DFused, a.x = nullptr)), INV);
   EXPECT(dfused(WITH(DFused, a.cs = nullptr)), INV);
   EXPECT(dfused(WITH(DFused, a.S = 3)), INV);

@@ -164,7 +164,6 @@ def test_decode_fused_checks(lib):
     assert fused(lib, B=0, x=None, y=None) == 0         # empty batch: nothing to do
     assert fused(lib, hd=64) == UNS
     assert fused(lib, hv=7) == UNS                      # Hv % Hk
-    assert fused(lib, hk=1, hv=121, xs=123 * 128) == UNS  # more than 120 value heads per key head
     assert fused(lib, x=None) == INV
     assert fused(lib, cs=None) == INV
     assert fused(lib, S=3) == INV                       # no slot array: a slot per entry needed
