@@ -1,5 +1,5 @@
 """GPU parity of agnes_gdn_decode_fused (conv + SiLU + L2(q, k) + recurrence + gated norm in one
-launch) against the fp64 layer oracle on identical input bytes.
+call) against the fp64 layer oracle on identical input bytes.
 
 Tolerances: every step runs in fp32 with nothing rounded in between, so the fp32 `y`, `o` and
 states are gated at rel-L2 1e-5 (as the unfused decode step); the bf16 `y` of the same call must
@@ -81,10 +81,12 @@ def test_decode_fused_steps_with_slots_and_padding(dtype):
         np.testing.assert_array_equal(host(st)[[1, 3, 5, 6, 8]], d["st"][[1, 3, 5, 6, 8]])
 
 
-@pytest.mark.parametrize("hk,hv,bias", [(1, 1, False), (2, 4, True), (1, 5, False), (3, 3, True), (1, 7, False)])
+@pytest.mark.parametrize("hk,hv,bias", [(1, 1, False), (2, 4, True), (1, 5, False), (3, 3, True), (1, 7, False),
+                                        (1, 130, True)])
 def test_decode_fused_group_sizes(hk, hv, bias):
-    """Value heads per key head 1, 2, 5 and 7 (more than one round of head groups per
-    workgroup), with and without conv bias; slots = None (entry b uses slot b)."""
+    """Value heads per key head 1, 2, 5, 7 and 130 (each of them convolving the key head's q and
+    k from the old history, which the second launch then advances), with and without conv bias;
+    slots = None (entry b uses slot b)."""
     rng = np.random.default_rng(310 + 10 * hk + hv)
     B = 4
     d = _case(rng, B, hk, hv, B, "bf16", bias)
