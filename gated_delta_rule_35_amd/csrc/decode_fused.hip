@@ -11,9 +11,10 @@
 // convolves the q and k heads of its key head and its own value head (48 items of 8 channels,
 // wave 0), issues the streaming loads of its 64 KiB state, runs the state update (a row over 16
 // lanes, one read and one write of the state), and wave 0 applies the gated norm.  The conv goes
-// first so that its raw inputs and the state are never live together: 108 registers, four
-// workgroups per CU (state loads first: 147 registers and three workgroups per CU, 2 % slower;
-// the same capped at 112 registers, 1.5 % slower).
+// first and the norm's operands are loaded only for the norm, so that the state never shares the
+// registers with other inputs: 104 registers, four workgroups per CU (state loads first: 147
+// registers and three workgroups per CU, 2 % slower; the norm's z and weight loaded beside the
+// state: 108 registers and 8 % slower).
 // Each of the G = Hv / Hk workgroups of a key head convolves that key head's q and k channels
 // from the old conv history, so that history is advanced only after all of them are done, by a
 // second, small launch; a workgroup advances the history of its own value head's channels
@@ -114,15 +115,6 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(FusedDecodeArgs a) {
     s[p][0] = load_f4_stream(S + row * 128 + c);
     s[p][1] = load_f4_stream(S + row * 128 + 64 + c);
   }
-  // the norm's operands (wave 0, two values a lane)
-  float zn[2] = {0.f, 0.f}, wn[2] = {0.f, 0.f};
-  if (w == 0) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      zn[i] = load1<DT>(a.z, bh * 128 + 2 * l + i);
-      wn[i] = load1<DT>(a.norm_w, 2 * l + i);
-    }
-  }
   const float alpha = __expf(a.g[bh]);
   const float beta = a.beta[bh];
   __syncthreads();
@@ -163,6 +155,12 @@ __global__ __launch_bounds__(256) void decode_fused_kernel(FusedDecodeArgs a) {
   __syncthreads();
   if (w == 0) {  // gated RMS-norm of the head, two values a lane
     const int64_t rb = bh * 128;
+    float zn[2], wn[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      zn[i] = load1<DT>(a.z, bh * 128 + 2 * l + i);
+      wn[i] = load1<DT>(a.norm_w, 2 * l + i);
+    }
     const float o0 = o_s[2 * l], o1 = o_s[2 * l + 1];
     float ss = fmaf(o0, o0, o1 * o1);
     ss = sum16_dpp(ss);
