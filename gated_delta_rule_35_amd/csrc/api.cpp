@@ -518,6 +518,7 @@ int layer_prefill_checked(const void* x, int64_t x_token_stride, int dtype, cons
   a.norm_w = norm_weight;
   a.norm_eps = norm_eps;
   a.y = y;
+  a.layer = true;
   a.single_stage = single_stage;
   return hip_status(agnes::launch_layer_prefill(a, static_cast<hipStream_t>(stream)));
 }

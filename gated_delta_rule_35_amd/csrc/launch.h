@@ -66,6 +66,9 @@ struct PrefillArgs {
   int stage = 0;          // whole-layer call: this stage's workgroup ticket counter
   unsigned wait_limit = 0;  // bounded waits poll at most this often (0: each wait's own bound)
   bool single_stage = false;  // run in one stage: no side stream, nothing created on first use
+  // The whole-layer call (set even where y is null, as it may be for an empty batch): its first
+  // prep clears the exchange words and the workgroup role counters.
+  bool layer = false;
 };
 
 // Process-wide poll bound handed to every bf16 prefill launch (agnes_gdn_set_wait_limit).

@@ -332,7 +332,7 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
   const int rd = (int)(lid % rounds);
   const int j = (int)((lid / rounds) % (unsigned)maxch);
   const int kh = (int)(lid / (rounds * (unsigned)maxch));
-  if (a.y && a.part_lo == 0) {  // whole-layer call, first stage: no partial sum published yet
+  if (a.layer && a.part_lo == 0) {  // whole-layer call, first stage: no partial sum published yet
     // (tag 0 matches no chunk), no ticket taken
     uint4* r = reinterpret_cast<uint4*>(base + ws.ring);
     const size_t n16 = (ws.layer_bytes - ws.ring) / 16;
@@ -1438,6 +1438,10 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
       } else {
         role = __hip_atomic_fetch_add(&cnt[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // plain start order
       }
+      if (claimed && role >= nblk) {  // (never when the counters were cleared for this call)
+        ws_report(a.workspace, wsbits::WAIT_ROLE);
+        claimed = false;
+      }
       sm.ticket = claimed ? role : ~0u;
     }
     __syncthreads();
@@ -1650,7 +1654,7 @@ static hipError_t launch_prep(const PrefillArgs& a, int64_t maxch, hipStream_t s
   } else {
     // (the whole-layer call's first prep also clears the exchange words and role counters, so it
     // runs even when every sequence is empty)
-    if (a.total == 0 && !(a.y && a.part_lo == 0)) return hipSuccess;
+    if (a.total == 0 && !(a.layer && a.part_lo == 0)) return hipSuccess;
     hipLaunchKernelGGL((prep_kernel<FUSED>), grid, block, 0, st, a, maxch);
   }
   return hipGetLastError();

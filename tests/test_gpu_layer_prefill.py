@@ -207,12 +207,14 @@ def test_layer_prefill_repeated_calls_reuse_the_workspace():
 
 
 def test_layer_prefill_all_sequences_empty_after_a_full_call():
-    """A batch of empty sequences right after a call that left its role counters and exchange
-    words in the same workspace: nothing is written to y, the final states are the initial
-    ones, and the conv history is unchanged."""
+    """A batch of empty sequences (y may then be null) right after a call that left its role
+    counters and exchange words in the same workspace, the rest of which holds all-ones bytes:
+    the empty call still clears its own counters, nothing is written to y, the final states are
+    the initial ones, the conv history is unchanged and no error bit is set."""
     rng = np.random.default_rng(660)
     d1 = _case(rng, [150, 40], 2, 6)
     ws = torch.empty(gdn.layer_prefill_workspace_size(3, 190, 2, 6), dtype=torch.uint8, device="cuda")
+    ws.fill_(255)  # every word the empty call would find uncleared reads as a huge counter
     gdn.layer_prefill(dev(d1["x"]), dev(d1["w"]), dev(d1["g"]), dev(d1["beta"]), dev(d1["cu"]), dev(d1["z"]),
                       dev(d1["nw"]), num_k_heads=2, conv_state=dev(d1["cs"]), initial_state=dev(d1["s0"]),
                       out_dtype=torch.float32, workspace=ws)
@@ -223,6 +225,7 @@ def test_layer_prefill_all_sequences_empty_after_a_full_call():
                                 dev(d0["z"]), dev(d0["nw"]), num_k_heads=2, conv_state=cs,
                                 initial_state=dev(d0["s0"]), y=y, workspace=ws)
     torch.cuda.synchronize()
+    assert gdn.workspace_status(ws) == 0
     assert y0.shape == (0, 6, D)
     np.testing.assert_array_equal(host(fin), d0["s0"])
     np.testing.assert_array_equal(host(cs), d0["cs"])
