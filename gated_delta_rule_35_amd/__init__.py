@@ -522,10 +522,14 @@ def set_wait_limit(polls):
 
 
 
-def set_prefill_stages(cuts=(26,)):
+def set_prefill_stages(cuts=None):
     """Process-wide stage cuts of the bf16 prefill calls, in 1/40ths of each sequence's chunks
-    (strictly increasing inside (0, 40), at most 7; () runs every call in one stage).  The
-    default (26,) runs two stages.  The cuts change the schedule only, not the results."""
+    (strictly increasing inside (0, 40), at most 7; () runs every call in one stage), for every
+    kind of call.  None restores the defaults: two stages, cut at 26 for the whole-layer calls
+    and at 28 for the prefill calls.  The cuts change the schedule only, not the results."""
+    if cuts is None:
+        _check("agnes_gdn_set_prefill_stages", _lib.load().agnes_gdn_set_prefill_stages(None, -1))
+        return
     arr = (ctypes.c_int32 * max(len(cuts), 1))(*[int(c) for c in cuts])
     _check("agnes_gdn_set_prefill_stages", _lib.load().agnes_gdn_set_prefill_stages(arr, len(cuts)))
 

@@ -20,10 +20,9 @@
 //  2. prep (all chunks in parallel, one workgroup per chunk and key group, four waves per
 //     value head of the group): the Gram matrices K K^T and Q K^T on matrix cores, then per
 //     value head in fp32 the decay-scaled P, A and X (the blocks of X off the diagonal on
-//     fp32 matrix cores), written as
-//     one 19 KiB record per (chunk, value head), and the fp16 image of the chunk's q and k
-//     rows, 34 KiB per (chunk, key group).  Everything in
-//     them depends only on the inputs, not on the state.
+//     fp32 matrix cores), written as one 13 KiB record per (chunk, value head), and the fp16
+//     image of the chunk's q and k rows, 33 KiB per (chunk, key group).  Everything in them
+//     depends only on the inputs, not on the state.
 //  3. scan (serial over chunks): one workgroup of 8 waves per (sequence, value head, block of
 //     32 value rows); the value rows of S are independent, so each workgroup scans its own
 //     [32 x 128] fp32 slice of the state.  The chain wave keeps that slice of S^T in matrix-core
@@ -61,7 +60,6 @@ namespace mp {
 constexpr int C = 64;        // chunk
 constexpr int D = 128;       // head dim (key and value)
 constexpr int LDQ = D + 8;   // fp16 row stride of staged Q/K rows
-constexpr int LDT = C + 8;   // fp16 row stride of [*, chunk] tiles
 constexpr int NVT = 2;       // 16-wide value tiles per scan workgroup
 // Value tiles per chain wave and per output wave.  One tile per wave (two chain and two output
 // waves) shortens each wave's serial work, but every wave then streams the whole K, Q, X and P
@@ -80,20 +78,43 @@ constexpr int VR_ROWS = 80;  // raw x rows of a V slice (fused): 3 halo + 64, to
 }  // namespace mp
 
 // Per (chunk, value head) record written by prep and copied verbatim into LDS by scan, so it
-// is laid out as the padded LDS image the consumers read (rows padded against bank conflicts).
+// is laid out as the LDS image the consumers read.  P and X are stored as the six 16x32
+// A-operand fragments the scan multiplies by: row block f, columns 0..31 (f = 0..3), and row
+// blocks 2, 3, columns 32..63 (f = 4, 5).  Lane 16g + m of fragment f holds row 16 rb(f) + m,
+// columns k0 + 4g .. + 3 and k0 + 16 + 4g .. + 3 (the order of a_perm), so a lane reads its
+// operand with one 16-byte LDS read.  The blocks above the diagonal inside the fragments, (0,1)
+// and (2,3), hold zeros; the other blocks above the diagonal are not stored.
 struct RecImage {
-  _Float16 P[mp::C][mp::LDT];      // P, row-major, zero above the diagonal
-  _Float16 X[mp::C][mp::LDT];      // X = (I + A)^-1, row-major, zero above the diagonal
+  h8 P[6][64];                     // P = lower_incl(exp(gamma_r - gamma_s) q_r.k_s)
+  h8 X[6][64];                     // X = (I + A)^-1
   float gt[3][mp::C];              // beta, exp(gamma), exp(gamma_63 - gamma)
   float pad[64];                   // to a whole number of 1 KiB copy steps
 };
-static_assert(sizeof(RecImage) == 19 * 1024, "record image is copied in 1 KiB steps");
-// Per (chunk, key group) image of the fp16 q and k rows (rows past the chunk end are zero).
+static_assert(sizeof(RecImage) == 13 * 1024, "record image is copied in 1 KiB steps");
+// Byte offset in a fragment-packed P or X of the four values (r, s .. s + 3), s a multiple of 4
+// and (r, s) inside a stored fragment.
+__host__ __device__ constexpr int frag_off(int r, int s) {
+  return ((((r >> 4) + 2 * (s >> 5)) * 64 + 16 * ((s & 15) >> 2) + (r & 15)) * 8 + 4 * ((s & 31) >> 4)) * 2;
+}
+static_assert(frag_off(0, 0) == 0 && frag_off(0, 16) == 8 && frag_off(1, 4) == 16 * 17 &&
+                  frag_off(32, 32) == 4 * 64 * 16 && frag_off(63, 60) == (5 * 64 + 63) * 16 + 8,
+              "fragment packing");
+// Per (chunk, key group) image of the fp16 q and k rows (rows past the chunk end are zero).  Q
+// is read only as the A operand of Q S^T, so it is stored as those sixteen 16x32 fragments
+// (fragment 4 ks + rt: rows 16 rt .. + 15, columns 32 ks .. + 31, lanes as for P and X); K is
+// also read transposed, so it stays row-major (rows padded against bank conflicts).
 struct QKImage {
-  _Float16 Q[mp::C][mp::LDQ];
+  h8 Q[16][64];
   _Float16 K[mp::C][mp::LDQ];
 };
-static_assert(sizeof(QKImage) == 34 * 1024, "q/k image is copied in 1 KiB steps");
+static_assert(sizeof(QKImage) == 33 * 1024, "q/k image is copied in 1 KiB steps");
+// Byte offset in the fragment-packed Q of the four values (r, s .. s + 3), s a multiple of 4.
+__host__ __device__ constexpr int qfrag_off(int r, int s) {
+  return ((((s >> 5) * 4 + (r >> 4)) * 64 + 16 * ((s & 15) >> 2) + (r & 15)) * 8 + 4 * ((s & 31) >> 4)) * 2;
+}
+static_assert(qfrag_off(0, 0) == 0 && qfrag_off(16, 0) == 64 * 16 && qfrag_off(0, 32) == 4 * 64 * 16 &&
+                  qfrag_off(63, 124) == (15 * 64 + 63) * 16 + 8,
+              "fragment packing");
 namespace mp {
 constexpr int REC_BYTES = sizeof(RecImage);
 constexpr int QK_BYTES = sizeof(QKImage);
@@ -471,7 +492,15 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
 #pragma unroll
       for (int e = 0; e < 8; ++e) hv[e] = r < L ? (_Float16)(y[e] * rs) : (_Float16)0.f;
       *reinterpret_cast<h8*>(hs ? &sm.u.qk.K[r][8 * col] : &sm.u.qk.Q[r][8 * col]) = hv;
-      if (rd == 0) *reinterpret_cast<h8*>(hs ? &img->K[r][8 * col] : &img->Q[r][8 * col]) = hv;
+      if (rd == 0) {
+        if (hs) {
+          *reinterpret_cast<h8*>(&img->K[r][8 * col]) = hv;
+        } else {
+          unsigned char* qb = reinterpret_cast<unsigned char*>(img->Q);
+          *reinterpret_cast<h4*>(qb + qfrag_off(r, 8 * col)) = h4{hv[0], hv[1], hv[2], hv[3]};
+          *reinterpret_cast<h4*>(qb + qfrag_off(r, 8 * col + 4)) = h4{hv[4], hv[5], hv[6], hv[7]};
+        }
+      }
     }
     lds_barrier();
   }
@@ -515,7 +544,14 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
 #pragma unroll
         for (int e = 0; e < 4; ++e) bad |= (wv[e] & 0x7fffu) >= 0x4780u || ((wv[e] >> 16) & 0x7fffu) >= 0x4780u;
       }
-      *reinterpret_cast<h8*>(isk ? &img->K[r][col] : &img->Q[r][col]) = cvt8(r < L ? u : make_uint4(0, 0, 0, 0));
+      const h8 hv = cvt8(r < L ? u : make_uint4(0, 0, 0, 0));
+      if (isk) {
+        *reinterpret_cast<h8*>(&img->K[r][col]) = hv;
+      } else {
+        unsigned char* qb = reinterpret_cast<unsigned char*>(img->Q);
+        *reinterpret_cast<h4*>(qb + qfrag_off(r, col)) = h4{hv[0], hv[1], hv[2], hv[3]};
+        *reinterpret_cast<h4*>(qb + qfrag_off(r, col + 4)) = h4{hv[4], hv[5], hv[6], hv[7]};
+      }
     }
   }
   lds_barrier();  // q/k rows are dead from here
@@ -546,15 +582,16 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
         bad |= !fp16_range(pv);
         pv4[e] = (_Float16)pv;
       }
-      *reinterpret_cast<h4*>(rz + offsetof(RecImage, P) + (pr * LDT + ps) * 2) = pv4;
+      *reinterpret_cast<h4*>(rz + offsetof(RecImage, P) + frag_off(pr, ps)) = pv4;
     }
   } else {
-    for (int i = tid - 640; i < PH * 2 * 16 * 2; i += 128) {  // (head, block, row, half row)
-      const int zz = i >> 6, blk = (i >> 5) & 1, r = 32 * blk + ((i >> 1) & 15), c = 16 + 32 * blk + 8 * (i & 1);
+    for (int i = tid - 640; i < PH * 2 * 64; i += 128) {  // (head, block, lane): the lane's upper half
+      const int zz = i >> 7, blk = (i >> 6) & 1, l = i & 63;
       if (rd * PH + zz < grp) {
         const int hz = kh * grp + rd * PH + zz;
         unsigned char* rz = base + ws.rec + ((size_t)hz * maxch + j) * REC_BYTES;
-        *reinterpret_cast<uint4*>(rz + offsetof(RecImage, P) + (r * LDT + c) * 2) = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint2*>(rz + offsetof(RecImage, P) + frag_off(32 * blk + (l & 15), 16 + 32 * blk + 4 * (l >> 4))) =
+            make_uint2(0, 0);
       }
     }
   }
@@ -599,20 +636,23 @@ __global__ __launch_bounds__(256 * mp::PH) __attribute__((amdgpu_waves_per_eu(6)
     for (int e = 0; e < 4; ++e) hd.X[tri(3, 0)][4 * lg + e][ln] = x[e];
   }
   lds_barrier();
-  // X -> record (fp16 rows, zero above the diagonal)
+  // X -> record (fp16 fragments, zero above the diagonal): item t is lane t % 64 of fragment t / 64
   if (act) {
-    for (int t = ts; t < C * C / 8; t += 256) {
-      const int r = t >> 3, s0 = 8 * (t & 7);
-      const int bi = r >> 4, bj = s0 >> 4;
-      const float* xr = &hd.X[bj <= bi ? tri(bi, bj) : 0][r & 15][s0 & 15];
+    for (int t = ts; t < 6 * 64; t += 256) {
+      const int f = t >> 6, g = (t >> 4) & 3, bi = f < 4 ? f : f - 2, r = 16 * bi + (t & 15);
       h8 xv;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float xe = s0 + e <= r ? xr[e] : 0.f;
-        bad |= !fp16_range(xe);
-        xv[e] = (_Float16)xe;
+      for (int hh = 0; hh < 2; ++hh) {
+        const int s0 = (f < 4 ? 0 : 32) + 16 * hh + 4 * g, bj = s0 >> 4;
+        const float* xr = &hd.X[bj <= bi ? tri(bi, bj) : 0][r & 15][s0 & 15];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float xe = s0 + e <= r ? xr[e] : 0.f;
+          bad |= !fp16_range(xe);
+          xv[4 * hh + e] = (_Float16)xe;
+        }
       }
-      *reinterpret_cast<h8*>(rec + offsetof(RecImage, X) + (r * LDT + s0) * 2) = xv;
+      *reinterpret_cast<h8*>(rec + offsetof(RecImage, X) + 16 * t) = xv;
     }
   }
   if (__any(bad) && lane == 0) ws_report(a.workspace, wsbits::RANGE);
@@ -745,9 +785,7 @@ __device__ __forceinline__ void chain_step(const ScanBuf& B, ExBuf& exU, ExBuf& 
     }
     if (ks == 2) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xa[i] = a_perm(&R.X[16 * i + ln][0], 0, lg);
-      xa[4] = a_perm(&R.X[32 + ln][0], 32, lg);
-      xa[5] = a_perm(&R.X[48 + ln][0], 32, lg);
+      for (int i = 0; i < 6; ++i) xa[i] = R.X[i][lane];
     }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
@@ -861,7 +899,7 @@ __device__ __forceinline__ void qs_step(const ScanBuf& B, const ExBuf& exS, int 
     for (int ks = 0; ks < 4; ++ks) sb[t][ks] = exS.s[t0 + t][ks][lane];
   h8 qa[2][4];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) qa[0][rt] = a_perm(&B.QK.Q[16 * rt + ln][0], 0, lg);
+  for (int rt = 0; rt < 4; ++rt) qa[0][rt] = B.QK.Q[rt][lane];
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
 #pragma unroll
@@ -871,12 +909,10 @@ __device__ __forceinline__ void qs_step(const ScanBuf& B, const ExBuf& exS, int 
   for (int ks = 0; ks < 4; ++ks) {
     if (ks < 3) {
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) qa[(ks + 1) & 1][rt] = a_perm(&B.QK.Q[16 * rt + ln][0], 32 * (ks + 1), lg);
+      for (int rt = 0; rt < 4; ++rt) qa[(ks + 1) & 1][rt] = B.QK.Q[4 * (ks + 1) + rt][lane];
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pa[i] = a_perm(&B.R.P[16 * i + ln][0], 0, lg);
-      pa[4] = a_perm(&B.R.P[32 + ln][0], 32, lg);
-      pa[5] = a_perm(&B.R.P[48 + ln][0], 32, lg);
+      for (int i = 0; i < 6; ++i) pa[i] = B.R.P[i][lane];
       gate_rows16(B.R.gt[1], lg, ge);
     }
 #pragma unroll
@@ -1207,7 +1243,7 @@ __device__ __forceinline__ void tile_wave(ScanSmem& sm, const PrefillArgs& a, co
 
 // Copy waves: issue the direct global -> LDS loads (no registers) of chunk c into buffer
 // B[c & 1] (c < 0: none) and, for the fused prologue, of the raw x rows of chunk cv's V slice
-// into Vr[cv & 1] (cv < 0: none).  A chunk is 58 copies of 1 KiB (q/k image 34, record 19, V
+// into Vr[cv & 1] (cv < 0: none).  A chunk is 51 copies of 1 KiB (q/k image 33, record 13, V
 // slice 5) landing back to back in the buffer; copy wave q of NCOPY issues the copies u = q,
 // q + NCOPY, ...  The q/k image and the record are contiguous; the V slice is gathered from
 // the strided tensor into padded rows, rows past the end of the chunk re-reading its first
@@ -1693,17 +1729,21 @@ static hipError_t launch_o(const PrefillArgs& a, hipStream_t st) {
 // a short time before it.  So the call runs as prep(first part of every sequence) -> scan(first
 // part) on the caller's stream, with prep(next part) on a side stream beside that scan (on the
 // compute units the scan leaves free), then scan(next part) carrying the state over.  Prep beside
-// a scan runs ~3x slower than alone, so the first part is the larger: 13/20 of the chunks.  More
+// a scan runs ~3x slower than alone, so the first part is the larger: 13/20 of the chunks for the
+// whole-layer call, 7/10 for the prefill calls (their scan is faster without the norm).  More
 // stages shorten the exposed first prep but cost more at each hand-over than they save (at
 // T = 8192: two stages 356 us, three 373-380 us, four 398 us).  Used when the scan leaves a
 // quarter of the chip free and sequences are long enough.  The cuts are a process-wide setting
-// (agnes_gdn_set_prefill_stages), read under the side-queue lock at each launch.
+// (agnes_gdn_set_prefill_stages, for every kind of call once set), read under the side-queue
+// lock at each launch.
 constexpr int SPLIT_DEN = 40;    // stage boundaries in 1/40 of each sequence's chunks
 constexpr int MAX_STAGES = 8;    // the workspace holds role counters for 8 stages
 struct StageCuts {
   int n = 1;                     // number of cuts: the call runs in n + 1 stages
   int cut[MAX_STAGES - 1] = {26};  // stage k covers [cut[k-1], cut[k]) of SPLIT_DEN
+  bool custom = false;           // set by the caller (else each kind of call takes its default)
 };
+constexpr int LAYER_CUT = 26, PREFILL_CUT = 28;  // defaults (measured at T = 8192)
 
 namespace {
 struct SideQueue {
@@ -1754,13 +1794,16 @@ hipError_t release_side_queues() {
 }
 
 // Sets the stage cuts of the later calls: n cuts strictly increasing inside (0, SPLIT_DEN),
-// n < MAX_STAGES (n = 0: one stage).  False, and nothing changed, for any other list.
+// n < MAX_STAGES (n = 0: one stage), or n = -1: back to each kind of call's default.  False, and
+// nothing changed, for any other list.
 bool set_stage_cuts(const int* cuts, int n) {
-  if (n < 0 || n >= MAX_STAGES || (n > 0 && !cuts)) return false;
+  if (n < -1 || n >= MAX_STAGES || (n > 0 && !cuts)) return false;
   for (int i = 0; i < n; ++i)
     if (cuts[i] <= (i ? cuts[i - 1] : 0) || cuts[i] >= SPLIT_DEN) return false;
   std::lock_guard<std::mutex> lock(g_side_mu);
   g_cuts = StageCuts{};
+  if (n < 0) return true;
+  g_cuts.custom = true;
   g_cuts.n = n;
   for (int i = 0; i < n; ++i) g_cuts.cut[i] = cuts[i];
   return true;
@@ -1771,7 +1814,8 @@ static hipError_t launch_staged(const PrefillArgs& a, hipStream_t st) {
   if (a.num_seqs == 0) return hipSuccess;
   if (a.single_stage) return launch_o<O_DT, FUSED, NORM>(a, st);
   std::lock_guard<std::mutex> lock(g_side_mu);
-  const StageCuts cuts = g_cuts;
+  StageCuts cuts = g_cuts;
+  if (!cuts.custom) cuts.cut[0] = NORM ? LAYER_CUT : PREFILL_CUT;
   if (cuts.n == 0) return launch_o<O_DT, FUSED, NORM>(a, st);
   SideQueue* q = nullptr;
   hipError_t e = side_queue(q);

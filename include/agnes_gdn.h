@@ -497,10 +497,11 @@ int agnes_gdn_set_wait_limit(uint32_t polls);
  * 40), the preparation of stage k + 1 overlapping the scan of stage k on a side stream and the
  * state carried between stages in the workspace.  The stages change the schedule only: the
  * results are the same bit for bit.  `cuts` (host, n_cuts values) must increase strictly inside
- * (0, 40), 0 <= n_cuts <= 7; n_cuts = 0 runs every call in one stage.  The default is one cut at
- * 26 (two stages, the first 13/20 of the chunks).  Not meant to change while calls are being
- * launched from other threads.  Returns AGNES_OK, or AGNES_ERR_INVALID_ARG (nothing changed)
- * for any other list.
+ * (0, 40), 0 <= n_cuts <= 7; n_cuts = 0 runs every call in one stage; once set, the cuts apply
+ * to every kind of call.  n_cuts = -1 (`cuts` not read) restores the defaults: one cut at 26 for
+ * the whole-layer calls (two stages, the first 13/20 of the chunks) and at 28 for the two prefill
+ * calls (7/10).  Not meant to change while calls are being launched from other threads.  Returns
+ * AGNES_OK, or AGNES_ERR_INVALID_ARG (nothing changed) for any other list.
  */
 int agnes_gdn_set_prefill_stages(const int32_t* cuts, int n_cuts);
 

@@ -447,13 +447,15 @@ void misc_cases() {
   const int nbad[] = {1, 1, 2, 2, 1, 8, 1};
   for (int i = 0; i < 7; ++i) EXPECT(agnes_gdn_set_prefill_stages(bad[i], nbad[i]), INV);
   EXPECT(agnes_gdn_set_prefill_stages(nullptr, 1), INV);
-  EXPECT(agnes_gdn_set_prefill_stages(nullptr, -1), INV);
+  EXPECT(agnes_gdn_set_prefill_stages(nullptr, -2), INV);
+  EXPECT(agnes_gdn_set_prefill_stages(nullptr, -IMAX - 1), INV);
   EXPECT(agnes_gdn_set_prefill_stages(nullptr, IMAX), INV);
   EXPECT(agnes_gdn_set_prefill_stages(nullptr, 0), OK);
   const int32_t seven[] = {1, 2, 3, 4, 5, 6, 39};
   EXPECT(agnes_gdn_set_prefill_stages(seven, 7), OK);
   const int32_t dflt[] = {26};
   EXPECT(agnes_gdn_set_prefill_stages(dflt, 1), OK);
+  EXPECT(agnes_gdn_set_prefill_stages(nullptr, -1), OK);  // the defaults again
   EXPECT(agnes_gdn_last_hip_error(), 0);
   EXPECT(agnes_gdn_release(), OK);  // nothing was created: no device call
 }

@@ -346,10 +346,11 @@ def test_stage_cuts_are_checked_on_the_host(lib):
     for bad in [(0,), (40,), (24, 24), (30, 20), (-1,), tuple(range(1, 9))]:
         assert lib.agnes_gdn_set_prefill_stages(*cuts(*bad)) == INV, bad
     assert lib.agnes_gdn_set_prefill_stages(None, 1) == INV
-    assert lib.agnes_gdn_set_prefill_stages(None, -1) == INV
+    assert lib.agnes_gdn_set_prefill_stages(None, -2) == INV
     assert lib.agnes_gdn_set_prefill_stages(None, 0) == 0
     assert lib.agnes_gdn_set_prefill_stages(*cuts(1, 2, 3, 4, 5, 6, 39)) == 0
-    assert lib.agnes_gdn_set_prefill_stages(*cuts(26)) == 0  # the default again
+    assert lib.agnes_gdn_set_prefill_stages(*cuts(26)) == 0
+    assert lib.agnes_gdn_set_prefill_stages(None, -1) == 0  # the defaults again
     assert lib.agnes_gdn_last_hip_error() == 0
 
 def test_noalloc_refuses_a_workspace_beyond_its_own_on_the_host(lib):
