@@ -61,14 +61,15 @@ constexpr int C = 64;        // chunk
 constexpr int D = 128;       // head dim (key and value)
 constexpr int LDQ = D + 8;   // fp16 row stride of staged Q/K rows
 constexpr int NVT = 2;       // 16-wide value tiles per scan workgroup
-// Value tiles per chain wave and per output wave.  One tile per wave (two chain and two output
-// waves) shortens each wave's serial work, but every wave then streams the whole K, Q, X and P
-// tiles from LDS for half the columns; at two tiles per wave the chunk period is the same or
-// shorter.
-constexpr int TPW = 2;
-constexpr int NPAIR = NVT / TPW;  // chain waves (and as many output waves) per scan workgroup
+// Value tiles per chain wave and per output wave (measured at T = 8192).  One tile per wave
+// (two chain and two output waves, one SIMD each) halves each wave's serial work, but every wave
+// then streams the whole K, Q, X and P tiles from LDS for half the products: the prefill calls
+// run 5 % faster so, the whole-layer call, whose two tile waves share the workgroup, 5-8 % slower.
+constexpr int tpw(bool norm) { return norm ? 2 : 1; }
+constexpr int npair(bool norm) { return NVT / tpw(norm); }  // chain waves (and as many output waves)
 constexpr int NCP = 6;       // copy waves
-constexpr int NWAVES = 2 * NPAIR + NCP;  // chain waves, output waves, copy waves
+constexpr int nwaves(bool norm) { return 2 * npair(norm) + NCP; }  // chain, output, copy waves
+constexpr int MAX_WAVES = 2 * NVT + NCP;
 constexpr int DVB = 16 * NVT;
 constexpr int RING = 8;      // whole-layer call: chunk slots of the partial-sum exchange
 static_assert(RING >= 4 && (RING & (RING - 1)) == 0, "exchange ring: no slot reused before it is read");
@@ -675,8 +676,8 @@ struct ScanSmem {
   float Os[mp::C][mp::DVB + 4];      // output tile staging of the output wave
   ExBuf X[2];                        // by chunk parity
   uint16_t Vr[2][mp::VR_ROWS][mp::DVB];  // fused prologue: raw x rows of the V slice, by chunk parity
-  int ks_done[mp::NPAIR];            // c + 1 once chain wave p's K S^T of chunk c is done
-  int os_ready;                      // whole-layer call: c + 1 once chunk c's output tile is in Os
+  int ks_done[mp::NVT];              // c + 1 once chain wave p's K S^T of chunk c is done
+  int os_ready;                      // whole-layer call: (output waves) x (c + 1) once chunk c's tile is in Os
   unsigned ticket;                   // whole-layer call: this workgroup's place in start order
 };
 static_assert(sizeof(ScanSmem) <= 160 * 1024, "scan LDS");
@@ -750,9 +751,9 @@ __device__ __forceinline__ f4 bf16x4_to_f4(uint2 u) {
 // per tile.
 // The wave issues in order, so the code is laid out by hand: operands are read a step ahead,
 // and the results of a product are first used several products later.
-template <bool VF16>
+template <int TPW, bool VF16>
 __device__ __forceinline__ void chain_step(const ScanBuf& B, ExBuf& exU, ExBuf& exS, int t0, int lane, int ln, int lg,
-                                           f4 (&sacc)[mp::TPW][8], h8 (&sb)[mp::TPW][4], int* ks_done, int c) {
+                                           f4 (&sacc)[TPW][8], h8 (&sb)[TPW][4], int* ks_done, int c) {
   using namespace mp;
   const RecImage& R = B.R;
   const f4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -888,8 +889,9 @@ __device__ __forceinline__ void chain_step(const ScanBuf& B, ExBuf& exU, ExBuf& 
 // Output wave, part 1 (chunk c in buffer B, value tiles t0 .. t0 + TPW - 1): Q S^T with the S^T
 // operands the chain wave handed over, and the operands of P and the gates exp(gamma) kept for
 // part 2.
+template <int TPW>
 __device__ __forceinline__ void qs_step(const ScanBuf& B, const ExBuf& exS, int t0, int lane, int ln, int lg,
-                                        f4 (&qs)[mp::TPW][4], h8 (&pa)[6], float (&ge)[16]) {
+                                        f4 (&qs)[TPW][4], h8 (&pa)[6], float (&ge)[16]) {
   using namespace mp;
   const f4 zero = {0.f, 0.f, 0.f, 0.f};
   h8 sb[TPW][4];
@@ -926,9 +928,9 @@ __device__ __forceinline__ void qs_step(const ScanBuf& B, const ExBuf& exS, int 
 // Output wave, part 2 (the chunk c of part 1, one iteration later): O = diag(exp gamma) Q S^T
 // + P U for its tiles, staged in their columns of Os by this wave and written out from there
 // (rows < L, 2 TPW lanes per row, eight values each).
-template <int O_DT, bool STAGE>
+template <int TPW, int O_DT, bool STAGE>
 __device__ __forceinline__ void o_step(const ExBuf& exU, float (*Os)[mp::DVB + 4], int* os_ready, const PrefillArgs& a,
-                                       const Geo& G, int c, int t0, const f4 (&qs)[mp::TPW][4], const h8 (&pa)[6],
+                                       const Geo& G, int c, int t0, const f4 (&qs)[TPW][4], const h8 (&pa)[6],
                                        const float (&gg)[16]) {
   using namespace mp;
   const int lane = G.lane, ln = G.ln, lg = G.lg;
@@ -962,10 +964,10 @@ __device__ __forceinline__ void o_step(const ExBuf& exU, float (*Os)[mp::DVB + 4
       for (int e = 0; e < 4; ++e) Os[16 * i + 4 * lg + e][16 * (t0 + t) + ln] = a.scale * o[t][i][e];
   if constexpr (STAGE) {
     // hand the tile to the tile waves, which write it out: the wave's LDS writes are complete
-    // before the flag is raised, and the tile is not rewritten before the next barrier
-    static_assert(NPAIR == 1, "one output wave stages the whole tile");
+    // before its count is added (one per chunk from each output wave), and the tile is
+    // not rewritten before the next barrier
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-    if (lane == 0) __hip_atomic_store(os_ready, c + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (lane == 0) __hip_atomic_fetch_add(os_ready, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     return;
   }
   // Os is written and read back by this wave only: LDS keeps a wave's accesses in order.
@@ -1218,7 +1220,7 @@ __device__ __forceinline__ void tile_wave(ScanSmem& sm, const PrefillArgs& a, co
       for (int e = 0; e < 8; ++e) xa[q][e] = xb[q][e];
     }
     if (c >= 1) {
-      wait_flag(&sm.os_ready, c, a);  // chunk c - 1 staged
+      wait_flag(&sm.os_ready, npair(true) * c, a);  // chunk c - 1 staged by every output wave
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
       tile_take<NG>(sm.Os, r0, lane, xb);
       row_sums<NG>(xb, sb);
@@ -1413,8 +1415,9 @@ __device__ __forceinline__ void conv_vslice(ScanSmem& sm, const PrefillArgs& a, 
 // chunk c; the output waves finish and write out chunk c-1 and start chunk c; the copy waves
 // fill the other buffer with chunk c+1.
 template <int O_DT, bool FUSED, bool NORM = false>
-__global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, int64_t maxch) {
+__global__ __launch_bounds__(64 * mp::nwaves(NORM)) void scan_kernel(PrefillArgs a, int64_t maxch) {
   using namespace mp;
+  constexpr int TPW = tpw(NORM), NPAIR = npair(NORM);
   extern __shared__ __align__(16) unsigned char smem_raw[];
   ScanSmem& sm = *reinterpret_cast<ScanSmem*>(smem_raw);
   const int32_t* off = ws_offsets(a.workspace);
@@ -1540,7 +1543,7 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
     lds_barrier();
     for (int c = 0; c < nc + 1; ++c) {
       if (c < nc)
-        chain_step<FUSED>(sm.B[c & 1], sm.X[c & 1], sm.X[(c + 1) & 1], t0, lane, ln, lg, sacc, sb, &sm.ks_done[pr], c);
+        chain_step<TPW, FUSED>(sm.B[c & 1], sm.X[c & 1], sm.X[(c + 1) & 1], t0, lane, ln, lg, sacc, sb, &sm.ks_done[pr], c);
       lds_barrier();
     }
     // An fp16 operand out of range anywhere in the sequence leaves the state out of range or not
@@ -1575,8 +1578,8 @@ __global__ __launch_bounds__(64 * mp::NWAVES) void scan_kernel(PrefillArgs a, in
       // Start once the chain wave is past K S^T: run beside it, the output wave's LDS reads
       // slow the chain's operand reads (the serial path) by about a third.
       if (c < nc) wait_flag(&sm.ks_done[pr], c + 1, a);
-      if (c >= 1) o_step<O_DT, NORM>(sm.X[(c - 1) & 1], sm.Os, &sm.os_ready, a, G, c - 1, t0, qs, pa, ge);
-      if (c < nc) qs_step(sm.B[c & 1], sm.X[c & 1], t0, lane, ln, lg, qs, pa, ge);
+      if (c >= 1) o_step<TPW, O_DT, NORM>(sm.X[(c - 1) & 1], sm.Os, &sm.os_ready, a, G, c - 1, t0, qs, pa, ge);
+      if (c < nc) qs_step<TPW>(sm.B[c & 1], sm.X[c & 1], t0, lane, ln, lg, qs, pa, ge);
       lds_barrier();
     }
   } else {  // copy wave
@@ -1664,7 +1667,7 @@ bool prefill_mfma_fits(int num_seqs, int64_t total, int hk, int hv) {
   using u128 = unsigned __int128;
   const int64_t rounds = (hv / hk + mp::PH - 1) / mp::PH;
   return grid_fits((u128)max_chunks(total, num_seqs) * (u128)hk * (u128)rounds, 256 * mp::PH) &&
-         grid_fits((u128)num_seqs * (u128)hv * mp::NB, 64 * mp::NWAVES);
+         grid_fits((u128)num_seqs * (u128)hv * mp::NB, 64 * mp::MAX_WAVES);
 }
 
 template <int O_DT, bool FUSED, bool NORM>
@@ -1700,7 +1703,7 @@ template <int O_DT, bool FUSED, bool NORM>
 static hipError_t launch_scan(const PrefillArgs& a, int64_t maxch, hipStream_t st) {
   const hipError_t e = scan_attr<O_DT, FUSED, NORM>();
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((int64_t)a.num_seqs * a.hv * mp::NB)), block(64 * mp::NWAVES);
+  const dim3 grid((unsigned)((int64_t)a.num_seqs * a.hv * mp::NB)), block(64 * mp::nwaves(NORM));
   hipLaunchKernelGGL((scan_kernel<O_DT, FUSED, NORM>), grid, block, sizeof(ScanSmem), st, a, maxch);
   return hipGetLastError();
 }
