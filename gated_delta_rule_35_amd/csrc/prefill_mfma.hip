@@ -63,8 +63,9 @@ constexpr int LDQ = D + 8;   // fp16 row stride of staged Q/K rows
 constexpr int NVT = 2;       // 16-wide value tiles per scan workgroup
 // Value tiles per chain wave and per output wave (measured at T = 8192).  One tile per wave
 // (two chain and two output waves, one SIMD each) halves each wave's serial work, but every wave
-// then streams the whole K, Q, X and P tiles from LDS for half the products: the prefill calls
-// run 5 % faster so, the whole-layer call, whose two tile waves share the workgroup, 5-8 % slower.
+// then streams the whole K, Q, X and P tiles from LDS for half the products, and ten waves leave
+// each at most 170 registers: the prefill calls run 5 % faster so, the whole-layer call (whose
+// two tile waves then share SIMDs with the chain or output waves) no faster.
 constexpr int tpw(bool norm) { return norm ? 2 : 1; }
 constexpr int npair(bool norm) { return NVT / tpw(norm); }  // chain waves (and as many output waves)
 constexpr int NCP = 6;       // copy waves
