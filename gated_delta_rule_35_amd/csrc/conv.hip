@@ -28,6 +28,49 @@ __device__ __forceinline__ void load_hist8(const ConvArgs& a, int n, int c0, int
   for (int e = 0; e < 8; ++e) out[e] = load1<DT>(a.state, base + e * 3 + idx);
 }
 
+// The whole history of channels c0..c0+7 of sequence n: 24 contiguous elements (entry j of
+// channel c0 + e at 3 e + j).  VEC: three 16-byte vectors each way (the host found the history
+// 16-byte aligned; an 8-channel group then starts on a 48-byte boundary for bf16, 96 for f32).
+template <int DT, bool VEC>
+__device__ __forceinline__ void load_hist_all(const ConvArgs& a, int n, int c0, float h[3][8]) {
+  if constexpr (VEC) {
+    const int64_t base = ((int64_t)n * a.channels + c0) * 3;
+    Raw8<DT> r[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) r[q] = load_raw8<DT>(a.state, base + 8 * q);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int j = 0; j < 3; ++j) h[j][e] = raw_at<DT>(r, 3 * e + j);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 3; ++j) load_hist8<DT>(a, n, c0, j, h[j]);
+  }
+}
+template <int DT, bool VEC>
+__device__ __forceinline__ void store_hist_all(const ConvArgs& a, int n, int c0, const float h0[8], const float h1[8],
+                                               const float h2[8]) {
+  const int64_t base = ((int64_t)n * a.channels + c0) * 3;
+  if constexpr (VEC) {
+    float f[24];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      f[3 * e] = h0[e];
+      f[3 * e + 1] = h1[e];
+      f[3 * e + 2] = h2[e];
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) store8<DT>(a.state, base + 8 * q, f + 8 * q);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      store1<DT>(a.state, base + e * 3 + 0, h0[e]);
+      store1<DT>(a.state, base + e * 3 + 1, h1[e]);
+      store1<DT>(a.state, base + e * 3 + 2, h2[e]);
+    }
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ void conv_token(const ConvArgs& a, const float w[8][4], const float bias[8],
                                            const float h0[8], const float h1[8], const float h2[8],
@@ -51,18 +94,36 @@ __device__ __forceinline__ void conv_token(const ConvArgs& a, const float w[8][4
   }
 }
 
-template <int DT>
+// Taps and bias of channels c0..c0+7.  VEC: as 16-byte vectors (the 32 taps and the 8 biases
+// are contiguous), used where the host found weight and bias 16-byte aligned; else one element
+// at a time (the C ABI asks only for 4-byte alignment).
+template <int DT, bool VEC>
 __device__ __forceinline__ void load_params(const ConvArgs& a, int c0, bool active, float w[8][4], float bias[8]) {
+  if constexpr (VEC) {
+    Raw8<DT> r[4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
+    for (int q = 0; q < 4; ++q) r[q] = active ? load_raw8<DT>(a.w, (int64_t)c0 * 4 + 8 * q) : Raw8<DT>{};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w[e][j] = active ? load1<DT>(a.w, (int64_t)(c0 + e) * 4 + j) : 0.f;
-    bias[e] = (active && a.bias) ? load1<DT>(a.bias, c0 + e) : 0.f;
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[e][j] = raw_at<DT>(r, 4 * e + j);
+    if (active && a.bias) load8<DT>(a.bias, c0, bias);
+    else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) bias[e] = 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[e][j] = active ? load1<DT>(a.w, (int64_t)(c0 + e) * 4 + j) : 0.f;
+      bias[e] = (active && a.bias) ? load1<DT>(a.bias, c0 + e) : 0.f;
+    }
   }
 }
 
 // Prefill over a packed batch: grid (channel blocks, token blocks).
-template <int DT>
+template <int DT, bool VEC>
 __global__ __launch_bounds__(CONV_THREADS) void conv_prefill_kernel(ConvArgs a) {
   const int c0 = (blockIdx.x * CONV_THREADS + threadIdx.x) * 8;
   const bool active = c0 < a.channels;
@@ -71,7 +132,7 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_prefill_kernel(ConvArgs a) 
   const int64_t t1 = t0 + CONV_TB < a.total ? t0 + CONV_TB : a.total;
 
   float w[8][4], bias[8];
-  load_params<DT>(a, c0, active, w, bias);
+  load_params<DT, VEC>(a, c0, active, w, bias);
 
   // sequence holding t0: largest n with cu[n] <= t0
   int lo = 0, hi = a.num_seqs - 1;
@@ -170,7 +231,7 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_prefill_kernel(ConvArgs a) 
 
 // Final history of every sequence, after the prefill kernel has read the old one:
 // new[j] = xh[end - 3 + j] (old history for positions before the sequence start).
-template <int DT>
+template <int DT, bool VEC>
 __global__ __launch_bounds__(CONV_THREADS) void conv_state_kernel(ConvArgs a) {
   const int c0 = (blockIdx.x * CONV_THREADS + threadIdx.x) * 8;
   const int n = blockIdx.y;
@@ -180,8 +241,7 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_state_kernel(ConvArgs a) {
   if (end < start) end = start;
   const int64_t len = end - start;
   float old[3][8], nw[3][8];
-#pragma unroll
-  for (int j = 0; j < 3; ++j) load_hist8<DT>(a, n, c0, j, old[j]);
+  load_hist_all<DT, VEC>(a, n, c0, old);
 #pragma unroll
   for (int j = 0; j < 3; ++j) {
     const int64_t p = len - 3 + j;  // position relative to the sequence start
@@ -191,30 +251,19 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_state_kernel(ConvArgs a) {
       for (int e = 0; e < 8; ++e) nw[j][e] = old[3 + p][e];
     }
   }
-  const int64_t base = ((int64_t)n * a.channels + c0) * 3;
-#pragma unroll
-  for (int j = 0; j < 3; ++j)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) store1<DT>(a.state, base + e * 3 + j, nw[j][e]);
+  store_hist_all<DT, VEC>(a, n, c0, nw[0], nw[1], nw[2]);
 }
 
 // Decode: one token per sequence, history read and advanced in place.
-template <int DT>
+template <int DT, bool VEC>
 __global__ __launch_bounds__(CONV_THREADS) void conv_decode_kernel(ConvArgs a) {
   const int c0 = (blockIdx.x * CONV_THREADS + threadIdx.x) * 8;
   const int n = blockIdx.y;
   const bool active = c0 < a.channels;
   const bool l2 = active && (c0 / 128) < a.l2_heads;
-  float w[8][4], bias[8], h[3][8], xc[8], y[8];
-  load_params<DT>(a, c0, active, w, bias);
-#pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    if (active) load_hist8<DT>(a, n, c0, j, h[j]);
-    else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) h[j][e] = 0.f;
-    }
-  }
+  float w[8][4], bias[8], h[3][8] = {}, xc[8], y[8];
+  load_params<DT, VEC>(a, c0, active, w, bias);
+  if (active) load_hist_all<DT, VEC>(a, n, c0, h);
   if (active) load8<DT>(a.x, (int64_t)n * a.x_stride + c0, xc);
   else {
 #pragma unroll
@@ -223,48 +272,57 @@ __global__ __launch_bounds__(CONV_THREADS) void conv_decode_kernel(ConvArgs a) {
   conv_token<DT>(a, w, bias, h[0], h[1], h[2], xc, l2, active, y);
   if (!active) return;
   store8_nt<DT>(a.y, (int64_t)n * a.y_stride + c0, y);
-  const int64_t base = ((int64_t)n * a.channels + c0) * 3;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    store1<DT>(a.state, base + e * 3 + 0, h[1][e]);
-    store1<DT>(a.state, base + e * 3 + 1, h[2][e]);
-    store1<DT>(a.state, base + e * 3 + 2, xc[e]);
-  }
+  store_hist_all<DT, VEC>(a, n, c0, h[1], h[2], xc);
 }
 
-template <int DT>
+static bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+// Taps, bias and history as 16-byte vectors: every one of them present is 16-byte aligned.
+static bool conv_vec(const ConvArgs& a) { return al16(a.w) && al16(a.bias) && al16(a.state); }
+
+template <int DT, bool VEC>
 static hipError_t launch_conv_t(const ConvArgs& a, hipStream_t st) {
   const unsigned cblocks = (unsigned)((a.channels / 8 + CONV_THREADS - 1) / CONV_THREADS);
   if (a.cu == nullptr) {
     if (a.num_seqs == 0) return hipSuccess;
-    hipLaunchKernelGGL((conv_decode_kernel<DT>), dim3(cblocks, (unsigned)a.num_seqs), dim3(CONV_THREADS), 0, st, a);
+    hipLaunchKernelGGL((conv_decode_kernel<DT, VEC>), dim3(cblocks, (unsigned)a.num_seqs), dim3(CONV_THREADS), 0, st,
+                       a);
     return hipGetLastError();
   }
   if (a.total > 0) {
     const unsigned tblocks = (unsigned)((a.total + CONV_TB - 1) / CONV_TB);
-    hipLaunchKernelGGL((conv_prefill_kernel<DT>), dim3(cblocks, tblocks), dim3(CONV_THREADS), 0, st, a);
+    hipLaunchKernelGGL((conv_prefill_kernel<DT, VEC>), dim3(cblocks, tblocks), dim3(CONV_THREADS), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (a.state && a.num_seqs > 0) {
-    hipLaunchKernelGGL((conv_state_kernel<DT>), dim3(cblocks, (unsigned)a.num_seqs), dim3(CONV_THREADS), 0, st, a);
+    hipLaunchKernelGGL((conv_state_kernel<DT, VEC>), dim3(cblocks, (unsigned)a.num_seqs), dim3(CONV_THREADS), 0, st,
+                       a);
     return hipGetLastError();
   }
   return hipSuccess;
 }
 
-hipError_t launch_conv_history(const ConvArgs& a, hipStream_t st) {
-  if (!a.state || a.num_seqs == 0) return hipSuccess;
+template <bool VEC>
+static hipError_t launch_history_t(const ConvArgs& a, hipStream_t st) {
   const unsigned cblocks = (unsigned)((a.channels / 8 + CONV_THREADS - 1) / CONV_THREADS);
   if (a.dtype == DT_BF16)
-    hipLaunchKernelGGL((conv_state_kernel<DT_BF16>), dim3(cblocks, (unsigned)a.num_seqs), dim3(CONV_THREADS), 0, st, a);
+    hipLaunchKernelGGL((conv_state_kernel<DT_BF16, VEC>), dim3(cblocks, (unsigned)a.num_seqs), dim3(CONV_THREADS), 0,
+                       st, a);
   else
-    hipLaunchKernelGGL((conv_state_kernel<DT_F32>), dim3(cblocks, (unsigned)a.num_seqs), dim3(CONV_THREADS), 0, st, a);
+    hipLaunchKernelGGL((conv_state_kernel<DT_F32, VEC>), dim3(cblocks, (unsigned)a.num_seqs), dim3(CONV_THREADS), 0,
+                       st, a);
   return hipGetLastError();
 }
 
+hipError_t launch_conv_history(const ConvArgs& a, hipStream_t st) {
+  if (!a.state || a.num_seqs == 0) return hipSuccess;
+  return al16(a.state) ? launch_history_t<true>(a, st) : launch_history_t<false>(a, st);
+}
+
 hipError_t launch_conv(const ConvArgs& a, hipStream_t st) {
-  return a.dtype == DT_BF16 ? launch_conv_t<DT_BF16>(a, st) : launch_conv_t<DT_F32>(a, st);
+  const bool vec = conv_vec(a);
+  if (a.dtype == DT_BF16) return vec ? launch_conv_t<DT_BF16, true>(a, st) : launch_conv_t<DT_BF16, false>(a, st);
+  return vec ? launch_conv_t<DT_F32, true>(a, st) : launch_conv_t<DT_F32, false>(a, st);
 }
 
 }  // namespace agnes

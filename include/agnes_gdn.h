@@ -106,6 +106,12 @@ typedef enum agnes_dtype {
  *               kernel_size-1), written after every read of the old contents.
  *   head_dim    channels per head for the L2 step (128); channels must be a
  *               multiple of 8 and l2norm_heads*head_dim <= channels.
+ *
+ * weight, bias and conv_state need only be 4-byte aligned (x and y 16-byte).
+ * When all three that are given are 16-byte aligned, the taps, biases and
+ * history are read, and the history written, as 16-byte vectors (measured:
+ * decode mode at 256 x 10240 channels 27.5 -> 14.1 us, prefill at 8192 tokens
+ * 70.7 -> 59.4 us); otherwise element by element, with the same results.
  */
 int agnes_gdn_conv(const void* x, int64_t x_token_stride, void* y, int64_t y_token_stride,
                    agnes_dtype dtype, const void* weight, const void* bias,

@@ -149,6 +149,46 @@ def test_conv_decode_mode(dtype):
     np.testing.assert_array_equal(oracle.as_f64(host(stt)), rst)
 
 
+def _at_4_bytes(t):
+    """A copy of t whose data starts 4 bytes past a 16-byte boundary (the C ABI's minimum for the
+    conv's taps, bias and history)."""
+    off = 4 // t.element_size()
+    buf = torch.empty(t.numel() + off, dtype=t.dtype, device=t.device)
+    v = buf[off:].view(t.shape)
+    v.copy_(t)
+    assert v.data_ptr() % 16 == 4
+    return v
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_conv_params_at_4_byte_alignment(dtype, mode):
+    """Taps, bias and history 16-byte aligned are read and written as 16-byte vectors, at the C
+    ABI's 4-byte minimum one element at a time: the outputs and the advanced history agree bit for
+    bit, and with the oracle."""
+    rng = np.random.default_rng(24)
+    lens = [1] * 9 if mode == "decode" else [5, 1, 0, 70, 2]
+    C = 2048
+    x, w, st, cu = _conv_case(rng, lens, C, dtype, True, 8)
+    conv = f32_to_bf16_bits if dtype == "bf16" else (lambda a: a)
+    b = conv(rng.uniform(-0.5, 0.5, C).astype(np.float32))
+    cut = None if mode == "decode" else _t(cu)
+    outs = []
+    for place in (lambda t: t, _at_4_bytes):
+        wt, bt, stt = place(_t(w)), place(_t(b)), place(_t(st))
+        y = gdn.conv(_t(x), wt, bias=bt, cu_seqlens=cut, conv_state=stt, l2norm_heads=8)
+        torch.cuda.synchronize()
+        outs.append((host(y), host(stt)))
+    np.testing.assert_array_equal(outs[1][0], outs[0][0])
+    np.testing.assert_array_equal(outs[1][1], outs[0][1])
+    ry, rst = oracle.causal_conv(x, w, cu, st, l2_heads=8, bias=b)
+    if dtype == "bf16":
+        _check_bf16_out(outs[0][0], ry)
+    else:
+        assert rel_l2(outs[0][0], ry) <= 1e-6
+    np.testing.assert_array_equal(oracle.as_f64(outs[0][1]), rst)
+
+
 # ------------------------------------------------------------------ gated RMSNorm
 
 @pytest.mark.parametrize("odt,zdt,ydt", [("bf16", "bf16", "bf16"), ("f32", "bf16", "bf16"),
