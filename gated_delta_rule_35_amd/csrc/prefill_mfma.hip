@@ -1750,48 +1750,92 @@ struct StageCuts {
 constexpr int LAYER_CUT = 26, PREFILL_CUT = 28;  // defaults (measured at T = 8192)
 
 namespace {
+// The side streams of the calls in stages: one per caller stream, up to SIDE_PER_DEV per device
+// (beyond that the least recently used one is shared with the new caller stream: its work stays
+// ordered on the side stream and every wait is enqueued against the event record it follows, so
+// sharing costs only concurrency).  Callers on different streams thus run their side-stream
+// preparation side by side.
+constexpr int SIDE_PER_DEV = 4;
 struct SideQueue {
   hipStream_t s = nullptr;
   hipEvent_t prepped[MAX_STAGES] = {};
+  hipStream_t owner = nullptr;  // the caller stream it last served
+  unsigned long long used = 0;  // when (g_side_tick)
   int cus = 0;
 };
-std::mutex g_side_mu;  // held while a call enqueues: the side queue's events are shared
-SideQueue g_side[64];
+std::mutex g_side_mu;  // held while a call enqueues: a side queue's events are shared
+SideQueue g_side[64][SIDE_PER_DEV];
+unsigned long long g_side_tick = 0;
 StageCuts g_cuts;      // under g_side_mu
 }  // namespace
 
-static hipError_t side_queue(SideQueue*& q) {
+static hipError_t destroy_side_queue(SideQueue& q) {
+  hipError_t first = hipSuccess;
+  for (int k = 0; k < MAX_STAGES; ++k)
+    if (q.prepped[k]) {
+      const hipError_t e = hipEventDestroy(q.prepped[k]);
+      if (first == hipSuccess) first = e;
+    }
+  if (q.s) {
+    const hipError_t e = hipStreamDestroy(q.s);
+    if (first == hipSuccess) first = e;
+  }
+  q = SideQueue{};
+  return first;
+}
+
+// The side queue of `caller` on the current device (under g_side_mu), created on first use.
+static hipError_t side_queue(hipStream_t caller, SideQueue*& q) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  q = &g_side[dev];
-  if (q->s) return hipSuccess;
-  if ((e = hipDeviceGetAttribute(&q->cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-  for (int k = 0; k < MAX_STAGES; ++k)
-    if ((e = hipEventCreate(&q->prepped[k])) != hipSuccess) return e;
-  return hipStreamCreateWithFlags(&q->s, hipStreamNonBlocking);  // default priority
+  SideQueue* row = g_side[dev];
+  SideQueue* pick = nullptr;
+  for (int i = 0; i < SIDE_PER_DEV && !pick; ++i)
+    if (row[i].s && row[i].owner == caller) pick = &row[i];
+  for (int i = 0; i < SIDE_PER_DEV && !pick; ++i)
+    if (!row[i].s) pick = &row[i];
+  if (!pick) {
+    pick = &row[0];
+    for (int i = 1; i < SIDE_PER_DEV; ++i)
+      if (row[i].used < pick->used) pick = &row[i];
+  }
+  if (!pick->s) {
+    SideQueue n;
+    e = hipDeviceGetAttribute(&n.cus, hipDeviceAttributeMultiprocessorCount, dev);
+    for (int k = 0; k < MAX_STAGES && e == hipSuccess; ++k) e = hipEventCreate(&n.prepped[k]);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&n.s, hipStreamNonBlocking);  // default priority
+    if (e != hipSuccess) {
+      destroy_side_queue(n);
+      return e;
+    }
+    *pick = n;
+  }
+  pick->owner = caller;
+  pick->used = ++g_side_tick;
+  q = pick;
+  return hipSuccess;
 }
 
-// Destroys the side queues (stream and events) the calls in stages created, after waiting for
+// Destroys the side queues (streams and events) the calls in stages created, after waiting for
 // their work; the next such call creates them again.  No HIP call at all when none exists.
 hipError_t release_side_queues() {
   std::lock_guard<std::mutex> lock(g_side_mu);
   bool any = false;
-  for (const SideQueue& q : g_side) any = any || q.s != nullptr;
+  for (const auto& row : g_side)
+    for (const SideQueue& q : row) any = any || q.s != nullptr;
   if (!any) return hipSuccess;
   int cur = 0;
   hipError_t first = hipGetDevice(&cur);
   for (int d = 0; d < 64; ++d) {
-    SideQueue& q = g_side[d];
-    if (!q.s) continue;
-    hipError_t e = hipSetDevice(d);
-    if (e == hipSuccess) e = hipStreamSynchronize(q.s);
-    if (e == hipSuccess) e = hipStreamDestroy(q.s);
-    for (int k = 0; k < MAX_STAGES && e == hipSuccess; ++k)
-      if (q.prepped[k]) e = hipEventDestroy(q.prepped[k]);
-    if (first == hipSuccess) first = e;
-    q = SideQueue{};
+    for (SideQueue& q : g_side[d]) {
+      if (!q.s) continue;
+      hipError_t e = hipSetDevice(d);
+      if (e == hipSuccess) e = hipStreamSynchronize(q.s);
+      if (e == hipSuccess) e = destroy_side_queue(q);  // (kept, with its work, if the wait failed)
+      if (first == hipSuccess) first = e;
+    }
   }
   const hipError_t e = hipSetDevice(cur);
   return first != hipSuccess ? first : e;
@@ -1822,7 +1866,7 @@ static hipError_t launch_staged(const PrefillArgs& a, hipStream_t st) {
   if (!cuts.custom) cuts.cut[0] = NORM ? LAYER_CUT : PREFILL_CUT;
   if (cuts.n == 0) return launch_o<O_DT, FUSED, NORM>(a, st);
   SideQueue* q = nullptr;
-  hipError_t e = side_queue(q);
+  hipError_t e = side_queue(st, q);
   if (e != hipSuccess) return e;
   const int64_t grid = (int64_t)a.num_seqs * a.hv * mp::NB;
   const bool split = 4 * grid <= 3 * (int64_t)q->cus && a.total >= (int64_t)a.num_seqs * 8 * mp::C;

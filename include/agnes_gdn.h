@@ -156,12 +156,14 @@ size_t agnes_gdn_prefill_workspace_size(int num_seqs, int64_t total_tokens, int 
  * With bf16 inputs, where the scan leaves a quarter of the device's compute
  * units free and the sequences average at least 512 tokens, the call runs in
  * two stages: the precomputation of the second part of every sequence runs
- * on a side stream of the library's own (created with two events on first
- * use, once per device, default priority) beside the scan of the first part,
+ * on a side stream of the library's own beside the scan of the first part,
  * and is joined back into `stream` before the second scan; work enqueued on
- * `stream` afterwards sees every result.  Calls enqueue under a lock; the side
- * stream joins a graph capture of `stream`.  Results are bit-identical to the
- * one-stage run.
+ * `stream` afterwards sees every result.  Each caller stream gets its own side
+ * stream (created with its events on first use, default priority, up to 4 per
+ * device; a fifth caller stream shares the least recently used one), so calls
+ * on different streams prepare side by side.  Calls enqueue under a lock; the
+ * side stream joins a graph capture of `stream`.  Results are bit-identical to
+ * the one-stage run.
  */
 int agnes_gdn_prefill_chunked(const void* q, const void* k, const void* v, agnes_dtype in_dtype,
                               int64_t qk_token_stride, int64_t v_token_stride,
@@ -532,9 +534,9 @@ int agnes_gdn_ceiling_rmw_stream(void* buf, size_t bytes, void* stream);
 int agnes_gdn_ceiling_mfma(float* sink, int blocks, int iters, void* stream);
 
 /*
- * agnes_gdn_release — destroys the HIP objects the library keeps between calls: the side stream
- * and the events per device that the calls in stages create on first use (after waiting for the
- * work on that stream).  A later call in stages creates them again.  Call it when no
+ * agnes_gdn_release — destroys the HIP objects the library keeps between calls: the side streams
+ * and their events that the calls in stages create on first use (after waiting for the work on
+ * each stream).  A later call in stages creates them again.  Call it when no
  * call of the library is in flight, e.g. before the process exits, so that no library handle is
  * left for the runtime's own teardown; it makes no HIP call when nothing was created.  Returns
  * AGNES_OK, or AGNES_ERR_HIP if a destroy fails.

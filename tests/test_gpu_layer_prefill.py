@@ -141,6 +141,42 @@ def test_layer_prefill_in_two_stages():
 
 
 
+def test_layer_prefill_in_two_stages_on_two_streams():
+    """Two calls in two stages enqueued back to back on two streams (each with its own side
+    stream, so both preparations may run at once, each call on its own workspace): y and the final
+    states equal, bit for bit, the same calls run one after the other on the default stream."""
+    rng = np.random.default_rng(651)
+    cases = [_case(rng, [1500, 900], 2, 6), _case(rng, [1200, 1, 700], 2, 6)]
+
+    def args(d):
+        return dict(x=dev(d["x"]), w=dev(d["w"]), g=dev(d["g"]), beta=dev(d["beta"]), cu=dev(d["cu"]),
+                    z=dev(d["z"]), nw=dev(d["nw"]), cs=dev(d["cs"]), s0=dev(d["s0"]))
+
+    def call(a, hk):
+        return gdn.layer_prefill(a["x"], a["w"], a["g"], a["beta"], a["cu"], a["z"], a["nw"], num_k_heads=hk,
+                                 conv_state=a["cs"], initial_state=a["s0"], out_dtype=torch.float32)
+
+    ref = []
+    for d in cases:
+        a = args(d)
+        y, fin = call(a, d["hk"])
+        torch.cuda.synchronize()
+        ref.append((host(y), host(fin), host(a["cs"])))
+    ins = [args(d) for d in cases]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for a, d, s in zip(ins, cases, streams):
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            outs.append(call(a, d["hk"]))
+    torch.cuda.synchronize()
+    for (y, fin), a, (ry, rf, rc) in zip(outs, ins, ref):
+        np.testing.assert_array_equal(host(y), ry)
+        np.testing.assert_array_equal(host(fin), rf)
+        np.testing.assert_array_equal(host(a["cs"]), rc)
+
+
 @pytest.mark.parametrize("cuts", [(), (18, 31), (10, 20, 30), (39,), (5, 10, 15, 20, 25, 30, 35)],
                          ids=["one", "three", "four", "late", "eight"])
 def test_layer_prefill_stage_cuts_change_nothing(cuts):
