@@ -304,7 +304,7 @@ def main():
         c["fin"] = torch.empty((len(lens), HV, D, D), dtype=torch.float32, device="cuda")
         return c, n
 
-    def layer_line(name, lens, seed, init, reps):
+    def layer_line(name, lens, seed, init, reps, traffic_key):
         c, n = layer_case(lens, seed, init)
         ms = timed(torch, lambda i: gdn.layer_prefill(c["x"], c["w"], c["g"], c["beta"], c["cu"], c["z"], nw,
                                                       num_k_heads=HK, initial_state=c["s0"], final_state=c["fin"],
@@ -320,13 +320,15 @@ def main():
                 "tokens_per_s": round(n / (med * 1e-3), 1),
                 "roofline": {"bound": "mfma", "kernel": "agnes_gdn_layer_prefill call", "achieved": round(tf, 2),
                              "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / MFMA_PEAK_TFLOPS, 4),
-                             "frac_of_measured_ceiling": round(tf / mfma_tf, 4), "traffic": None,
+                             "frac_of_measured_ceiling": round(tf / mfma_tf, 4),
+                             "traffic": measured_traffic(traffic_key),
                              "flops_per_launch": flops, "bytes_per_launch": nbytes,
                              "hbm_GBps_algorithmic": round(nbytes / (np.mean(ms) * 1e-3) / 1e9, 1)}}
 
-    long_line = layer_line("layer T=65536", [65536], 2002, "normal", args.reps)
+    long_line = layer_line("layer T=65536", [65536], 2002, "normal", args.reps, "layer_prefill_t65536")
     vl = varlen_lengths(np.random.default_rng(1004))
-    varlen_line = layer_line("layer varlen 32", [int(x) for x in vl], 2004, "alternate", args.reps)
+    varlen_line = layer_line("layer varlen 32", [int(x) for x in vl], 2004, "alternate", args.reps,
+                             "layer_prefill_varlen32")
 
     # ---- decode: 256 sequences, fp32 states in place (805 MB, larger than every cache)
     state = to_dev(dec["state"], torch)
