@@ -141,12 +141,16 @@ def test_layer_prefill_in_two_stages():
 
 
 
-def test_layer_prefill_in_two_stages_on_two_streams():
-    """Two calls in two stages enqueued back to back on two streams (each with its own side
-    stream, so both preparations may run at once, each call on its own workspace): y and the final
-    states equal, bit for bit, the same calls run one after the other on the default stream."""
+@pytest.mark.parametrize("nstreams", [2, 6])
+def test_layer_prefill_in_two_stages_on_several_streams(nstreams):
+    """Calls in two stages enqueued back to back on several streams (each with a side stream of its
+    own, so the preparations may run at once; six streams are more than the library keeps side
+    queues for, so some share one), each call on its own workspace: y, the final states and the
+    conv histories equal, bit for bit, the same calls run one after the other on the default
+    stream."""
     rng = np.random.default_rng(651)
-    cases = [_case(rng, [1500, 900], 2, 6), _case(rng, [1200, 1, 700], 2, 6)]
+    lens = [[1500, 900], [1200, 1, 700], [800, 400], [2100], [700, 700, 200], [1000, 999]]  # all in stages
+    cases = [_case(rng, lens[i], 2, 6) for i in range(nstreams)]
 
     def args(d):
         return dict(x=dev(d["x"]), w=dev(d["w"]), g=dev(d["g"]), beta=dev(d["beta"]), cu=dev(d["cu"]),
@@ -164,7 +168,7 @@ def test_layer_prefill_in_two_stages_on_two_streams():
         ref.append((host(y), host(fin), host(a["cs"])))
     ins = [args(d) for d in cases]
     torch.cuda.synchronize()
-    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    streams = [torch.cuda.Stream() for _ in range(nstreams)]
     outs = []
     for a, d, s in zip(ins, cases, streams):
         s.wait_stream(torch.cuda.current_stream())
